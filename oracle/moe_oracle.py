@@ -1,0 +1,533 @@
+"""CPU oracle of the routed MXFP4 mixture-of-experts layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check and the benchmark's CPU
+baseline leg use it.  It shares no code with the HIP library (no kernels,
+headers, tables or helpers); both sides consume the same seeded input bytes.
+
+Everything is plain NumPy in float64, written to be checked by eye against
+the pages it follows:
+
+  [P1] "Running DeepSeek-V4-Flash across four free GPUs"
+  [P2] "An elephant through a straw"
+  [P3] "DeepSeek V4.1 Flash on 5x 8 GB (PP5 full residency)"
+
+The layer (P1 §What the expert cache actually does; P2 §Not all six experts
+matter equally, §43 graphs, 43 syncs):
+  1. route: pick each token's top-k experts from the router's scores and
+     renormalise their weights;
+  2. remap expert ids onto slots of a fixed-size global LRU slot cache,
+     classifying each rank against the precision ladder (a, b);
+  3. run the SwiGLU expert MLP on MXFP4 weights (or on the 2-bit copy);
+  4. combine the expert outputs with the renormalised weights.
+
+Readings where the pages are silent are stated at each function; the list of
+them is kept with the design notes.  Functions whose result could not be tied
+to anything outside this file would say "parity unpinned" here; every function
+below is pinned by a test (closed form, brute force, independent textbook
+model or a value printed on the pages).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ============================================================================
+# 1. element and scale formats
+# ============================================================================
+
+# FP4 E2M1 value of each 4-bit code (sign, 2 exponent bits, 1 mantissa bit,
+# exponent bias 1, no infinities or NaN).  The format is the MXFP4 element
+# type of the OCP Microscaling spec that P2 cites (References) and that P1
+# names for the routed experts (§The model: FP4 packed into I8 with F8_E8M0
+# scales alongside).
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                        -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0], dtype=np.float64)
+
+
+def e8m0_value(e):
+    """E8M0 scale byte -> 2^(e-127); 255 is NaN (OCP MX).  P1 §The model."""
+    e = np.asarray(e, dtype=np.int64)
+    v = np.ldexp(1.0, e - 127)
+    return np.where(e == 255, np.nan, v)
+
+
+def _e4m3_table() -> np.ndarray:
+    """FP8 E4M3 (OCP 'E4M3FN'): bias 7, exponent field 0 is subnormal
+    (m/8 * 2^-6), S.1111.111 is NaN, no infinities, largest finite 448.
+    P2 names it as the scale type of the 2-bit copies (opening section;
+    §Rig, model & methodology: per-32 fp8-e4m3 scales)."""
+    t = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        s = -1.0 if code & 0x80 else 1.0
+        ef = (code >> 3) & 0xF
+        m = code & 0x7
+        if ef == 0xF and m == 0x7:
+            t[code] = np.nan
+        elif ef == 0:
+            t[code] = s * (m / 8.0) * 2.0 ** -6
+        else:
+            t[code] = s * (1.0 + m / 8.0) * 2.0 ** (ef - 7)
+    return t
+
+
+E4M3_VALUES = _e4m3_table()
+E4M3_MAX = 448.0
+
+
+def e4m3_value(b):
+    return E4M3_VALUES[np.asarray(b, dtype=np.int64)]
+
+
+def int2_level(c):
+    """2-bit code -> signed level (c - 1.5): {-1.5, -0.5, +0.5, +1.5}.
+    P2 gives only '2-bit codes with one fp8 scale per group of 32 weights'
+    (opening section); the symmetric mid-rise codebook is the plain reading."""
+    return np.asarray(c, dtype=np.float64) - 1.5
+
+
+# ============================================================================
+# 2. expert record layout and sizes
+# ============================================================================
+# One expert = three matrices w1 (gate), w3 (up), w2 (down) (P1 §What you
+# actually get: 768 expert tensors per shard = 256 experts x w1, w2, w3),
+# stored [out][in] with one scale per 32 consecutive weights along the input
+# dimension (P1 §Step 2 / Check it divides: FP4 32-element scale blocks).
+# Record order: w1 codes, w3 codes, w2 codes, w1 scales, w3 scales, w2 scales.
+
+def fp4_expert_nbytes(H: int, I: int) -> int:
+    """Bytes of one MXFP4 expert: 3*H*I weights at 4 bits plus one byte per 32
+    weights.  P2 (opening section) prints 13,369,344 bytes for its model."""
+    n = 3 * H * I
+    return n // 2 + n // 32
+
+
+def int2_expert_nbytes(H: int, I: int) -> int:
+    """Bytes of one 2-bit expert: 2 bits per weight plus one fp8 scale per 32
+    (2.25 bits/weight; P2 §Rig, model & methodology: 6.75 MB/expert)."""
+    n = 3 * H * I
+    return n // 4 + n // 32
+
+
+def split_record(rec: np.ndarray, H: int, I: int, bits: int) -> dict:
+    """Slice a record into (codes, scales) per matrix, each [rows, bytes]."""
+    assert bits in (4, 2)
+    per = 8 // bits
+    shapes = {"w1": (I, H), "w3": (I, H), "w2": (H, I)}
+    out, off = {}, 0
+    for name in ("w1", "w3", "w2"):
+        r, c = shapes[name]
+        n = r * c // per
+        out[name + "_codes"] = rec[off:off + n].reshape(r, c // per)
+        off += n
+    for name in ("w1", "w3", "w2"):
+        r, c = shapes[name]
+        n = r * c // 32
+        out[name + "_scales"] = rec[off:off + n].reshape(r, c // 32)
+        off += n
+    assert off == rec.size, (off, rec.size)
+    return out
+
+
+def unpack_fp4_codes(codes: np.ndarray) -> np.ndarray:
+    """[rows, cols/2] bytes -> [rows, cols] 4-bit codes; element 2j is the low
+    nibble of byte j (reading: pages silent, the common I8 packing)."""
+    c = np.empty((codes.shape[0], codes.shape[1] * 2), dtype=np.uint8)
+    c[:, 0::2] = codes & 0x0F
+    c[:, 1::2] = codes >> 4
+    return c
+
+
+def unpack_int2_codes(codes: np.ndarray) -> np.ndarray:
+    """[rows, cols/4] bytes -> [rows, cols] 2-bit codes; element 4j+q is bits
+    2q..2q+1 of byte j (reading)."""
+    c = np.empty((codes.shape[0], codes.shape[1] * 4), dtype=np.uint8)
+    for q in range(4):
+        c[:, q::4] = (codes >> (2 * q)) & 0x3
+    return c
+
+
+def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """W[o, i] = E2M1(code[o, i]) * 2^(scale[o, i // 32] - 127), float64."""
+    c = unpack_fp4_codes(codes)
+    s = e8m0_value(scales)
+    return E2M1_VALUES[c] * np.repeat(s, 32, axis=1)
+
+
+def dequant_int2(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """W[o, i] = (code[o, i] - 1.5) * e4m3(scale[o, i // 32]), float64."""
+    c = unpack_int2_codes(codes)
+    s = e4m3_value(scales)
+    return int2_level(c) * np.repeat(s, 32, axis=1)
+
+
+def expert_weights(rec: np.ndarray, H: int, I: int, prec: int = 0):
+    """(W1 [I,H], W3 [I,H], W2 [H,I]) float64 of one record; prec 0 = FP4,
+    1 = the 2-bit copy."""
+    if prec == 0:
+        p = split_record(rec, H, I, 4)
+        dq = dequant_mxfp4
+    else:
+        p = split_record(rec, H, I, 2)
+        dq = dequant_int2
+    return (dq(p["w1_codes"], p["w1_scales"]),
+            dq(p["w3_codes"], p["w3_scales"]),
+            dq(p["w2_codes"], p["w2_scales"]))
+
+
+# ============================================================================
+# 3. routing
+# ============================================================================
+
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """l[t, e] = x[t] . W_r[e], float64 (tiny configuration computes its
+    router scores from the activations)."""
+    return np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
+
+
+def route(logits: np.ndarray, k: int):
+    """Top-k selection with renormalised weights.
+
+    Each token keeps the k experts with the largest router scores and
+    renormalises their weights so they sum to one (P1 §What the expert cache
+    actually does: the router picks its top_k experts; P2 §Not all six experts
+    matter equally: the router emits six weights per token).  Reading: the
+    score is a softmax over all E logits; ties in the logit go to the lower
+    expert id; experts are emitted in rank order (weight descending).
+
+    Returns ids int32 [T, k] and weights float64 [T, k]."""
+    lg = np.asarray(logits, dtype=np.float64)
+    T, E = lg.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    eid = np.arange(E)
+    for t in range(T):
+        order = np.lexsort((eid, -lg[t]))        # primary: logit desc; secondary: id asc
+        sel = order[:k]
+        p = np.exp(lg[t] - lg[t].max())
+        p = p / p.sum()                          # softmax over all experts
+        ids[t] = sel
+        w[t] = p[sel] / p[sel].sum()             # renormalise over the selected
+    return ids, w
+
+
+# ============================================================================
+# 4. grouping tokens by expert
+# ============================================================================
+
+def group_pairs(ids: np.ndarray, E: int):
+    """Stable counting sort of the T*k (token, rank) pairs by expert id.
+
+    P2 §43 graphs, 43 syncs fires grouped expert kernels; grouping each
+    expert's tokens lets its weights stream once.  Returns counts [E],
+    offsets [E+1] and perm [T*k] (pair index t*k + r, expert-major, ascending
+    pair index within an expert)."""
+    flat = np.asarray(ids, np.int64).reshape(-1)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.argsort(flat, kind="stable").astype(np.int32)
+    return counts, offsets, perm
+
+
+# ============================================================================
+# 5. the expert MLP and the combine
+# ============================================================================
+
+def silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def expert_mlp(x: np.ndarray, W1: np.ndarray, W3: np.ndarray, W2: np.ndarray) -> np.ndarray:
+    """SwiGLU expert: y = W2 (silu(W1 x) * (W3 x)), float64.  x is [H] or
+    [n, H].  Reading: plain SwiGLU, no clamp and no routed scaling factor."""
+    x = np.asarray(x, np.float64)
+    g = x @ W1.T
+    u = x @ W3.T
+    h = silu(g) * u
+    return h @ W2.T
+
+
+def combine(y: np.ndarray, w: np.ndarray, y_shared=None) -> np.ndarray:
+    """out = sum over ranks in rank order of w[r] * y[r] (+ the shared expert
+    with weight one).  P1 §What the expert cache actually does (_expert_gemm
+    takes topk_weights); P2 §Not all six experts matter equally (survivors
+    renormalised).  y is [k, H], w is [k] (zero for dropped ranks)."""
+    out = np.zeros(y.shape[-1], dtype=np.float64)
+    for r in range(y.shape[0]):
+        out = out + w[r] * y[r]
+    if y_shared is not None:
+        out = out + y_shared
+    return out
+
+
+def layer_forward(x, ids, w, get_record, H: int, I: int, shared_rec=None, prec=None):
+    """Full layer for T tokens: out[t] = sum_r w[t,r] * expert_{ids[t,r]}(x[t])
+    (+ shared expert).  get_record(e) returns the FP4 record of expert e.
+    prec (optional [T,k]: 0 FP4, 1 INT2, -1 dropped) with get_record(e, p)
+    selecting the precision.  Returns float64 [T, H]."""
+    x = np.asarray(x, np.float64)
+    T, k = ids.shape
+    out = np.zeros((T, H), dtype=np.float64)
+    cache = {}
+
+    def weights(e, p):
+        key = (int(e), int(p))
+        if key not in cache:
+            rec = get_record(e) if prec is None else get_record(e, p)
+            cache[key] = expert_weights(rec, H, I, p)
+        return cache[key]
+
+    shared_w = expert_weights(shared_rec, H, I, 0) if shared_rec is not None else None
+    for t in range(T):
+        ys = np.zeros((k, H))
+        wt = np.array(w[t], dtype=np.float64)
+        for r in range(k):
+            p = 0 if prec is None else int(prec[t, r])
+            if p < 0:
+                wt[r] = 0.0
+                continue
+            ys[r] = expert_mlp(x[t], *weights(ids[t, r], p))
+        ysh = expert_mlp(x[t], *shared_w) if shared_w is not None else None
+        out[t] = combine(ys, wt, ysh)
+    return out
+
+
+def dense_layer_forward(x, gate: np.ndarray, weights_all, shared_w=None) -> np.ndarray:
+    """Brute force: every expert evaluated for every token and mixed by a dense
+    gate matrix G[t, e] (the renormalised weight on selected experts, zero
+    elsewhere).  Used only to pin the sparse path."""
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    E = len(weights_all)
+    Y = np.stack([expert_mlp(x, *weights_all[e]) for e in range(E)], axis=1)   # [T, E, H]
+    out = np.einsum("te,teh->th", gate, Y)
+    if shared_w is not None:
+        out = out + expert_mlp(x, *shared_w)
+    return out
+
+
+# ============================================================================
+# 6. output rounding
+# ============================================================================
+
+def round_to_bf16(v) -> np.ndarray:
+    """float64 -> nearest bfloat16 (ties to even), returned as float64.
+    bf16 = 8 significant bits, exponent range of float32."""
+    v = np.asarray(v, np.float64)
+    out = np.empty_like(v)
+    flat, of = v.reshape(-1), out.reshape(-1)
+    for i, a in enumerate(flat):
+        if not math.isfinite(a) or a == 0.0:
+            of[i] = a
+            continue
+        e = math.frexp(abs(a))[1] - 1             # |a| in [2^e, 2^(e+1))
+        e = max(e, -126)                          # subnormal spacing below 2^-126
+        q = 2.0 ** (e - 7)
+        r = round(a / q) * q                      # Python round: ties to even, exact
+        of[i] = r if abs(r) <= 3.3895313892515355e38 else math.copysign(math.inf, a)
+    return out
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+# ============================================================================
+# 7. MXFP8 activation quantisation (prefill-sized grouped GEMM)
+# ============================================================================
+# The prefill workload feeds the FP4 weights and FP8 activations to a scaled
+# matrix instruction; activations get one E8M0 scale per 32 consecutive
+# elements along the reduction dimension.  Rule (OCP MX): shared exponent =
+# floor(log2(amax)) - 8 (8 = exponent of E4M3's largest power of two),
+# clamped to the E8M0 range; elements = v / 2^shared rounded to nearest E4M3
+# (ties to even) with saturation at +-448; an all-zero group gets scale
+# code 0 and zero elements.
+
+_E4M3_POS = E4M3_VALUES[:127]          # codes 0x00..0x7E, ascending, finite
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 code, ties to the even code, saturating at +-448."""
+    v = np.asarray(v, np.float64)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")       # first value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(a == _E4M3_POS[hi], hi, code).astype(np.uint8)
+    sign = np.signbit(v).astype(np.uint8) << 7
+    return (code | sign).astype(np.uint8)
+
+
+def quant_mxfp8(v: np.ndarray):
+    """[n, K] values -> (E4M3 codes uint8 [n, K], E8M0 scale bytes uint8 [n, K/32])."""
+    v = np.asarray(v, np.float64)
+    n, K = v.shape
+    g = v.reshape(n, K // 32, 32)
+    amax = np.abs(g).max(axis=2)
+    scales = np.zeros((n, K // 32), dtype=np.uint8)
+    codes = np.zeros((n, K // 32, 32), dtype=np.uint8)
+    for i in range(n):
+        for j in range(K // 32):
+            if amax[i, j] == 0.0:
+                scales[i, j] = 0
+                codes[i, j] = e4m3_encode(g[i, j])            # signed zeros
+                continue
+            e = math.frexp(amax[i, j])[1] - 1                  # floor(log2(amax))
+            sh = min(max(e - 8, -127), 127)
+            scales[i, j] = sh + 127
+            codes[i, j] = e4m3_encode(g[i, j] / 2.0 ** sh)
+    return codes.reshape(n, K), scales
+
+
+def dequant_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    return e4m3_value(codes) * np.repeat(e8m0_value(scales), 32, axis=1)
+
+
+def prefill_forward(x, ids, w, get_record, H: int, I: int, shared_rec=None, tokens=None) -> np.ndarray:
+    """Prefill layer with MXFP8 activations: x is quantised per 32 along H, the
+    SwiGLU output h per 32 along I, each feeding the FP4-weight products.
+    tokens (optional) restricts the evaluation to a subset of token indices.
+    Returns float64 [len(tokens), H]."""
+    x = np.asarray(x, np.float64)
+    T, k = ids.shape
+    tokens = range(T) if tokens is None else tokens
+    wcache = {}
+
+    def weights(e):
+        if e not in wcache:
+            wcache[e] = expert_weights(get_record(e), H, I, 0)
+        return wcache[e]
+
+    def one(xq, W1, W3, W2):
+        g = W1 @ xq
+        u = W3 @ xq
+        h = silu(g) * u
+        hc, hs = quant_mxfp8(h[None, :])
+        return W2 @ dequant_mxfp8(hc, hs)[0]
+
+    shared_w = expert_weights(shared_rec, H, I, 0) if shared_rec is not None else None
+    rows = []
+    for t in tokens:
+        xc, xs = quant_mxfp8(x[t][None, :])
+        xq = dequant_mxfp8(xc, xs)[0]
+        ys = np.stack([one(xq, *weights(int(ids[t, r]))) for r in range(k)])
+        ysh = one(xq, *shared_w) if shared_w is not None else None
+        rows.append(combine(ys, np.asarray(w[t], np.float64), ysh))
+    return np.stack(rows)
+
+
+# ============================================================================
+# 8. the slot cache with the precision ladder
+# ============================================================================
+
+FP4, INT2, DROPPED = 0, 1, -1
+
+
+class SlotCache:
+    """Global LRU slot cache over (layer, expert) pairs with the (a, b) ladder.
+
+    P1 §What the expert cache actually does: a fixed number of expert slots
+    in device memory ('not layers, not experts, slots'), shared by all layers
+    (the cache is global, not per-layer), LRU eviction, expert ids rewritten
+    to slots in place, only misses copied from the host banks.
+    P2 §Not all six experts matter equally: ranks 1..a always FP4 (fetched on
+    a miss); ranks a+1..b FP4 if resident, else the 2-bit copy; ranks > b used
+    if resident, dropped otherwise; survivors renormalised.
+
+    Readings where the pages are silent:
+      * residency for a token's classification is read once, before any of
+        that token's fetches;
+      * slots used by any rank of the call are protected from eviction for
+        the rest of the call;
+      * fetches are processed in rank order; each hit or fetch stamps the
+        slot with the next value of a global clock; the victim of a fetch is
+        the lowest-index empty slot, else the unprotected slot with the
+        oldest stamp;
+      * 2-bit copies are not cached: every use is a fresh copy into a staging
+        area, index t*(b-a) + (rank-a-1) within the call;
+      * if every rank of a token is dropped, all its weights are zero.
+    """
+
+    def __init__(self, L: int, E: int, S: int, k: int, a: int, b: int):
+        assert 0 <= a <= b <= k and S >= 1
+        self.L, self.E, self.S, self.k, self.a, self.b = L, E, S, k, a, b
+        self.map = np.full(L * E, -1, dtype=np.int64)      # pair -> slot
+        self.owner = np.full(S, -1, dtype=np.int64)        # slot -> pair
+        self.stamp = np.zeros(S, dtype=np.int64)           # 0 = empty
+        self.clock = 0
+        self.hits = self.misses = self.int2 = self.drops = 0
+
+    def resident(self, layer: int, e: int) -> bool:
+        return self.map[layer * self.E + e] >= 0
+
+    def step(self, layer: int, ids: np.ndarray, w: np.ndarray):
+        """One call for T tokens of one layer.  ids [T,k] expert ids and w
+        [T,k] weights in rank order.  Returns (slot int32 [T,k], prec int8
+        [T,k], w' float64 [T,k], copies list of (kind, layer, expert, dest))."""
+        ids = np.asarray(ids).reshape(-1, self.k)
+        w = np.asarray(w, np.float64).reshape(-1, self.k)
+        T, k, a, b, E = ids.shape[0], self.k, self.a, self.b, self.E
+        assert T * k <= self.S
+        slot = np.full((T, k), -1, dtype=np.int32)
+        prec = np.full((T, k), DROPPED, dtype=np.int8)
+        wout = np.zeros((T, k), dtype=np.float64)
+        copies = []
+        protected = set()
+        for t in range(T):
+            res = [self.resident(layer, int(e)) for e in ids[t]]      # snapshot
+            cls = []
+            for r in range(k):
+                rank = r + 1
+                if rank <= a:
+                    cls.append(FP4)
+                elif rank <= b:
+                    cls.append(FP4 if res[r] else INT2)
+                else:
+                    cls.append(FP4 if res[r] else DROPPED)
+            for r in range(k):
+                if cls[r] == FP4 and res[r]:
+                    protected.add(int(self.map[layer * E + int(ids[t, r])]))
+            for r in range(k):
+                e = int(ids[t, r])
+                pair = layer * E + e
+                if cls[r] == FP4 and res[r]:
+                    s = int(self.map[pair])
+                    self.clock += 1
+                    self.stamp[s] = self.clock
+                    slot[t, r], prec[t, r] = s, FP4
+                    self.hits += 1
+                elif cls[r] == FP4:
+                    cand = [s for s in range(self.S) if s not in protected]
+                    s = min(cand, key=lambda q: (self.stamp[q], q))   # empty (0) first, then oldest
+                    if self.owner[s] >= 0:
+                        self.map[self.owner[s]] = -1
+                    self.owner[s] = pair
+                    self.map[pair] = s
+                    self.clock += 1
+                    self.stamp[s] = self.clock
+                    protected.add(s)
+                    slot[t, r], prec[t, r] = s, FP4
+                    copies.append(("fp4", layer, e, s))
+                    self.misses += 1
+                elif cls[r] == INT2:
+                    st = t * (b - a) + (r + 1 - a - 1)
+                    slot[t, r], prec[t, r] = st, INT2
+                    copies.append(("int2", layer, e, st))
+                    self.int2 += 1
+                else:
+                    self.drops += 1
+            keep = prec[t] != DROPPED
+            tot = w[t][keep].sum()
+            if tot > 0:
+                wout[t][keep] = w[t][keep] / tot
+        return slot, prec, wout, copies
+
+    def slot_map(self) -> np.ndarray:
+        return self.map.astype(np.int32).copy()
