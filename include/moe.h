@@ -1,0 +1,202 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed MXFP4 mixture-of-experts layer.
+ *
+ * The layer follows two pages:
+ *   [P1] "Running DeepSeek-V4-Flash across four free GPUs",
+ *        §What the expert cache actually does: the router picks top_k experts
+ *        per token, the cache rewrites expert ids to slots of a fixed-size
+ *        slot cache in place, only misses are copied from pinned host banks,
+ *        and the expert GEMM indexes the slot buffers with the token weights.
+ *   [P2] "An elephant through a straw",
+ *        §Not all six experts matter equally: the (a,b) precision ladder and
+ *        the renormalisation of the surviving weights;
+ *        §43 graphs, 43 syncs: one host sync per layer reads the router's
+ *        picks, classifies them, then fires the grouped expert kernels.
+ *
+ * Conventions (every entry point):
+ *   - Pointers are DEVICE memory unless the parameter says "host".  The caller
+ *     owns every buffer and stream; the library never frees caller memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     GPU work is enqueued asynchronously on it; no entry point synchronises
+ *     except moe_cache_ensure (one host sync per call, as in [P2] §43 graphs).
+ *   - Arrays are dense row-major.  Sizes are int.
+ *   - On error an entry point returns a non-zero moe_status, launches nothing
+ *     (validation happens before any launch), and moe_last_error() returns a
+ *     message for the calling thread.  Nothing is thrown across the ABI.
+ *
+ * Expert record (one expert's weights, contiguous bytes):
+ *     w1 codes | w3 codes | w2 codes | w1 scales | w3 scales | w2 scales
+ *   w1 = gate [I][H], w3 = up [I][H], w2 = down [H][I]  ([P1] §What you
+ *   actually get: three matrices w1, w2, w3 per expert), each [out][in]
+ *   row-major with one scale per 32 consecutive inputs ([P1] §Step 2, Check
+ *   it divides: FP4 32-element scale blocks).
+ *   MXFP4 record: FP4 E2M1 codes, two per byte, element 2j in the low nibble;
+ *     E8M0 scale bytes (value 2^(e-127)).  ([P1] §The model: FP4 packed in I8
+ *     tensors with F8_E8M0 scales; [P2] opening section: 13,369,344 bytes per
+ *     expert at H=4096, I=2048.)  Size: moe_fp4_expert_bytes(H, I).
+ *   2-bit record: codes four per byte, element 4j+q in bits 2q..2q+1, value
+ *     (code - 1.5) * scale; FP8 E4M3 scale bytes.  ([P2] opening section and
+ *     §Rig, model & methodology: 2-bit codes, one fp8 e4m3 scale per 32,
+ *     2.25 bits per weight.)  Size: moe_int2_expert_bytes(H, I).
+ *
+ * Supported shapes: H and I multiples of 32 with H/32 and I/32 either a power
+ * of two <= 64 or a multiple of 64 up to 256 (H, I <= 8192); 1 <= k <= E <= 1024,
+ * k <= 64.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* NULL pointer, bad enum, k > E, a > b, ... */
+  MOE_ESHAPE = 2,        /* unsupported H, I, E, T or k */
+  MOE_ECACHE_SMALL = 3,  /* slot cache below its floor */
+  MOE_ENOMEM = 4,        /* workspace or host allocation too small / failed */
+  MOE_EHIP = 5,          /* a HIP runtime call or kernel launch failed */
+  MOE_ESTATE = 6         /* call out of order (e.g. cache used after an error) */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+/* Message describing the calling thread's last non-OK return ("" if none).
+ * The pointer stays valid until the thread's next failing call. */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+/* Bytes of one MXFP4 / 2-bit expert record (host arithmetic, no GPU). */
+size_t moe_fp4_expert_bytes(int H, int I);
+size_t moe_int2_expert_bytes(int H, int I);
+
+/* Where a layer's expert records live.
+ *   fp4_base + s * fp4_stride       : MXFP4 record of slot s, 0 <= s < num_slots
+ *                                     (for a fully resident layer, slot = expert id)
+ *   int2_base + j * int2_stride     : 2-bit record of staging entry j, 0 <= j < num_int2
+ *                                     (NULL / 0 when no 2-bit copies are used)
+ *   shared                          : MXFP4 record of the always-on shared expert
+ *                                     ([P2] §Rig, model & methodology: 256 routed experts
+ *                                     plus 1 shared per layer), weight 1.0, outside the
+ *                                     renormalisation; NULL = no shared expert.
+ * Strides must be >= the record size and multiples of 16 bytes; records 16-byte aligned. */
+typedef struct {
+  int H, I;
+  const uint8_t* fp4_base;
+  size_t fp4_stride;
+  int num_slots;
+  const uint8_t* int2_base;
+  size_t int2_stride;
+  int num_int2;
+  const uint8_t* shared;
+} moe_layer;
+
+/* ---------------------------------------------------------------- routing */
+
+/* Router scores of the tiny configuration: logits[t][e] = sum_h x[t][h] * w_router[e][h],
+ * fp32 accumulation.  x [T][H] in xt (MOE_F32 or MOE_BF16), w_router [E][H] fp32,
+ * logits [T][E] fp32 out. */
+moe_status moe_router_logits(const void* x, moe_dtype xt, const float* w_router, int T, int E, int H,
+                             float* logits, moe_stream_t stream);
+
+/* Top-k routing with renormalised weights ([P1] §What the expert cache actually does:
+ * the router picks its top_k experts per token; [P2] §Not all six experts matter
+ * equally: six weights per token, renormalised).  Softmax scoring; the k largest
+ * logits win, ties to the lower expert id; outputs in rank order (weight
+ * descending).  The weights equal softmax over the selected logits (the full
+ * softmax denominator cancels in the renormalisation).
+ *   logits [T][E] fp32 (finite), ids [T][k] int32 out, w [T][k] fp32 out.
+ * T may be 0 (no launch). */
+moe_status moe_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                     moe_stream_t stream);
+
+/* Stable grouping of n keys in [0, nkeys): counts [nkeys], offsets [nkeys+1]
+ * (exclusive prefix of counts), perm [n] = indices of the keys sorted by key,
+ * ascending index within a key.  Used to group the (token, rank) pairs by
+ * expert so each expert's weights stream once ([P2] §43 graphs, 43 syncs:
+ * grouped expert kernels).  keys int32 [n] (out-of-range keys are not counted
+ * and not placed).  n <= 1<<20, nkeys <= 4096. */
+moe_status moe_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int32_t* offsets,
+                     int32_t* perm, moe_stream_t stream);
+
+/* ------------------------------------------------------------ expert MLP */
+
+/* Workspace bytes moe_expert_forward needs for T tokens, top-k, with or without
+ * the shared expert. */
+size_t moe_expert_workspace_bytes(int H, int I, int T, int k, int has_shared);
+
+/* SwiGLU expert MLP for every selected (token, rank) and the shared expert:
+ *     y = W2 (silu(W1 x) * (W3 x)), dequantised in registers, fp32 accumulation.
+ * ([P1] §What the expert cache actually does: _expert_gemm over the slot
+ * buffers; [P2] §43 graphs, 43 syncs: grouped expert kernels.)
+ *   x        [T][H] activations in xt
+ *   slot_ids [T][k] int32: record index (FP4 slot, or 2-bit staging entry)
+ *   prec     [T][k] int8 or NULL (= all FP4): 0 MXFP4, 1 2-bit copy, -1 dropped
+ *   w        [T][k] fp32 renormalised weights, or NULL
+ *   out      if w != NULL: [T][H] in ot = sum over non-dropped ranks, in rank order,
+ *                          of w * y (+ the shared expert's y), one final rounding
+ *            if w == NULL: [T][k + has_shared][H] fp32 per-rank outputs (rank k =
+ *                          shared); dropped ranks are zero
+ *   workspace: device, >= moe_expert_workspace_bytes(...), 256-byte aligned.
+ * Slot ids outside [0, num_slots) (or [0, num_int2) for 2-bit) are treated as dropped. */
+moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype xt, int T, int k,
+                              const int32_t* slot_ids, const int8_t* prec, const float* w,
+                              void* out, moe_dtype ot, void* workspace, size_t workspace_bytes,
+                              moe_stream_t stream);
+
+/* Weighted combine ([P1] §What the expert cache actually does: the expert GEMM
+ * takes topk_weights; [P2] §Not all six experts matter equally: survivors
+ * renormalised):  out[t] = sum_{r < k, prec[t][r] >= 0} w[t][r] * y[t][r]
+ * (+ y[t][k] if has_shared), summed in rank order, one rounding to ot.
+ *   y [T][k + has_shared][H] fp32, w [T][k] fp32, prec [T][k] int8 or NULL,
+ *   out [T][H] in ot. */
+moe_status moe_combine(const float* y, const float* w, const int8_t* prec, int T, int k, int H,
+                       int has_shared, void* out, moe_dtype ot, moe_stream_t stream);
+
+/* Dequantise one matrix of a record to fp32 [rows][cols] with the same decode
+ * path the expert kernels use (bit-exact check of the formats).
+ *   record: device record; prec 0 = MXFP4, 1 = 2-bit; matrix 0 = w1, 1 = w3, 2 = w2. */
+moe_status moe_debug_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out,
+                             moe_stream_t stream);
+
+/* ------------------------------------------------------------ timing */
+
+/* Kernel kinds reported by moe_profile_end. */
+typedef enum {
+  MOE_PROF_ROUTE = 0,
+  MOE_PROF_ROUTER_LOGITS = 1,
+  MOE_PROF_GATEUP = 2,      /* decode gate/up GEMV + SwiGLU */
+  MOE_PROF_DOWN = 3,        /* decode down GEMV */
+  MOE_PROF_COMBINE = 4,
+  MOE_PROF_GROUP = 5,
+  MOE_PROF_PLAN = 6,        /* pair keys / active-group list */
+  MOE_PROF_QUANT = 7,       /* MXFP8 activation quantisation */
+  MOE_PROF_GEMM_GATEUP = 8, /* prefill grouped GEMM, gate/up */
+  MOE_PROF_GEMM_DOWN = 9,   /* prefill grouped GEMM, down */
+  MOE_PROF_DEQUANT = 10,
+  MOE_PROF_KINDS = 16
+} moe_prof_kind;
+
+/* Start timing the library's kernels: every launch made after this call is
+ * bracketed by two HIP events recorded on its own stream (up to max_launches
+ * launches; later ones are not timed).  Host-side bookkeeping only. */
+moe_status moe_profile_begin(int max_launches);
+
+/* Stop timing, wait for the recorded events and report, per moe_prof_kind,
+ * the summed kernel time in milliseconds (total_ms[nkinds], host) and the
+ * number of timed launches (counts[nkinds], host).  Either may be NULL. */
+moe_status moe_profile_end(double* total_ms, int* counts, int nkinds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

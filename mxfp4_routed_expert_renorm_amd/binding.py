@@ -1,0 +1,202 @@
+"""ctypes binding of libmoe_mi355x.so: argument marshalling only.
+
+Every function here forwards to the C entry point of the same name in
+include/moe.h.  Tensors are torch tensors on the GPU (torch supplies device
+memory and streams); their data pointers, sizes and the current HIP stream are
+passed through unchanged.  Nothing is computed in Python, and there is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+FP4, INT2, DROPPED = 0, 1, -1
+
+c_int, c_size_t, c_void_p, c_char_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_char_p
+
+
+class MoeError(RuntimeError):
+    def __init__(self, name, status, msg):
+        super().__init__(f"{name} failed with status {status}: {msg}")
+        self.status = status
+
+
+class moe_layer(ctypes.Structure):
+    _fields_ = [
+        ("H", c_int), ("I", c_int),
+        ("fp4_base", c_void_p), ("fp4_stride", c_size_t), ("num_slots", c_int),
+        ("int2_base", c_void_p), ("int2_stride", c_size_t), ("num_int2", c_int),
+        ("shared", c_void_p),
+    ]
+
+
+class moe_cache_desc(ctypes.Structure):
+    _fields_ = [
+        ("L", c_int), ("E", c_int), ("H", c_int), ("I", c_int),
+        ("num_slots", c_int), ("k", c_int), ("ladder_a", c_int), ("ladder_b", c_int),
+        ("max_tokens", c_int),
+        ("fp4_host", c_void_p), ("int2_host", c_void_p),
+        ("fp4_arena", c_void_p), ("int2_staging", c_void_p),
+    ]
+
+
+class moe_cache_stats(ctypes.Structure):
+    _fields_ = [
+        ("calls", ctypes.c_int64), ("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
+        ("int2_uses", ctypes.c_int64), ("drops", ctypes.c_int64),
+        ("bytes_h2d", ctypes.c_int64), ("evictions", ctypes.c_int64),
+    ]
+
+
+_SIGS = {
+    "moe_last_error": (c_char_p, []),
+    "moe_version": (c_char_p, []),
+    "moe_fp4_expert_bytes": (c_size_t, [c_int, c_int]),
+    "moe_int2_expert_bytes": (c_size_t, [c_int, c_int]),
+    "moe_router_logits": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p]),
+    "moe_route": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "moe_group": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_expert_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+    "moe_expert_forward": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
+    "moe_combine": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p]),
+    "moe_debug_dequant": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
+    "moe_profile_begin": (c_int, [c_int]),
+    "moe_profile_end": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int), c_int]),
+}
+
+_lib = None
+
+
+def load():
+    """Load the built library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(or python -m mxfp4_routed_expert_renorm_amd.build)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(name, st):
+    if st != 0:
+        raise MoeError(name, st, load().moe_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    import torch
+    return c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t):
+    import torch
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------------- sizes
+
+def moe_version() -> str:
+    return load().moe_version().decode()
+
+
+def moe_fp4_expert_bytes(H, I) -> int:
+    return load().moe_fp4_expert_bytes(H, I)
+
+
+def moe_int2_expert_bytes(H, I) -> int:
+    return load().moe_int2_expert_bytes(H, I)
+
+
+def moe_expert_workspace_bytes(H, I, T, k, has_shared) -> int:
+    return load().moe_expert_workspace_bytes(H, I, T, k, int(bool(has_shared)))
+
+
+# -------------------------------------------------------------------- routing
+
+def moe_router_logits(x, w_router, logits, stream=None):
+    T, H = x.shape
+    E = w_router.shape[0]
+    _check("moe_router_logits", load().moe_router_logits(_p(x), _dt(x), _p(w_router), T, E, H, _p(logits),
+                                                         _stream(stream)))
+    return logits
+
+
+def moe_route(logits, k, ids, w, stream=None):
+    T, E = logits.shape
+    _check("moe_route", load().moe_route(_p(logits), T, E, k, _p(ids), _p(w), _stream(stream)))
+    return ids, w
+
+
+def moe_group(keys, nkeys, counts, offsets, perm, stream=None):
+    n = keys.numel()
+    _check("moe_group", load().moe_group(_p(keys), n, nkeys, _p(counts), _p(offsets), _p(perm), _stream(stream)))
+    return counts, offsets, perm
+
+
+# ----------------------------------------------------------------- expert MLP
+
+def make_layer(H, I, fp4_base=None, fp4_stride=0, num_slots=0, int2_base=None, int2_stride=0, num_int2=0,
+               shared=None) -> moe_layer:
+    """A moe_layer descriptor from device tensors (uint8 records)."""
+    return moe_layer(H, I, _p(fp4_base), fp4_stride, num_slots, _p(int2_base), int2_stride, num_int2, _p(shared))
+
+
+def moe_expert_forward(layer: moe_layer, x, T, k, slot_ids, prec, w, out, workspace, stream=None):
+    ot = _dt(out)
+    st = load().moe_expert_forward(ctypes.byref(layer), _p(x), _dt(x), T, k, _p(slot_ids), _p(prec), _p(w),
+                                   _p(out), ot, _p(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream))
+    _check("moe_expert_forward", st)
+    return out
+
+
+def moe_combine(y, w, prec, T, k, H, has_shared, out, stream=None):
+    st = load().moe_combine(_p(y), _p(w), _p(prec), T, k, H, int(bool(has_shared)), _p(out), _dt(out),
+                            _stream(stream))
+    _check("moe_combine", st)
+    return out
+
+
+def moe_debug_dequant(record, H, I, prec, matrix, out, stream=None):
+    _check("moe_debug_dequant", load().moe_debug_dequant(_p(record), H, I, prec, matrix, _p(out), _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------- timing
+
+PROF_KINDS = ("route", "router_logits", "gateup", "down", "combine", "group", "plan", "quant",
+              "gemm_gateup", "gemm_down", "dequant")
+MOE_PROF_KINDS = 16
+
+
+def moe_profile_begin(max_launches: int):
+    _check("moe_profile_begin", load().moe_profile_begin(max_launches))
+
+
+def moe_profile_end() -> dict:
+    """{kind: (total_ms, launches)} for every kind that ran."""
+    tot = (ctypes.c_double * MOE_PROF_KINDS)()
+    cnt = (c_int * MOE_PROF_KINDS)()
+    _check("moe_profile_end", load().moe_profile_end(tot, cnt, MOE_PROF_KINDS))
+    return {PROF_KINDS[i]: (tot[i], cnt[i]) for i in range(len(PROF_KINDS)) if cnt[i] > 0}

@@ -1,0 +1,176 @@
+// C entry points of the MoE library: validate every argument, then enqueue.
+//
+// Validation happens before any launch and fails with a targeted message
+// rather than producing wrong math, the behaviour "Running DeepSeek-V4-Flash
+// across four free GPUs" (§Step 2, Check it divides; §Step 7, the slot-count
+// floor) asks of a serving runtime.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+
+namespace moe {
+
+static thread_local std::string g_last_error;
+
+void set_error(const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+moe_status launch_router_logits(const void* x, moe_dtype xt, const float* wr, int T, int E, int H, float* logits,
+                                hipStream_t s);
+moe_status launch_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out, hipStream_t s);
+bool decode_shape_ok(int H, int I);
+size_t decode_plan_ints(int P);
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+}  // namespace moe
+
+using namespace moe;
+
+#define REQUIRE(cond, st, ...)          \
+  do {                                  \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+size_t moe_fp4_expert_bytes(int H, int I) {
+  if (H <= 0 || I <= 0) return 0;
+  return record_layout(H, I, 4).bytes;
+}
+
+size_t moe_int2_expert_bytes(int H, int I) {
+  if (H <= 0 || I <= 0) return 0;
+  return record_layout(H, I, 2).bytes;
+}
+
+moe_status moe_router_logits(const void* x, moe_dtype xt, const float* w_router, int T, int E, int H, float* logits,
+                             moe_stream_t stream) {
+  REQUIRE(T >= 0 && E >= 1 && H >= 1, MOE_ESHAPE, "moe_router_logits: bad sizes T=%d E=%d H=%d", T, E, H);
+  REQUIRE(xt == MOE_F32 || xt == MOE_BF16, MOE_EINVAL, "moe_router_logits: bad dtype %d", (int)xt);
+  REQUIRE(T == 0 || (x && w_router && logits), MOE_EINVAL, "moe_router_logits: NULL pointer");
+  return launch_router_logits(x, xt, w_router, T, E, H, logits, (hipStream_t)stream);
+}
+
+moe_status moe_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, moe_stream_t stream) {
+  REQUIRE(T >= 0, MOE_ESHAPE, "moe_route: T=%d < 0", T);
+  REQUIRE(E >= 1 && E <= 1024, MOE_ESHAPE, "moe_route: E=%d outside 1..1024", E);
+  REQUIRE(k >= 1 && k <= E && k <= 64, MOE_EINVAL, "moe_route: k=%d must satisfy 1 <= k <= min(E=%d, 64)", k, E);
+  REQUIRE(T == 0 || (logits && ids && w), MOE_EINVAL, "moe_route: NULL pointer");
+  return launch_route(logits, T, E, k, ids, w, (hipStream_t)stream);
+}
+
+moe_status moe_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int32_t* offsets, int32_t* perm,
+                     moe_stream_t stream) {
+  REQUIRE(n >= 0 && n <= (1 << 20), MOE_ESHAPE, "moe_group: n=%d outside 0..2^20", n);
+  REQUIRE(nkeys >= 1 && nkeys <= 4096, MOE_ESHAPE, "moe_group: nkeys=%d outside 1..4096", nkeys);
+  REQUIRE(counts && offsets && (n == 0 || (keys && perm)), MOE_EINVAL, "moe_group: NULL pointer");
+  return launch_group(keys, n, nkeys, counts, offsets, perm, (hipStream_t)stream);
+}
+
+size_t moe_expert_workspace_bytes(int H, int I, int T, int k, int has_shared) {
+  if (H <= 0 || I <= 0 || T < 0 || k <= 0) return 0;
+  const size_t P = (size_t)T * (size_t)(k + (has_shared ? 1 : 0));
+  return align256(P * I * 4) + align256(P * H * 4) + align256(decode_plan_ints((int)P) * 4);
+}
+
+static moe_status check_layer(const moe_layer* L, const char* who) {
+  REQUIRE(L, MOE_EINVAL, "%s: layer is NULL", who);
+  REQUIRE(decode_shape_ok(L->H, L->I), MOE_ESHAPE,
+          "%s: H=%d I=%d unsupported (need multiples of 32 with H/32, I/32 a power of two in 4..64 or 128/256)", who,
+          L->H, L->I);
+  const size_t fb = record_layout(L->H, L->I, 4).bytes, ib = record_layout(L->H, L->I, 2).bytes;
+  REQUIRE(L->fp4_base || L->num_slots == 0, MOE_EINVAL, "%s: fp4_base is NULL with num_slots=%d", who, L->num_slots);
+  REQUIRE(L->num_slots >= 0 && L->num_int2 >= 0, MOE_EINVAL, "%s: negative slot counts", who);
+  REQUIRE(L->num_slots == 0 || (L->fp4_stride >= fb && L->fp4_stride % 16 == 0), MOE_EINVAL,
+          "%s: fp4_stride=%zu must be >= %zu and a multiple of 16", who, L->fp4_stride, fb);
+  REQUIRE(!L->int2_base || L->num_int2 == 0 || (L->int2_stride >= ib && L->int2_stride % 16 == 0), MOE_EINVAL,
+          "%s: int2_stride=%zu must be >= %zu and a multiple of 16", who, L->int2_stride, ib);
+  REQUIRE(aligned(L->fp4_base, 16) && aligned(L->int2_base, 16) && aligned(L->shared, 16), MOE_EINVAL,
+          "%s: expert records must be 16-byte aligned", who);
+  return MOE_OK;
+}
+
+moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype xt, int T, int k,
+                              const int32_t* slot_ids, const int8_t* prec, const float* w, void* out, moe_dtype ot,
+                              void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  moe_status st = check_layer(layer, "moe_expert_forward");
+  if (st != MOE_OK) return st;
+  REQUIRE(T >= 0 && T <= 65536, MOE_ESHAPE, "moe_expert_forward: T=%d outside 0..65536", T);
+  REQUIRE(k >= 1 && k <= 64, MOE_EINVAL, "moe_expert_forward: k=%d outside 1..64", k);
+  REQUIRE(xt == MOE_F32 || xt == MOE_BF16, MOE_EINVAL, "moe_expert_forward: bad activation dtype %d", (int)xt);
+  REQUIRE(w || ot == MOE_F32, MOE_EINVAL, "moe_expert_forward: per-rank outputs (w == NULL) are fp32");
+  REQUIRE(ot == MOE_F32 || ot == MOE_BF16, MOE_EINVAL, "moe_expert_forward: bad output dtype %d", (int)ot);
+  if (T == 0) return MOE_OK;
+  REQUIRE(x && slot_ids && out && workspace, MOE_EINVAL, "moe_expert_forward: NULL pointer");
+  REQUIRE(aligned(x, 16) && aligned(out, 16) && aligned(workspace, 256), MOE_EINVAL,
+          "moe_expert_forward: x/out must be 16-byte and workspace 256-byte aligned");
+  const int has_shared = layer->shared ? 1 : 0;
+  const size_t need = moe_expert_workspace_bytes(layer->H, layer->I, T, k, has_shared);
+  REQUIRE(workspace_bytes >= need, MOE_ENOMEM, "moe_expert_forward: workspace %zu bytes < %zu needed",
+          workspace_bytes, need);
+  const int nkeys = layer->num_slots + (layer->int2_base ? layer->num_int2 : 0) + 1;
+  REQUIRE(T == 1 || nkeys <= 4096, MOE_ESHAPE,
+          "moe_expert_forward: batched grouping supports at most 4095 slots + 2-bit entries (got %d)", nkeys - 1);
+  const int K1 = k + has_shared;
+  const size_t P = (size_t)T * K1;
+  char* ws = (char*)workspace;
+  float* h = (float*)ws;
+  float* y = (float*)(ws + align256(P * layer->I * 4));
+  int32_t* plan = (int32_t*)(ws + align256(P * layer->I * 4) + align256(P * layer->H * 4));
+  float* yout = w ? y : (float*)out;
+  hipStream_t s = (hipStream_t)stream;
+  st = launch_expert_decode(layer, x, xt, T, k, slot_ids, prec, h, yout, plan, s);
+  if (st != MOE_OK) return st;
+  if (w) return launch_combine(y, w, prec, T, k, layer->H, has_shared, out, ot, s);
+  return MOE_OK;
+}
+
+moe_status moe_combine(const float* y, const float* w, const int8_t* prec, int T, int k, int H, int has_shared,
+                       void* out, moe_dtype ot, moe_stream_t stream) {
+  REQUIRE(T >= 0 && k >= 1 && H >= 4 && H % 4 == 0, MOE_ESHAPE, "moe_combine: bad sizes T=%d k=%d H=%d", T, k, H);
+  REQUIRE(ot == MOE_F32 || ot == MOE_BF16, MOE_EINVAL, "moe_combine: bad output dtype %d", (int)ot);
+  if (T == 0) return MOE_OK;
+  REQUIRE(y && w && out, MOE_EINVAL, "moe_combine: NULL pointer");
+  REQUIRE(aligned(y, 16) && aligned(out, 8), MOE_EINVAL, "moe_combine: y must be 16-byte, out 8-byte aligned");
+  return launch_combine(y, w, prec, T, k, H, has_shared ? 1 : 0, out, ot, (hipStream_t)stream);
+}
+
+moe_status moe_debug_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out,
+                             moe_stream_t stream) {
+  REQUIRE(H > 0 && I > 0 && H % 32 == 0 && I % 32 == 0, MOE_ESHAPE, "moe_debug_dequant: H=%d I=%d", H, I);
+  REQUIRE(prec == 0 || prec == 1, MOE_EINVAL, "moe_debug_dequant: prec=%d", prec);
+  REQUIRE(matrix >= 0 && matrix <= 2, MOE_EINVAL, "moe_debug_dequant: matrix=%d", matrix);
+  REQUIRE(record && out, MOE_EINVAL, "moe_debug_dequant: NULL pointer");
+  REQUIRE(aligned(record, 4), MOE_EINVAL, "moe_debug_dequant: record must be 4-byte aligned");
+  return launch_dequant(record, H, I, prec, matrix, out, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,152 @@
+// Internal helpers of the gfx950 MoE library: device-side format decoding,
+// wavefront reductions, the expert record layout and host error plumbing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include <string>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// expert record layout (shared by every kernel; the byte order is fixed by
+// the public header): w1 codes | w3 codes | w2 codes | w1 scales | w3 scales
+// | w2 scales, each matrix [out][in] row-major, one scale per 32 inputs.
+struct RecordLayout {
+  size_t w1c, w3c, w2c, w1s, w3s, w2s, bytes;
+};
+
+__host__ __device__ inline RecordLayout record_layout(int H, int I, int bits) {
+  const size_t n = (size_t)H * (size_t)I;
+  const size_t cb = n * (size_t)bits / 8;  // code bytes per matrix
+  const size_t sb = n / 32;                // scale bytes per matrix
+  RecordLayout L;
+  L.w1c = 0;
+  L.w3c = cb;
+  L.w2c = 2 * cb;
+  L.w1s = 3 * cb;
+  L.w3s = 3 * cb + sb;
+  L.w2s = 3 * cb + 2 * sb;
+  L.bytes = 3 * cb + 3 * sb;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// scalar formats
+
+// E8M0 scale byte -> float 2^(e-127); 0 -> 2^-127 (a float32 subnormal);
+// 255 -> NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  uint32_t bits = e << 23;
+  bits = (e == 0u) ? 0x00400000u : bits;
+  bits = (e == 255u) ? 0x7fc00000u : bits;
+  return __uint_as_float(bits);
+}
+
+// FP8 E4M3 (OCP E4M3FN: bias 7, no infinities, S.1111.111 = NaN) -> float.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t s = (b >> 7) & 1u, ef = (b >> 3) & 15u, m = b & 7u;
+  float v;
+  if (ef == 0u) {
+    v = (float)m * 0.001953125f;  // m/8 * 2^-6
+  } else {
+    v = __uint_as_float(((ef + 120u) << 23) | (m << 20));
+  }
+  if (ef == 15u && m == 7u) v = __uint_as_float(0x7fc00000u);
+  return s ? -v : v;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// float -> bfloat16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// packed conversions (gfx950 scaled FP4 converts, scale 1.0: the block scale
+// is applied once per 32 products)
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// element 2j of a byte is its low nibble; sel picks the byte of the dword
+template <int SEL>
+__device__ __forceinline__ v2f fp4x2_to_f32(uint32_t dw) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(dw, 1.0f, SEL);
+}
+
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t dw) {
+  v2bf r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, 1.0f, SEL);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// wavefront reductions over aligned groups of N lanes (N a power of two <= 64)
+
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = N / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// host-side error plumbing
+
+void set_error(const char* fmt, ...);
+moe_status fail(moe_status st, const char* fmt, ...);
+
+#define MOE_HIP_CHECK(expr)                                                      \
+  do {                                                                           \
+    hipError_t _e = (expr);                                                      \
+    if (_e != hipSuccess)                                                        \
+      return ::moe::fail(MOE_EHIP, "%s failed: %s", #expr, hipGetErrorString(_e)); \
+  } while (0)
+
+#define MOE_LAUNCH_CHECK()                                                       \
+  do {                                                                           \
+    hipError_t _e = hipGetLastError();                                           \
+    if (_e != hipSuccess)                                                        \
+      return ::moe::fail(MOE_EHIP, "kernel launch failed: %s", hipGetErrorString(_e)); \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// event timing of the library's launches (off unless moe_profile_begin ran)
+
+class ProfScope {
+ public:
+  ProfScope(int kind, hipStream_t s);
+  ~ProfScope();
+
+ private:
+  int idx_;
+  hipStream_t s_;
+};
+
+// ---------------------------------------------------------------------------
+// internal launchers (each validates nothing: the C entry points do)
+
+struct ExpertArgs;  // defined in expert_decode.hip
+moe_status launch_expert_decode(const moe_layer* L, const void* x, moe_dtype xt, int T, int k,
+                                const int32_t* slot_ids, const int8_t* prec, float* h, float* y,
+                                int32_t* plan, hipStream_t s);
+moe_status launch_combine(const float* y, const float* w, const int8_t* prec, int T, int k, int H,
+                          int has_shared, void* out, moe_dtype ot, hipStream_t s);
+moe_status launch_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, hipStream_t s);
+
+}  // namespace moe

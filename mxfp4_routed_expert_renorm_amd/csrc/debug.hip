@@ -1,0 +1,51 @@
+// Dequantise one matrix of an expert record to fp32 with the same decode
+// steps the expert kernels use: the gfx950 scaled FP4 convert (scale 1.0)
+// times the E8M0 block scale, or the 2-bit level (code - 1.5) times the E4M3
+// block scale.  Lets the formats be checked bit for bit against the oracle.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+// one thread per 4 code bytes (8 FP4 or 16 two-bit elements)
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales, int rows, int cols,
+                                                      int bits, float* __restrict__ out) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const int per_dw = 32 / bits;  // elements per dword
+  const long ndw = (long)rows * cols / per_dw;
+  if (idx >= ndw) return;
+  const long e0 = idx * per_dw;
+  const int r = (int)(e0 / cols), c0 = (int)(e0 % cols);
+  const uint32_t dw = ((const uint32_t*)codes)[idx];
+  const uint32_t sb = scales[(size_t)r * (cols / 32) + c0 / 32];
+  float* o = out + e0;
+  if (bits == 4) {
+    const float s = e8m0_to_f32(sb);
+    const v2f a0 = fp4x2_to_f32<0>(dw), a1 = fp4x2_to_f32<1>(dw), a2 = fp4x2_to_f32<2>(dw),
+              a3 = fp4x2_to_f32<3>(dw);
+    o[0] = a0.x * s; o[1] = a0.y * s; o[2] = a1.x * s; o[3] = a1.y * s;
+    o[4] = a2.x * s; o[5] = a2.y * s; o[6] = a3.x * s; o[7] = a3.y * s;
+  } else {
+    const float s = e4m3_to_f32(sb);
+    for (int q = 0; q < 16; ++q) o[q] = ((float)((dw >> (2 * q)) & 3u) - 1.5f) * s;
+  }
+}
+
+}  // namespace
+
+moe_status launch_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out, hipStream_t s) {
+  const int bits = prec == 0 ? 4 : 2;
+  const RecordLayout L = record_layout(H, I, bits);
+  const size_t coff[3] = {L.w1c, L.w3c, L.w2c}, soff[3] = {L.w1s, L.w3s, L.w2s};
+  const int rows = matrix == 2 ? H : I, cols = matrix == 2 ? I : H;
+  const long ndw = (long)rows * cols / (32 / bits);
+  ProfScope prof(MOE_PROF_DEQUANT, s);
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0, s, record + coff[matrix],
+                     record + soff[matrix], rows, cols, bits, out);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+}  // namespace moe

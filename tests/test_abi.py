@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports every symbol its headers declare, and its
+validation rejects bad arguments before touching a GPU (no GPU needed)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from mxfp4_routed_expert_renorm_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("library not built: run __graft_entry__.build()")
+    return B.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+
+
+def test_sizes_match_pages(lib):
+    assert lib.moe_fp4_expert_bytes(4096, 2048) == 13369344
+    assert lib.moe_int2_expert_bytes(4096, 2048) == 7077888
+    assert lib.moe_fp4_expert_bytes(0, 2048) == 0
+
+
+def _status(lib, fn, *args):
+    st = getattr(lib, fn)(*args)
+    return st, lib.moe_last_error().decode()
+
+
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def test_route_validation(lib):
+    st, msg = _status(lib, "moe_route", FAKE, 1, 8, 9, FAKE, FAKE, None)
+    assert st == 1 and "k=9" in msg
+    st, msg = _status(lib, "moe_route", FAKE, 1, 2000, 8, FAKE, FAKE, None)
+    assert st == 2 and "E=2000" in msg
+    st, msg = _status(lib, "moe_route", None, 4, 8, 2, FAKE, FAKE, None)
+    assert st == 1 and "NULL" in msg
+    st, msg = _status(lib, "moe_route", FAKE, -1, 8, 2, FAKE, FAKE, None)
+    assert st == 2
+
+
+def test_group_validation(lib):
+    st, msg = _status(lib, "moe_group", FAKE, 10, 0, FAKE, FAKE, FAKE, None)
+    assert st == 2 and "nkeys" in msg
+    st, msg = _status(lib, "moe_group", FAKE, 10, 5000, FAKE, FAKE, FAKE, None)
+    assert st == 2
+
+
+def test_expert_forward_validation(lib):
+    good = B.moe_layer(256, 128, 0x1000, lib.moe_fp4_expert_bytes(256, 128), 8, None, 0, 0, None)
+    ws = lib.moe_expert_workspace_bytes(256, 128, 4, 2, 0)
+    args = lambda layer, xt=0, T=4, k=2, w=FAKE, ot=0, wsb=ws: _status(
+        lib, "moe_expert_forward", ctypes.byref(layer), FAKE, xt, T, k, FAKE, None, w, FAKE, ot,
+        ctypes.c_void_p(0x10000), wsb, None)
+    bad_h = B.moe_layer(300, 128, 0x1000, 10 ** 6, 8, None, 0, 0, None)
+    st, msg = args(bad_h)
+    assert st == 2 and "H=300" in msg
+    short = B.moe_layer(256, 128, 0x1000, 100, 8, None, 0, 0, None)
+    st, msg = args(short)
+    assert st == 1 and "fp4_stride" in msg
+    st, msg = args(good, wsb=ws - 1)
+    assert st == 4 and "workspace" in msg
+    st, msg = args(good, k=0)
+    assert st == 1
+    st, msg = args(good, xt=7)
+    assert st == 1
+    st, msg = args(good, w=None, ot=1)
+    assert st == 1 and "fp32" in msg
+    unaligned = B.moe_layer(256, 128, 0x1001, lib.moe_fp4_expert_bytes(256, 128), 8, None, 0, 0, None)
+    st, msg = args(unaligned)
+    assert st == 1 and "aligned" in msg
+    st, msg = _status(lib, "moe_expert_forward", None, FAKE, 0, 1, 1, FAKE, None, FAKE, FAKE, 0, FAKE, ws, None)
+    assert st == 1 and "layer is NULL" in msg
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+    _status(lib, "moe_route", FAKE, 1, 8, 9, FAKE, FAKE, None)
+    main_msg = lib.moe_last_error().decode()
+    seen = {}
+
+    def other():
+        seen["before"] = lib.moe_last_error().decode()
+        lib.moe_route(FAKE, 1, 2000, 8, FAKE, FAKE, None)
+        seen["after"] = lib.moe_last_error().decode()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["before"] == ""
+    assert "E=2000" in seen["after"]
+    assert lib.moe_last_error().decode() == main_msg

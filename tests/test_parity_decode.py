@@ -1,0 +1,378 @@
+"""GPU parity of the decode path against the CPU oracle, through the C ABI.
+
+Bit-exact: dequantised weights (every FP4 code x every E8M0 byte, every 2-bit
+code x every E4M3 byte), routing ids, grouping.  Within tolerance: router
+weights, expert outputs and the combined layer output."""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from mxfp4_routed_expert_renorm_amd import workloads as W
+from tests.gpu_util import (TOL_BF16_MAX_REL, TOL_F32_REL_L2, bf16_dev, dev, log, max_rel, rel_l2, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+# ------------------------------------------------------------------ formats
+
+def _exhaustive_fp4_record(H, I):
+    """Record whose w1 covers every (code, E8M0 byte) pair: block b has scale
+    b % 256 and codes cycling 0..15 twice."""
+    rec = np.zeros(O.fp4_expert_nbytes(H, I), np.uint8)
+    p = O.split_record(rec, H, I, 4)
+    nblk = I * H // 32
+    codes = np.tile(np.arange(16, dtype=np.uint8), 2)
+    elems = np.tile(codes, nblk).reshape(I, H)
+    p["w1_codes"][:] = elems[:, 0::2] | (elems[:, 1::2] << 4)
+    p["w1_scales"][:] = (np.arange(nblk) % 256).reshape(I, H // 32).astype(np.uint8)
+    rng = np.random.default_rng(3)
+    p["w3_codes"][:] = rng.integers(0, 256, p["w3_codes"].shape, dtype=np.uint8)
+    p["w3_scales"][:] = rng.integers(0, 256, p["w3_scales"].shape, dtype=np.uint8)
+    p["w2_codes"][:] = rng.integers(0, 256, p["w2_codes"].shape, dtype=np.uint8)
+    p["w2_scales"][:] = rng.integers(0, 256, p["w2_scales"].shape, dtype=np.uint8)
+    return rec
+
+
+def _same_bits(got, want):
+    got = np.asarray(got, np.float32)
+    want = np.asarray(want, np.float64).astype(np.float32)
+    nan_ok = np.isnan(got) == np.isnan(want)
+    eq = (got.view(np.uint32) == want.view(np.uint32)) | (np.isnan(got) & np.isnan(want))
+    return bool(np.all(nan_ok) and np.all(eq))
+
+
+def test_dequant_fp4_bit_exact_all_codes_all_scales(gpu_lib):
+    torch = _torch()
+    H, I = 256, 128
+    rec = _exhaustive_fp4_record(H, I)
+    want = O.expert_weights(rec, H, I, 0)
+    d_rec = dev(rec)
+    for m in range(3):
+        rows, cols = (I, H) if m < 2 else (H, I)
+        out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+        gpu_lib.moe_debug_dequant(d_rec, H, I, 0, m, out)
+        torch.cuda.synchronize()
+        assert _same_bits(out.cpu().numpy(), want[m]), f"matrix {m}"
+
+
+def test_dequant_int2_bit_exact_all_codes_all_scales(gpu_lib):
+    torch = _torch()
+    H, I = 256, 128
+    rec = np.zeros(O.int2_expert_nbytes(H, I), np.uint8)
+    p = O.split_record(rec, H, I, 2)
+    nblk = I * H // 32
+    p["w1_codes"][:] = 0xE4                        # codes 0,1,2,3 repeating
+    p["w1_scales"][:] = (np.arange(nblk) % 256).reshape(I, H // 32).astype(np.uint8)
+    rng = np.random.default_rng(5)
+    for k in ("w3_codes", "w2_codes", "w3_scales", "w2_scales"):
+        p[k][:] = rng.integers(0, 256, p[k].shape, dtype=np.uint8)
+    want = O.expert_weights(rec, H, I, 1)
+    d_rec = dev(rec)
+    for m in range(3):
+        rows, cols = (I, H) if m < 2 else (H, I)
+        out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+        gpu_lib.moe_debug_dequant(d_rec, H, I, 1, m, out)
+        torch.cuda.synchronize()
+        assert _same_bits(out.cpu().numpy(), want[m]), f"matrix {m}"
+
+
+# ------------------------------------------------------------------ routing
+
+def _route_gpu(gpu_lib, logits, k):
+    torch = _torch()
+    T = logits.shape[0]
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    gpu_lib.moe_route(dev(logits.astype(np.float32)), k, ids, w)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg_i", [1, 2, 3])
+def test_route_bit_exact_ids(gpu_lib, cfg_i):
+    cfg = W.CONFIGS[cfg_i]
+    d = W.make_layer_inputs(cfg, W.config_seed(cfg_i), step=0, with_bank=False)
+    lg = d["logits"]
+    log(f"route parity config {cfg_i}: T={lg.shape[0]} E={lg.shape[1]} k={cfg['k']}")
+    ids, w = _route_gpu(gpu_lib, lg, cfg["k"])
+    oids, ow = O.route(lg, cfg["k"])
+    assert np.array_equal(ids, oids)
+    assert np.max(np.abs(w - ow)) <= 1e-6
+    assert np.max(np.abs(w.sum(axis=1) - 1)) <= 1e-6
+
+
+def test_route_ties_ragged_and_edges(gpu_lib):
+    rng = np.random.default_rng(9)
+    cases = []
+    lg = np.zeros((3, 8), np.float32)                      # all tied
+    cases.append((lg, 3))
+    lg = rng.integers(-2, 3, size=(37, 64)).astype(np.float32)   # many ties, ragged T
+    cases.append((lg, 6))
+    lg = rng.standard_normal((5, 1000)).astype(np.float32)        # E not a multiple of 64
+    lg[:, 999] = 50.0
+    cases.append((lg, 8))
+    lg = rng.standard_normal((2, 17)).astype(np.float32)          # k == E
+    cases.append((lg, 17))
+    lg = np.full((1, 256), -0.0, np.float32)
+    lg[0, ::2] = 0.0                                               # +0 and -0 tie
+    cases.append((lg, 5))
+    for lg, k in cases:
+        ids, w = _route_gpu(gpu_lib, lg, k)
+        oids, ow = O.route(lg, k)
+        assert np.array_equal(ids, oids), (lg.shape, k)
+        assert np.max(np.abs(w - ow)) <= 1e-6
+
+
+def test_route_T0_is_noop(gpu_lib):
+    torch = _torch()
+    z = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    gpu_lib.moe_route(z, 2, ids, w)
+
+
+def test_router_logits_and_decisions_tiny(gpu_lib):
+    """Tiny configuration: router scores from x; the GPU decides on its fp32
+    logits, the oracle on fp64 ones; decisions must agree wherever the k-th
+    and (k+1)-th logits are not within 1e-5 of each other."""
+    torch = _torch()
+    cfg = W.CONFIGS[0]
+    d = W.make_layer_inputs(cfg, W.config_seed(0))
+    T, E, H, k = cfg["T"], cfg["E"], cfg["H"], cfg["k"]
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    gpu_lib.moe_router_logits(dev(d["x"]), dev(d["router_w"]), logits)
+    torch.cuda.synchronize()
+    ol = O.router_logits(d["x"], d["router_w"])
+    gl = logits.cpu().numpy()
+    assert np.max(np.abs(gl - ol)) <= 1e-5 * np.abs(ol).max()
+    ids, w = _route_gpu(gpu_lib, gl, k)
+    oids, ow = O.route(ol, k)
+    srt = np.sort(ol, axis=1)[:, ::-1]
+    clear = (srt[:, k - 1] - srt[:, k]) > 1e-5
+    assert clear.all(), "seeded tiny routing has a near-tie; choose another seed"
+    assert np.array_equal(ids[clear], oids[clear])
+
+
+# ------------------------------------------------------------------ grouping
+
+def test_group_bit_exact(gpu_lib):
+    torch = _torch()
+    rng = np.random.default_rng(17)
+    for n, nk in [(384, 257), (32768, 257), (5, 3), (1000, 4096), (64, 1)]:
+        keys = rng.integers(0, nk, n).astype(np.int32)
+        counts = torch.empty(nk, dtype=torch.int32, device="cuda")
+        offsets = torch.empty(nk + 1, dtype=torch.int32, device="cuda")
+        perm = torch.empty(n, dtype=torch.int32, device="cuda")
+        gpu_lib.moe_group(dev(keys), nk, counts, offsets, perm)
+        torch.cuda.synchronize()
+        oc, oo, op = O.group_pairs(keys, nk)
+        assert np.array_equal(counts.cpu().numpy(), oc)
+        assert np.array_equal(offsets.cpu().numpy(), oo)
+        assert np.array_equal(perm.cpu().numpy(), op)
+
+
+def test_group_skips_out_of_range_keys(gpu_lib):
+    torch = _torch()
+    rng = np.random.default_rng(18)
+    keys = rng.integers(-3, 40, 500).astype(np.int32)
+    nk = 32
+    counts = torch.empty(nk, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(nk + 1, dtype=torch.int32, device="cuda")
+    valid = (keys >= 0) & (keys < nk)
+    perm = torch.full((int(valid.sum()),), -1, dtype=torch.int32, device="cuda")
+    gpu_lib.moe_group(dev(keys), nk, counts, offsets, perm)
+    torch.cuda.synchronize()
+    pos = np.nonzero(valid)[0]
+    oc, oo, op = O.group_pairs(keys[valid], nk)
+    assert np.array_equal(counts.cpu().numpy(), oc)
+    assert np.array_equal(offsets.cpu().numpy(), oo)
+    assert np.array_equal(perm.cpu().numpy(), pos[op])
+
+
+# ------------------------------------------------------------- layer outputs
+
+class Layer:
+    """A fully resident layer on the GPU: bank [E, rec] (+ shared record)."""
+
+    def __init__(self, gpu_lib, bank, shared, H, I, int2_bank=None):
+        self.lib = gpu_lib
+        self.H, self.I = H, I
+        self.bank = dev(bank)
+        self.shared = dev(shared) if shared is not None else None
+        self.int2 = dev(int2_bank) if int2_bank is not None else None
+        self.desc = gpu_lib.make_layer(
+            H, I, fp4_base=self.bank, fp4_stride=bank.shape[1], num_slots=bank.shape[0],
+            int2_base=self.int2, int2_stride=(int2_bank.shape[1] if int2_bank is not None else 0),
+            num_int2=(int2_bank.shape[0] if int2_bank is not None else 0), shared=self.shared)
+
+    def forward(self, x_dev, T, k, slots, prec, w, out):
+        torch = _torch()
+        nb = self.lib.moe_expert_workspace_bytes(self.H, self.I, T, k, self.shared is not None)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+        self.lib.moe_expert_forward(self.desc, x_dev, T, k, slots, prec, w, out, ws)
+        return out
+
+
+def _layer_check(gpu_lib, cfg_i, steps=(0,), bank=None):
+    torch = _torch()
+    cfg = W.CONFIGS[cfg_i]
+    seed = W.config_seed(cfg_i)
+    E, H, I, k, T = cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"]
+    if bank is None:
+        d0 = W.make_layer_inputs(cfg, seed, 0)
+        bank, shared = d0["bank"], d0["shared_rec"]
+    else:
+        bank, shared = bank
+    layer = Layer(gpu_lib, bank, shared, H, I)
+    wcache = {}
+    for step in steps:
+        d = W.make_layer_inputs(cfg, seed, step, with_bank=False)
+        log(f"layer parity config {cfg_i} step {step}")
+        if cfg["x_dtype"] == "f32":
+            x_dev = dev(d["x"])
+            x64 = d["x"].astype(np.float64)
+        else:
+            x_dev = bf16_dev(d["x"])
+            x64 = O.bf16_bits_to_f64(d["x"])
+        if d["logits"] is None:
+            lg_dev = torch.empty((T, E), dtype=torch.float32, device="cuda")
+            gpu_lib.moe_router_logits(x_dev, dev(d["router_w"]), lg_dev)
+            ol = O.router_logits(d["x"], d["router_w"])
+        else:
+            lg_dev = dev(d["logits"])
+            ol = d["logits"]
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        gpu_lib.moe_route(lg_dev, k, ids, w)
+        K1 = k + (1 if shared is not None else 0)
+        odt = torch.float32 if cfg["out_dtype"] == "f32" else torch.bfloat16
+        out = torch.empty((T, H), dtype=odt, device="cuda")
+        layer.forward(x_dev, T, k, ids, None, w, out)
+        yr = torch.empty((T, K1, H), dtype=torch.float32, device="cuda")
+        layer.forward(x_dev, T, k, ids, None, None, yr)
+        torch.cuda.synchronize()
+        oids, ow = O.route(ol, k)
+        assert np.array_equal(ids.cpu().numpy(), oids)
+        # oracle per-rank outputs (each expert dequantised once) and their combine
+        yo = np.zeros((T, K1, H))
+        for t in range(T):
+            for r in range(K1):
+                key = int(oids[t, r]) if r < k else -1
+                if key not in wcache:
+                    wcache[key] = O.expert_weights(bank[key] if r < k else shared, H, I)
+                yo[t, r] = O.expert_mlp(x64[t], *wcache[key])
+        ref = np.stack([O.combine(yo[t, :k], ow[t], yo[t, k] if K1 > k else None) for t in range(T)])
+        got = to_f64(out)
+        if cfg["out_dtype"] == "f32":
+            err = rel_l2(got, ref)
+            log(f"  rel-L2 {err:.3e}")
+            assert err <= TOL_F32_REL_L2
+        else:
+            err = max_rel(got, ref)
+            log(f"  max-rel {err:.3e}")
+            assert err <= TOL_BF16_MAX_REL
+        # per-rank outputs (fp32) against each expert evaluated alone
+        yg = yr.cpu().numpy().astype(np.float64)
+        for t in range(T):
+            for r in range(K1):
+                e = rel_l2(yg[t, r], yo[t, r])
+                assert e <= TOL_F32_REL_L2, (t, r, e)
+
+
+def test_layer_tiny_fp32(gpu_lib):
+    _layer_check(gpu_lib, 0, steps=(0, 1, 2))
+
+
+def test_layer_decode_b1_full_size(gpu_lib):
+    """Batch-1 decode at the full shape (256 experts + shared, H 4096,
+    I 2048, top-8), the launch configuration the benchmark times."""
+    _layer_check(gpu_lib, 1, steps=(0, 1))
+
+
+def _mixed_case(gpu_lib, T, xbf16, with_shared, seed):
+    """Mid-size layer (several tiles, 2-bit copies, drops) in both modes."""
+    torch = _torch()
+    H, I, E, k, NI = 512, 256, 16, 4, 12
+    bank = W.fp4_bank(seed, 1, E, H, I)
+    int2 = W.int2_bank(seed, 7, NI, H, I)
+    shared = W.fp4_record(seed, 2, 0, H, I) if with_shared else None
+    layer = Layer(gpu_lib, bank, shared, H, I, int2_bank=int2)
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    prec = rng.choice([0, 0, 1, -1], size=(T, k)).astype(np.int8)
+    slots = np.where(prec == 1, rng.integers(0, NI, (T, k)), ids).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    if xbf16:
+        xb = W.bf16_normal(seed, (3,), (T, H))
+        x_dev, x64 = bf16_dev(xb), O.bf16_bits_to_f64(xb)
+    else:
+        xf = W.f32_normal(seed, (3,), (T, H))
+        x_dev, x64 = dev(xf), xf.astype(np.float64)
+    K1 = k + (1 if with_shared else 0)
+    yr = torch.empty((T, K1, H), dtype=torch.float32, device="cuda")
+    layer.forward(x_dev, T, k, dev(slots), dev(prec), None, yr)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    layer.forward(x_dev, T, k, dev(slots), dev(prec), dev(w), out)
+    torch.cuda.synchronize()
+    yg = yr.cpu().numpy().astype(np.float64)
+
+    def rec_of(t, r):
+        return int2[slots[t, r]] if prec[t, r] == 1 else bank[slots[t, r]]
+
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for r in range(K1):
+            if r < k and prec[t, r] < 0:
+                assert np.all(yg[t, r] == 0)
+                continue
+            rec, pr = (rec_of(t, r), int(prec[t, r])) if r < k else (shared, 0)
+            yo = O.expert_mlp(x64[t], *O.expert_weights(rec, H, I, pr))
+            assert rel_l2(yg[t, r], yo) <= TOL_F32_REL_L2, (t, r)
+            ref[t] += (w[t, r] if r < k else 1.0) * yo
+    assert rel_l2(out.cpu().numpy(), ref) <= TOL_F32_REL_L2
+
+
+@pytest.mark.parametrize("T", [1, 3, 33])
+@pytest.mark.parametrize("xbf16", [False, True])
+def test_layer_mixed_precision_and_drops(gpu_lib, T, xbf16):
+    _mixed_case(gpu_lib, T, xbf16, with_shared=True, seed=100 + T)
+
+
+def test_layer_no_shared_batched(gpu_lib):
+    _mixed_case(gpu_lib, 7, True, with_shared=False, seed=77)
+
+
+def test_all_dropped_gives_shared_only(gpu_lib):
+    torch = _torch()
+    H, I, E, k = 256, 128, 8, 2
+    bank = W.fp4_bank(5, 1, E, H, I)
+    shared = W.fp4_record(5, 2, 0, H, I)
+    layer = Layer(gpu_lib, bank, shared, H, I)
+    x = W.f32_normal(5, (3,), (2, H))
+    prec = np.full((2, k), -1, np.int8)
+    slots = np.zeros((2, k), np.int32)
+    w = np.zeros((2, k), np.float32)
+    out = torch.empty((2, H), dtype=torch.float32, device="cuda")
+    layer.forward(dev(x), 2, k, dev(slots), dev(prec), dev(w), out)
+    torch.cuda.synchronize()
+    ys = O.expert_mlp(x.astype(np.float64), *O.expert_weights(shared, H, I))
+    assert rel_l2(out.cpu().numpy(), ys) <= TOL_F32_REL_L2
+
+
+def test_combine_standalone(gpu_lib):
+    torch = _torch()
+    rng = np.random.default_rng(1)
+    T, k, H = 5, 3, 64
+    y = rng.standard_normal((T, k + 1, H)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    prec = np.array([[0, -1, 0]] * T, np.int8)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    gpu_lib.moe_combine(dev(y), dev(w), dev(prec), T, k, H, True, out)
+    torch.cuda.synchronize()
+    ref = np.stack([O.combine(y[t, :k].astype(np.float64), np.where(prec[t] < 0, 0, w[t]), y[t, k]) for t in range(T)])
+    assert rel_l2(out.cpu().numpy(), ref) <= 1e-6
