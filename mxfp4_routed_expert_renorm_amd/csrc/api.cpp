@@ -40,6 +40,9 @@ moe_status launch_router_logits(const void* x, moe_dtype xt, const float* wr, in
                                 hipStream_t s);
 moe_status launch_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out, hipStream_t s);
 bool decode_shape_ok(int H, int I);
+bool b1_path_ok(int H, int I, int K1, bool xbf16);
+moe_status launch_b1(const moe_layer* L, const void* x, moe_dtype xt, int k, const int32_t* slot_ids,
+                     const int8_t* prec, const float* w, void* h, void* out, moe_dtype ot, hipStream_t s);
 size_t decode_plan_ints(int P);
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -147,6 +150,8 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype x
   int32_t* plan = (int32_t*)(ws + align256(P * layer->I * 4) + align256(P * layer->H * 4));
   float* yout = w ? y : (float*)out;
   hipStream_t s = (hipStream_t)stream;
+  if (T == 1 && w && b1_path_ok(layer->H, layer->I, K1, xt == MOE_BF16))
+    return launch_b1(layer, x, xt, k, slot_ids, prec, w, h, out, ot, s);
   st = launch_expert_decode(layer, x, xt, T, k, slot_ids, prec, h, yout, plan, s);
   if (st != MOE_OK) return st;
   if (w) return launch_combine(y, w, prec, T, k, layer->H, has_shared, out, ot, s);

@@ -72,6 +72,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // ---------------------------------------------------------------------------
+// streaming loads of expert weights: read once per step, so they are fetched
+// non-temporally (no reuse to protect in the caches)
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 ld_stream16(const uint8_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint2 ld_stream8(const uint8_t* p) {
+  const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)p);
+  return make_uint2(v.x, v.y);
+}
+
+// ---------------------------------------------------------------------------
 // packed conversions (gfx950 scaled FP4 converts, scale 1.0: the block scale
 // is applied once per 32 products)
 
@@ -102,6 +119,39 @@ __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
   for (int off = N / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
+}
+
+// Full-wavefront reductions on DPP lane moves (no LDS crossbar): butterfly
+// within quads, mirrors within rows of 16, then row broadcasts fold the four
+// rows so that lane 63 ends up with the result over all 64 lanes.
+namespace dpp {
+constexpr int kQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+}  // namespace dpp
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// sum over the 64 lanes, valid in lane 63
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v += dpp_f32<dpp::kQuadXor1>(v);
+  v += dpp_f32<dpp::kQuadXor2>(v);
+  v += dpp_f32<dpp::kRowHalfMirror>(v);
+  v += dpp_f32<dpp::kRowMirror>(v);
+  v += dpp_f32<dpp::kRowBcast15, 0xA>(v);
+  v += dpp_f32<dpp::kRowBcast31, 0xC>(v);
+  return v;
+}
+
+// sum over the 64 lanes, uniform (every lane gets it)
+__device__ __forceinline__ float wave_sum(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_to_lane63(v)), 63));
 }
 
 // ---------------------------------------------------------------------------

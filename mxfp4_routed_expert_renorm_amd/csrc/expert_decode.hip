@@ -246,8 +246,8 @@ __global__ __launch_bounds__(256) void gateup_kernel(DecodeArgs a) {
 #pragma unroll
         for (int q = 0; q < CPL; ++q) {
           const int c = q * LPR + sub;
-          c1[u][q] = *(const uint4*)(g.rec + L.w1c + row * rowc4 + (size_t)c * 16);
-          c3[u][q] = *(const uint4*)(g.rec + L.w3c + row * rowc4 + (size_t)c * 16);
+          c1[u][q] = ld_stream16(g.rec + L.w1c + row * rowc4 + (size_t)c * 16);
+          c3[u][q] = ld_stream16(g.rec + L.w3c + row * rowc4 + (size_t)c * 16);
           s1[u][q] = g.rec[L.w1s + row * rows + c];
           s3[u][q] = g.rec[L.w3s + row * rows + c];
         }
@@ -280,8 +280,8 @@ __global__ __launch_bounds__(256) void gateup_kernel(DecodeArgs a) {
 #pragma unroll
         for (int q = 0; q < CPL; ++q) {
           const int c = q * LPR + sub;
-          c1[u][q] = *(const uint2*)(g.rec + L.w1c + row * rowc2 + (size_t)c * 8);
-          c3[u][q] = *(const uint2*)(g.rec + L.w3c + row * rowc2 + (size_t)c * 8);
+          c1[u][q] = ld_stream8(g.rec + L.w1c + row * rowc2 + (size_t)c * 8);
+          c3[u][q] = ld_stream8(g.rec + L.w3c + row * rowc2 + (size_t)c * 8);
           s1[u][q] = g.rec[L.w1s + row * rows + c];
           s3[u][q] = g.rec[L.w3s + row * rows + c];
         }
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
 #pragma unroll
         for (int q = 0; q < CPL; ++q) {
           const int c = q * LPR + sub;
-          c2[u][q] = *(const uint4*)(g.rec + L.w2c + row * rowc4 + (size_t)c * 16);
+          c2[u][q] = ld_stream16(g.rec + L.w2c + row * rowc4 + (size_t)c * 16);
           s2[u][q] = g.rec[L.w2s + row * rows + c];
         }
       }
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
 #pragma unroll
         for (int q = 0; q < CPL; ++q) {
           const int c = q * LPR + sub;
-          c2[u][q] = *(const uint2*)(g.rec + L.w2c + row * rowc2 + (size_t)c * 8);
+          c2[u][q] = ld_stream8(g.rec + L.w2c + row * rowc2 + (size_t)c * 8);
           s2[u][q] = g.rec[L.w2s + row * rows + c];
         }
       }

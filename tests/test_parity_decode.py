@@ -376,3 +376,47 @@ def test_combine_standalone(gpu_lib):
     torch.cuda.synchronize()
     ref = np.stack([O.combine(y[t, :k].astype(np.float64), np.where(prec[t] < 0, 0, w[t]), y[t, k]) for t in range(T)])
     assert rel_l2(out.cpu().numpy(), ref) <= 1e-6
+
+
+@pytest.mark.parametrize("xbf16", [True, False])
+def test_layer_b1_fused_path_mixed_precision(gpu_lib, xbf16):
+    """Batch 1 at H = I = 2048 takes the fused streaming kernels; mix FP4,
+    2-bit copies and drops, with the shared expert."""
+    torch = _torch()
+    H, I, E, k, NI = 2048, 2048, 12, 6, 3
+    seed = 31 + int(xbf16)
+    bank = W.fp4_bank(seed, 1, E, H, I)
+    int2 = W.int2_bank(seed, 7, NI, H, I)
+    shared = W.fp4_record(seed, 2, 0, H, I)
+    layer = Layer(gpu_lib, bank, shared, H, I, int2_bank=int2)
+    ids = np.array([[3, 7, 0, 11, 5, 9]], np.int32)
+    prec = np.array([[0, 0, 1, 1, 0, -1]], np.int8)
+    slots = np.array([[3, 7, 0, 2, 5, -1]], np.int32)
+    w = np.array([[0.3, 0.25, 0.2, 0.1, 0.15, 0.0]], np.float32)
+    if xbf16:
+        xb = W.bf16_normal(seed, (3,), (1, H))
+        x_dev, x64 = bf16_dev(xb), O.bf16_bits_to_f64(xb)
+        odt = torch.bfloat16
+    else:
+        xf = W.f32_normal(seed, (3,), (1, H))
+        x_dev, x64 = dev(xf), xf.astype(np.float64)
+        odt = torch.float32
+    out = torch.empty((1, H), dtype=odt, device="cuda")
+    layer.forward(x_dev, 1, k, dev(slots), dev(prec), dev(w), out)
+    torch.cuda.synchronize()
+    ref = np.zeros(H)
+    for r in range(k):
+        if prec[0, r] < 0:
+            continue
+        rec = int2[slots[0, r]] if prec[0, r] == 1 else bank[slots[0, r]]
+        ref += w[0, r] * O.expert_mlp(x64[0], *O.expert_weights(rec, H, I, int(prec[0, r])))
+    ref += O.expert_mlp(x64[0], *O.expert_weights(shared, H, I))
+    got = to_f64(out)[0]
+    if xbf16:
+        err = max_rel(got, ref)
+        log(f"b1 fused path bf16: max-rel {err:.3e}")
+        assert err <= TOL_BF16_MAX_REL
+    else:
+        err = rel_l2(got, ref)
+        log(f"b1 fused path fp32: rel-L2 {err:.3e}")
+        assert err <= TOL_F32_REL_L2
