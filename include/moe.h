@@ -167,6 +167,75 @@ moe_status moe_combine(const float* y, const float* w, const int8_t* prec, int T
 moe_status moe_debug_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out,
                              moe_stream_t stream);
 
+/* ------------------------------------------------------------ slot cache */
+
+/* Pinned host memory of exactly `bytes` bytes (hipHostMalloc), for the expert
+ * banks.  Exact size matters at this scale: a power-of-two rounding allocator
+ * would turn a 27.4 GB bank into 34.4 GB ([P3] §Exact-size Engram pinning
+ * describes the same loss with torch's pinned allocator).  Free with
+ * moe_pinned_free. */
+moe_status moe_pinned_alloc(size_t bytes, void** out);
+moe_status moe_pinned_free(void* p);
+
+/* Fixed-size slot cache over (layer, expert) pairs with LRU eviction and the
+ * (a,b) precision ladder ([P1] §What the expert cache actually does; [P2]
+ * §Not all six experts matter equally).  Opaque; created and destroyed on the
+ * host. */
+typedef struct moe_cache moe_cache;
+
+typedef struct {
+  int L, E, H, I;        /* layers, experts per layer, hidden, expert intermediate */
+  int num_slots;         /* FP4 slots in device memory, shared by all layers; >= E */
+  int k;                 /* ranks per token */
+  int ladder_a, ladder_b;/* 0 <= a <= b <= k */
+  int max_tokens;        /* most tokens per ensure call; max_tokens * k <= num_slots */
+  const uint8_t* fp4_host;   /* host pinned: L*E FP4 records, pair l*E+e at (l*E+e)*moe_fp4_expert_bytes */
+  const uint8_t* int2_host;  /* host pinned: L*E 2-bit records (NULL if a == b) */
+  uint8_t* fp4_arena;        /* device: num_slots FP4 records (NULL: host-only planning) */
+  uint8_t* int2_staging;     /* device: max_tokens*(b-a) 2-bit records (NULL if a == b) */
+} moe_cache_desc;
+
+typedef struct {
+  int64_t calls, hits, misses, int2_uses, drops, bytes_h2d, evictions;
+} moe_cache_stats;
+
+/* Validates the descriptor (slot floor num_slots >= E: [P1] §Step 7, "moe_cache_size
+ * ... too small: need at least num_experts"), allocates host bookkeeping only; the
+ * cache starts cold.  The caller keeps every buffer alive until moe_cache_destroy. */
+moe_status moe_cache_create(const moe_cache_desc* desc, moe_cache** out);
+moe_status moe_cache_destroy(moe_cache* c);
+/* Back to the cold state (empty slots, clock 0, zero stats). */
+moe_status moe_cache_reset(moe_cache* c);
+
+/* One call of the policy on host arrays, no GPU work: for T tokens of `layer`,
+ * ids [T][k] expert ids and w [T][k] weights in rank order (host) ->
+ * slots [T][k] (FP4 slot, 2-bit staging entry, or -1), prec [T][k] (0 FP4,
+ * 1 2-bit, -1 dropped), w_out [T][k] renormalised over the survivors (host).
+ * Advances the cache state exactly as moe_cache_ensure does. */
+moe_status moe_cache_plan(moe_cache* c, int layer, int T, const int32_t* ids, const float* w, int32_t* slots,
+                          int8_t* prec, float* w_out);
+
+/* The per-layer call of the decode loop ([P1] §What the expert cache actually does:
+ * ensure_experts + copy_missing; [P2] §43 graphs, 43 syncs: one host sync per layer).
+ *   ids_inout [T][k] int32 device: expert ids in, slot / staging indices out (in place)
+ *   w_inout   [T][k] fp32 device: router weights in, renormalised survivors out
+ *   prec_out  [T][k] int8 device: 0 FP4, 1 2-bit, -1 dropped
+ * Enqueues a device->host read of ids and w on `compute` and waits for it (the one
+ * host sync), runs the policy, enqueues the FP4 miss copies and 2-bit copies from the
+ * pinned banks on `copy` (NULL = compute), makes `compute` wait for them, and
+ * enqueues the small host->device writes of the results on `compute`.  Everything the
+ * caller enqueues on `compute` afterwards sees the copied experts.  Not capturable in
+ * a graph (it synchronises).  Use moe_cache_layer's descriptor with
+ * moe_expert_forward. */
+moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, float* w_inout, int8_t* prec_out,
+                            moe_stream_t compute, moe_stream_t copy);
+
+/* Host copy of the (layer, expert) -> slot map, [L*E] int32 (-1 = not resident). */
+moe_status moe_cache_slot_map(const moe_cache* c, int32_t* map_host);
+moe_status moe_cache_get_stats(const moe_cache* c, moe_cache_stats* out);
+/* moe_layer descriptor of the cache's device arena and 2-bit staging (no shared expert). */
+moe_status moe_cache_layer(const moe_cache* c, moe_layer* out);
+
 /* ------------------------------------------------------------ timing */
 
 /* Kernel kinds reported by moe_profile_end. */

@@ -66,6 +66,16 @@ _SIGS = {
                                    c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "moe_combine": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p]),
     "moe_debug_dequant": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
+    "moe_pinned_alloc": (c_int, [c_size_t, ctypes.POINTER(c_void_p)]),
+    "moe_pinned_free": (c_int, [c_void_p]),
+    "moe_cache_create": (c_int, [ctypes.POINTER(moe_cache_desc), ctypes.POINTER(c_void_p)]),
+    "moe_cache_destroy": (c_int, [c_void_p]),
+    "moe_cache_reset": (c_int, [c_void_p]),
+    "moe_cache_plan": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_cache_ensure": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_cache_slot_map": (c_int, [c_void_p, c_void_p]),
+    "moe_cache_get_stats": (c_int, [c_void_p, ctypes.POINTER(moe_cache_stats)]),
+    "moe_cache_layer": (c_int, [c_void_p, ctypes.POINTER(moe_layer)]),
     "moe_profile_begin": (c_int, [c_int]),
     "moe_profile_end": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int), c_int]),
 }
@@ -181,6 +191,95 @@ def moe_combine(y, w, prec, T, k, H, has_shared, out, stream=None):
 def moe_debug_dequant(record, H, I, prec, matrix, out, stream=None):
     _check("moe_debug_dequant", load().moe_debug_dequant(_p(record), H, I, prec, matrix, _p(out), _stream(stream)))
     return out
+
+
+# ----------------------------------------------------------------- slot cache
+
+class PinnedBuffer:
+    """Exact-size pinned host memory from moe_pinned_alloc, viewed as uint8."""
+
+    def __init__(self, nbytes: int):
+        import numpy as np
+        p = c_void_p()
+        _check("moe_pinned_alloc", load().moe_pinned_alloc(nbytes, ctypes.byref(p)))
+        self.ptr, self.nbytes = p.value, nbytes
+        self.array = np.ctypeslib.as_array((ctypes.c_uint8 * nbytes).from_address(self.ptr))
+
+    def free(self):
+        if self.ptr:
+            self.array = None
+            _check("moe_pinned_free", load().moe_pinned_free(c_void_p(self.ptr)))
+            self.ptr = None
+
+
+def _np_p(a):
+    return None if a is None else c_void_p(a.ctypes.data)
+
+
+def _addr(x):
+    """Address of a torch tensor, a PinnedBuffer, an int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, PinnedBuffer):
+        return c_void_p(x.ptr)
+    if isinstance(x, int):
+        return c_void_p(x)
+    return c_void_p(x.data_ptr())
+
+
+class Cache:
+    """moe_cache handle.  Host banks and device buffers are supplied by the
+    caller and must outlive the handle."""
+
+    def __init__(self, L, E, H, I, num_slots, k, a, b, max_tokens=1, fp4_host=None, int2_host=None,
+                 fp4_arena=None, int2_staging=None):
+        d = moe_cache_desc(L, E, H, I, num_slots, k, a, b, max_tokens, _addr(fp4_host), _addr(int2_host),
+                           _addr(fp4_arena), _addr(int2_staging))
+        h = c_void_p()
+        _check("moe_cache_create", load().moe_cache_create(ctypes.byref(d), ctypes.byref(h)))
+        self.h, self.L, self.E, self.k = h, L, E, k
+
+    def destroy(self):
+        if self.h:
+            _check("moe_cache_destroy", load().moe_cache_destroy(self.h))
+            self.h = None
+
+    def reset(self):
+        _check("moe_cache_reset", load().moe_cache_reset(self.h))
+
+    def plan(self, layer, ids, w):
+        """Host-only policy step: ids int32 [T,k], w float32 [T,k] numpy."""
+        import numpy as np
+        ids = np.ascontiguousarray(ids, np.int32)
+        w = np.ascontiguousarray(w, np.float32)
+        T = ids.shape[0]
+        slots = np.empty_like(ids)
+        prec = np.empty(ids.shape, np.int8)
+        wo = np.empty_like(w)
+        _check("moe_cache_plan", load().moe_cache_plan(self.h, layer, T, _np_p(ids), _np_p(w), _np_p(slots),
+                                                       _np_p(prec), _np_p(wo)))
+        return slots, prec, wo
+
+    def ensure(self, layer, T, ids_inout, w_inout, prec_out, compute=None, copy=None):
+        st = load().moe_cache_ensure(self.h, layer, T, _p(ids_inout), _p(w_inout), _p(prec_out),
+                                     _stream(compute), None if copy is None else _stream(copy))
+        _check("moe_cache_ensure", st)
+
+    def slot_map(self):
+        import numpy as np
+        m = np.empty(self.L * self.E, np.int32)
+        _check("moe_cache_slot_map", load().moe_cache_slot_map(self.h, _np_p(m)))
+        return m
+
+    def stats(self) -> dict:
+        s = moe_cache_stats()
+        _check("moe_cache_get_stats", load().moe_cache_get_stats(self.h, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in moe_cache_stats._fields_}
+
+    def layer(self) -> moe_layer:
+        lay = moe_layer()
+        _check("moe_cache_layer", load().moe_cache_layer(self.h, ctypes.byref(lay)))
+        return lay
 
 
 # --------------------------------------------------------------------- timing

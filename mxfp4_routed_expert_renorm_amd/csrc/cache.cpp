@@ -1,0 +1,329 @@
+// Slot cache with the (a,b) precision ladder: host policy and miss copies.
+//
+// "Running DeepSeek-V4-Flash across four free GPUs", §What the expert cache
+// actually does: the expert banks live in pinned host memory; a fixed number
+// of expert slots in device memory is shared by every layer (global, not per
+// layer); each step the router's expert ids are rewritten to slots in place
+// and only the misses are copied across the host link; eviction is LRU.
+// "An elephant through a straw", §Not all six experts matter equally: ranks
+// 1..a always use FP4 (fetched on a miss), ranks a+1..b use FP4 if resident
+// and the 2-bit copy otherwise, lower ranks are used if resident and dropped
+// otherwise, and the survivors' weights are renormalised; §43 graphs, 43
+// syncs: one host sync per layer reads the router's picks.
+//
+// Policy details the pages leave open (same as the oracle): residency is read
+// once per token before its fetches; slots used anywhere in the call are
+// protected from eviction for the rest of the call; fetches go in rank order;
+// a global clock stamps every hit and fetch; the victim is the lowest-index
+// empty slot, else the unprotected slot with the oldest stamp; 2-bit copies
+// are not cached but copied per use into a staging area at index
+// t*(b-a) + (rank-a-1).
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+
+struct moe_cache {
+  moe_cache_desc d;
+  size_t fp4_bytes = 0, int2_bytes = 0;
+  std::vector<int32_t> map;      // (layer, expert) -> slot or -1
+  std::vector<int32_t> owner;    // slot -> pair or -1
+  std::vector<int64_t> stamp;    // 0 = empty
+  int64_t clock = 0;
+  moe_cache_stats st{};
+  // per-call scratch
+  std::vector<int32_t> ids_h, slots_h;
+  std::vector<int8_t> prec_h;
+  std::vector<float> w_h, wout_h;
+  std::vector<uint8_t> prot;
+  struct Copy {
+    int kind;  // 0 FP4, 1 2-bit
+    int pair, dest;
+  };
+  std::vector<Copy> copies;
+  // device-side plumbing (created on first ensure)
+  void* pin_in = nullptr;   // pinned: ids [T*k] int32, w [T*k] f32
+  void* pin_out = nullptr;  // pinned: slots [T*k] int32, w' [T*k] f32, prec [T*k] int8
+  hipEvent_t ev_read = nullptr, ev_copy = nullptr;
+  bool broken = false;
+};
+
+namespace moe {
+
+namespace {
+
+size_t pin_in_bytes(const moe_cache_desc& d) { return (size_t)d.max_tokens * d.k * 8; }
+size_t pin_out_bytes(const moe_cache_desc& d) { return (size_t)d.max_tokens * d.k * 9; }
+
+// one call of the policy on host arrays; fills c->slots_h, prec_h, wout_h, copies
+moe_status plan(moe_cache* c, int layer, int T, const int32_t* ids, const float* w) {
+  const moe_cache_desc& d = c->d;
+  const int k = d.k, a = d.ladder_a, b = d.ladder_b, E = d.E, S = d.num_slots;
+  c->slots_h.assign((size_t)T * k, -1);
+  c->prec_h.assign((size_t)T * k, -1);
+  c->wout_h.assign((size_t)T * k, 0.0f);
+  c->copies.clear();
+  c->prot.assign(S, 0);
+  // validate everything before the state changes
+  for (int i = 0; i < T * k; ++i)
+    if (ids[i] < 0 || ids[i] >= E)
+      return fail(MOE_EINVAL, "moe_cache: expert id %d at position %d outside [0, %d)", ids[i], i, E);
+  for (int t = 0; t < T; ++t)
+    for (int r = 0; r < k; ++r)
+      for (int q = 0; q < r; ++q)
+        if (ids[(size_t)t * k + q] == ids[(size_t)t * k + r])
+          return fail(MOE_EINVAL, "moe_cache: token %d lists expert %d twice", t, ids[(size_t)t * k + r]);
+  for (int t = 0; t < T; ++t) {
+    const int32_t* id = ids + (size_t)t * k;
+    int cls[64];
+    bool res[64];
+    for (int r = 0; r < k; ++r) {
+      const int rank = r + 1;
+      res[r] = c->map[(size_t)layer * E + id[r]] >= 0;  // snapshot before this token's fetches
+      if (rank <= a)
+        cls[r] = 0;
+      else if (rank <= b)
+        cls[r] = res[r] ? 0 : 1;
+      else
+        cls[r] = res[r] ? 0 : -1;
+    }
+    for (int r = 0; r < k; ++r)
+      if (cls[r] == 0 && res[r]) c->prot[c->map[(size_t)layer * E + id[r]]] = 1;
+    for (int r = 0; r < k; ++r) {
+      const int pair = layer * E + id[r];
+      const size_t o = (size_t)t * k + r;
+      if (cls[r] == 0 && res[r]) {
+        const int s = c->map[pair];
+        c->stamp[s] = ++c->clock;
+        c->slots_h[o] = s;
+        c->prec_h[o] = 0;
+        c->st.hits++;
+      } else if (cls[r] == 0) {
+        int victim = -1;
+        for (int s = 0; s < S; ++s) {
+          if (c->prot[s]) continue;
+          if (victim < 0 || c->stamp[s] < c->stamp[victim]) victim = s;
+        }
+        if (victim < 0) return fail(MOE_ECACHE_SMALL, "moe_cache: every slot is in use by this call");
+        if (c->owner[victim] >= 0) {
+          c->map[c->owner[victim]] = -1;
+          c->st.evictions++;
+        }
+        c->owner[victim] = pair;
+        c->map[pair] = victim;
+        c->stamp[victim] = ++c->clock;
+        c->prot[victim] = 1;
+        c->slots_h[o] = victim;
+        c->prec_h[o] = 0;
+        c->copies.push_back({0, pair, victim});
+        c->st.misses++;
+      } else if (cls[r] == 1) {
+        const int st = t * (b - a) + (r + 1 - a - 1);
+        c->slots_h[o] = st;
+        c->prec_h[o] = 1;
+        c->copies.push_back({1, pair, st});
+        c->st.int2_uses++;
+      } else {
+        c->st.drops++;
+      }
+    }
+    double tot = 0.0;
+    for (int r = 0; r < k; ++r)
+      if (c->prec_h[(size_t)t * k + r] >= 0) tot += (double)w[(size_t)t * k + r];
+    if (tot > 0.0)
+      for (int r = 0; r < k; ++r)
+        if (c->prec_h[(size_t)t * k + r] >= 0)
+          c->wout_h[(size_t)t * k + r] = (float)((double)w[(size_t)t * k + r] / tot);
+  }
+  c->st.calls++;
+  return MOE_OK;
+}
+
+moe_status check_call(const moe_cache* c, int layer, int T) {
+  if (!c) return fail(MOE_EINVAL, "moe_cache: handle is NULL");
+  if (c->broken) return fail(MOE_ESTATE, "moe_cache: an earlier ensure failed midway; reset the cache");
+  if (layer < 0 || layer >= c->d.L) return fail(MOE_EINVAL, "moe_cache: layer %d outside [0, %d)", layer, c->d.L);
+  if (T < 1 || T > c->d.max_tokens)
+    return fail(MOE_ESHAPE, "moe_cache: T=%d outside [1, max_tokens=%d]", T, c->d.max_tokens);
+  return MOE_OK;
+}
+
+}  // namespace
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+moe_status moe_pinned_alloc(size_t bytes, void** out) {
+  if (!out || bytes == 0) return fail(MOE_EINVAL, "moe_pinned_alloc: bytes=%zu out=%p", bytes, (void*)out);
+  *out = nullptr;
+  hipError_t e = hipHostMalloc(out, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    *out = nullptr;
+    return fail(MOE_ENOMEM, "moe_pinned_alloc: hipHostMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_pinned_free(void* p) {
+  if (!p) return MOE_OK;
+  hipError_t e = hipHostFree(p);
+  if (e != hipSuccess) return fail(MOE_EHIP, "moe_pinned_free: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+moe_status moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
+  if (!d || !out) return fail(MOE_EINVAL, "moe_cache_create: NULL argument");
+  *out = nullptr;
+  if (d->L < 1 || d->E < 1 || d->E > 1024) return fail(MOE_ESHAPE, "moe_cache_create: L=%d E=%d", d->L, d->E);
+  if (d->k < 1 || d->k > 64 || d->k > d->E) return fail(MOE_EINVAL, "moe_cache_create: k=%d (E=%d)", d->k, d->E);
+  if (d->ladder_a < 0 || d->ladder_a > d->ladder_b || d->ladder_b > d->k)
+    return fail(MOE_EINVAL, "moe_cache_create: ladder (a=%d, b=%d) must satisfy 0 <= a <= b <= k=%d", d->ladder_a,
+                d->ladder_b, d->k);
+  if (d->max_tokens < 1) return fail(MOE_EINVAL, "moe_cache_create: max_tokens=%d", d->max_tokens);
+  if (d->num_slots < d->E)
+    return fail(MOE_ECACHE_SMALL, "moe_cache_create: num_slots=%d is too small: need at least num_experts=%d",
+                d->num_slots, d->E);
+  if ((long)d->max_tokens * d->k > d->num_slots)
+    return fail(MOE_ECACHE_SMALL, "moe_cache_create: max_tokens*k=%ld exceeds num_slots=%d",
+                (long)d->max_tokens * d->k, d->num_slots);
+  if (d->H % 32 || d->I % 32 || d->H <= 0 || d->I <= 0) return fail(MOE_ESHAPE, "moe_cache_create: H=%d I=%d", d->H, d->I);
+  const bool int2 = d->ladder_b > d->ladder_a;
+  if (d->fp4_host == nullptr && d->fp4_arena != nullptr)
+    return fail(MOE_EINVAL, "moe_cache_create: fp4_host is NULL");
+  if (int2 && d->fp4_arena && (!d->int2_host || !d->int2_staging))
+    return fail(MOE_EINVAL, "moe_cache_create: ladder a < b needs int2_host and int2_staging");
+  moe_cache* c = new moe_cache();
+  c->d = *d;
+  c->fp4_bytes = record_layout(d->H, d->I, 4).bytes;
+  c->int2_bytes = record_layout(d->H, d->I, 2).bytes;
+  c->map.assign((size_t)d->L * d->E, -1);
+  c->owner.assign(d->num_slots, -1);
+  c->stamp.assign(d->num_slots, 0);
+  *out = c;
+  return MOE_OK;
+}
+
+moe_status moe_cache_destroy(moe_cache* c) {
+  if (!c) return MOE_OK;
+  if (c->pin_in) (void)hipHostFree(c->pin_in);
+  if (c->pin_out) (void)hipHostFree(c->pin_out);
+  if (c->ev_read) (void)hipEventDestroy(c->ev_read);
+  if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
+  delete c;
+  return MOE_OK;
+}
+
+moe_status moe_cache_reset(moe_cache* c) {
+  if (!c) return fail(MOE_EINVAL, "moe_cache_reset: handle is NULL");
+  std::fill(c->map.begin(), c->map.end(), -1);
+  std::fill(c->owner.begin(), c->owner.end(), -1);
+  std::fill(c->stamp.begin(), c->stamp.end(), 0);
+  c->clock = 0;
+  c->st = moe_cache_stats{};
+  c->broken = false;
+  return MOE_OK;
+}
+
+moe_status moe_cache_plan(moe_cache* c, int layer, int T, const int32_t* ids, const float* w, int32_t* slots,
+                          int8_t* prec, float* w_out) {
+  moe_status s = check_call(c, layer, T);
+  if (s != MOE_OK) return s;
+  if (!ids || !w || !slots || !prec || !w_out) return fail(MOE_EINVAL, "moe_cache_plan: NULL pointer");
+  s = plan(c, layer, T, ids, w);
+  if (s != MOE_OK) return s;
+  const size_t n = (size_t)T * c->d.k;
+  std::memcpy(slots, c->slots_h.data(), n * 4);
+  std::memcpy(prec, c->prec_h.data(), n);
+  std::memcpy(w_out, c->wout_h.data(), n * 4);
+  for (const auto& cp : c->copies) c->st.bytes_h2d += (int64_t)(cp.kind == 0 ? c->fp4_bytes : c->int2_bytes);
+  return MOE_OK;
+}
+
+moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, float* w_inout, int8_t* prec_out,
+                            moe_stream_t compute, moe_stream_t copy) {
+  moe_status s = check_call(c, layer, T);
+  if (s != MOE_OK) return s;
+  if (!ids_inout || !w_inout || !prec_out) return fail(MOE_EINVAL, "moe_cache_ensure: NULL pointer");
+  if (!c->d.fp4_arena) return fail(MOE_EINVAL, "moe_cache_ensure: the cache has no device arena");
+  hipStream_t cs = (hipStream_t)compute, ps = copy ? (hipStream_t)copy : cs;
+  const size_t n = (size_t)T * c->d.k;
+  if (!c->pin_in) {
+    MOE_HIP_CHECK(hipHostMalloc(&c->pin_in, pin_in_bytes(c->d), hipHostMallocDefault));
+    MOE_HIP_CHECK(hipHostMalloc(&c->pin_out, pin_out_bytes(c->d), hipHostMallocDefault));
+    MOE_HIP_CHECK(hipEventCreateWithFlags(&c->ev_read, hipEventDisableTiming));
+    MOE_HIP_CHECK(hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming));
+  }
+  int32_t* ids_h = (int32_t*)c->pin_in;
+  float* w_h = (float*)((char*)c->pin_in + (size_t)c->d.max_tokens * c->d.k * 4);
+  // the one host sync of the call: read the router's picks
+  MOE_HIP_CHECK(hipMemcpyAsync(ids_h, ids_inout, n * 4, hipMemcpyDeviceToHost, cs));
+  MOE_HIP_CHECK(hipMemcpyAsync(w_h, w_inout, n * 4, hipMemcpyDeviceToHost, cs));
+  MOE_HIP_CHECK(hipEventRecord(c->ev_read, cs));
+  MOE_HIP_CHECK(hipEventSynchronize(c->ev_read));
+  s = plan(c, layer, T, ids_h, w_h);
+  if (s != MOE_OK) return s;
+  // from here on the host state has advanced: a failure leaves the cache inconsistent
+  c->broken = true;
+  for (const auto& cp : c->copies) {
+    if (cp.kind == 0) {
+      MOE_HIP_CHECK(hipMemcpyAsync(c->d.fp4_arena + (size_t)cp.dest * c->fp4_bytes,
+                                   c->d.fp4_host + (size_t)cp.pair * c->fp4_bytes, c->fp4_bytes,
+                                   hipMemcpyHostToDevice, ps));
+      c->st.bytes_h2d += (int64_t)c->fp4_bytes;
+    } else {
+      MOE_HIP_CHECK(hipMemcpyAsync(c->d.int2_staging + (size_t)cp.dest * c->int2_bytes,
+                                   c->d.int2_host + (size_t)cp.pair * c->int2_bytes, c->int2_bytes,
+                                   hipMemcpyHostToDevice, ps));
+      c->st.bytes_h2d += (int64_t)c->int2_bytes;
+    }
+  }
+  if (ps != cs && !c->copies.empty()) {
+    MOE_HIP_CHECK(hipEventRecord(c->ev_copy, ps));
+    MOE_HIP_CHECK(hipStreamWaitEvent(cs, c->ev_copy, 0));
+  }
+  int32_t* slots_o = (int32_t*)c->pin_out;
+  float* w_o = (float*)((char*)c->pin_out + (size_t)c->d.max_tokens * c->d.k * 4);
+  int8_t* prec_o = (int8_t*)((char*)c->pin_out + (size_t)c->d.max_tokens * c->d.k * 8);
+  std::memcpy(slots_o, c->slots_h.data(), n * 4);
+  std::memcpy(w_o, c->wout_h.data(), n * 4);
+  std::memcpy(prec_o, c->prec_h.data(), n);
+  MOE_HIP_CHECK(hipMemcpyAsync(ids_inout, slots_o, n * 4, hipMemcpyHostToDevice, cs));
+  MOE_HIP_CHECK(hipMemcpyAsync(w_inout, w_o, n * 4, hipMemcpyHostToDevice, cs));
+  MOE_HIP_CHECK(hipMemcpyAsync(prec_out, prec_o, n, hipMemcpyHostToDevice, cs));
+  c->broken = false;
+  return MOE_OK;
+}
+
+moe_status moe_cache_slot_map(const moe_cache* c, int32_t* map_host) {
+  if (!c || !map_host) return fail(MOE_EINVAL, "moe_cache_slot_map: NULL argument");
+  std::memcpy(map_host, c->map.data(), c->map.size() * 4);
+  return MOE_OK;
+}
+
+moe_status moe_cache_get_stats(const moe_cache* c, moe_cache_stats* out) {
+  if (!c || !out) return fail(MOE_EINVAL, "moe_cache_get_stats: NULL argument");
+  *out = c->st;
+  return MOE_OK;
+}
+
+moe_status moe_cache_layer(const moe_cache* c, moe_layer* out) {
+  if (!c || !out) return fail(MOE_EINVAL, "moe_cache_layer: NULL argument");
+  out->H = c->d.H;
+  out->I = c->d.I;
+  out->fp4_base = c->d.fp4_arena;
+  out->fp4_stride = c->fp4_bytes;
+  out->num_slots = c->d.num_slots;
+  const bool int2 = c->d.ladder_b > c->d.ladder_a;
+  out->int2_base = int2 ? c->d.int2_staging : nullptr;
+  out->int2_stride = c->int2_bytes;
+  out->num_int2 = int2 ? c->d.max_tokens * (c->d.ladder_b - c->d.ladder_a) : 0;
+  out->shared = nullptr;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+"""The library's slot-cache policy (C++, host-only planning entry point)
+against the oracle, bit for bit, on CPU: the full slot-cache decode trace
+(8 layers x 256 experts, 512 slots, top-6, ladder (2,4), 512 tokens), other
+ladders, batched calls, and the validation errors."""
+import numpy as np
+import pytest
+
+from mxfp4_routed_expert_renorm_amd import binding as B
+from mxfp4_routed_expert_renorm_amd import workloads as W
+from oracle import moe_oracle as O
+
+
+def _route_all(logits, k):
+    """Oracle routing of every (token, layer): ids [T,L,k], w float32 [T,L,k]."""
+    T, L, E = logits.shape
+    ids, w = O.route(logits.reshape(T * L, E), k)
+    return ids.reshape(T, L, k), w.astype(np.float32).reshape(T, L, k)
+
+
+def _compare_trace(L, E, S, k, a, b, ids, w, T_call=1):
+    c = B.Cache(L, E, 4096, 2048, S, k, a, b, max_tokens=T_call)
+    oc = O.SlotCache(L, E, S, k, a, b)
+    T = ids.shape[0]
+    try:
+        for t0 in range(0, T, T_call):
+            for l in range(L):
+                ii = ids[t0:t0 + T_call, l]
+                ww = w[t0:t0 + T_call, l]
+                slots, prec, wo = c.plan(l, ii, ww)
+                oslots, oprec, owo, _ = oc.step(l, ii, ww.astype(np.float64))
+                assert np.array_equal(slots, oslots), (t0, l)
+                assert np.array_equal(prec, oprec), (t0, l)
+                assert np.max(np.abs(wo - owo)) <= 1e-6
+                assert np.array_equal(c.slot_map(), oc.slot_map()), (t0, l)
+        st = c.stats()
+        assert (st["hits"], st["misses"], st["int2_uses"], st["drops"]) == (oc.hits, oc.misses, oc.int2, oc.drops)
+        return st
+    finally:
+        c.destroy()
+
+
+def test_slotcache_trace_full_size_bit_exact():
+    cfg = W.CONFIGS[4]
+    L, E, k, S, (a, b), T = cfg["L"], cfg["E"], cfg["k"], cfg["slots"], cfg["ladder"], cfg["T"]
+    logits = W.slotcache_logits(W.config_seed(4), L, E, T, cfg["zipf"])
+    ids, w = _route_all(logits, k)
+    st = _compare_trace(L, E, S, k, a, b, ids, w)
+    # sanity of the workload: both fetch kinds and drops occur
+    assert st["misses"] > 0 and st["int2_uses"] > 0 and st["drops"] > 0 and st["hits"] > 0
+
+
+@pytest.mark.parametrize("a,b", [(0, 0), (1, 4), (4, 4), (0, 4), (6, 6)])
+def test_slotcache_other_ladders(a, b):
+    L, E, k, S, T = 3, 32, 6, 40, 60
+    rng = np.random.default_rng(a * 10 + b)
+    logits = rng.standard_normal((T, L, E)).astype(np.float32)
+    logits += W.zipf_bias(5, (1,), E, 1.1)[None, None, :]
+    ids, w = _route_all(logits, k)
+    _compare_trace(L, E, S, k, a, b, ids, w)
+
+
+def test_slotcache_batched_calls():
+    L, E, k, S, T = 2, 16, 3, 16, 40
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((T, L, E)).astype(np.float32)
+    ids, w = _route_all(logits, k)
+    _compare_trace(L, E, S, k, 1, 2, ids, w, T_call=4)
+
+
+def test_slotcache_validation():
+    with pytest.raises(B.MoeError, match="too small"):
+        B.Cache(2, 256, 4096, 2048, 128, 8, 2, 4)
+    with pytest.raises(B.MoeError, match="ladder"):
+        B.Cache(2, 8, 256, 128, 8, 4, 3, 2)
+    with pytest.raises(B.MoeError, match="max_tokens"):
+        B.Cache(2, 8, 256, 128, 8, 4, 1, 2, max_tokens=3)
+    c = B.Cache(2, 8, 256, 128, 8, 3, 1, 2)
+    try:
+        with pytest.raises(B.MoeError, match="twice"):
+            c.plan(0, np.array([[1, 1, 2]]), np.ones((1, 3)))
+        with pytest.raises(B.MoeError, match="outside"):
+            c.plan(0, np.array([[1, 9, 2]]), np.ones((1, 3)))
+        with pytest.raises(B.MoeError, match="layer"):
+            c.plan(5, np.array([[1, 3, 2]]), np.ones((1, 3)))
+        # a rejected call leaves the state untouched
+        assert np.all(c.slot_map() == -1)
+        slots, prec, wo = c.plan(0, np.array([[1, 3, 2]]), np.array([[0.5, 0.3, 0.2]]))
+        assert prec.tolist() == [[0, 1, -1]] and slots.tolist() == [[0, 0, -1]]
+        assert np.allclose(wo, [[0.625, 0.375, 0.0]])
+        c.reset()
+        assert np.all(c.slot_map() == -1) and c.stats()["calls"] == 0
+    finally:
+        c.destroy()

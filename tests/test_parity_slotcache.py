@@ -1,0 +1,102 @@
+"""GPU parity of the slot-cache decode loop against the oracle, through the C ABI:
+per (token, layer) route on the GPU, moe_cache_ensure (one host sync, FP4 miss
+copies and 2-bit copies from pinned host banks on a side stream, ids rewritten
+to slots in place), then the expert MLP over the slot arena.  Slots,
+precisions and the slot map are compared bit for bit at every call, the
+renormalised weights to 1e-6, the layer outputs to tolerance."""
+import numpy as np
+import pytest
+
+from mxfp4_routed_expert_renorm_amd import workloads as W
+from oracle import moe_oracle as O
+from tests.gpu_util import TOL_BF16_MAX_REL, bf16_dev, dev, log, max_rel
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1):
+    import torch
+    lib = gpu_lib
+    rb4, rb2 = O.fp4_expert_nbytes(H, I), O.int2_expert_nbytes(H, I)
+    logits = W.slotcache_logits(seed, L, E, T, zipf)                 # [T, L, E]
+    # the oracle's own trace tells which host records are ever read
+    oc0 = O.SlotCache(L, E, S, k, a, b)
+    need4, need2 = set(), set()
+    for t in range(T):
+        for l in range(L):
+            oids, ow = O.route(logits[t, l][None, :], k)
+            for kind, ll, e, _ in oc0.step(l, oids, ow)[3]:
+                (need4 if kind == "fp4" else need2).add(ll * E + e)
+    log(f"slot cache L={L} E={E} H={H} I={I} S={S} k={k} ladder=({a},{b}) T={T}: "
+        f"{len(need4)} FP4 and {len(need2)} 2-bit records read")
+    fp4_host = lib.PinnedBuffer(L * E * rb4)
+    int2_host = lib.PinnedBuffer(L * E * rb2) if b > a else None
+    for p in need4:
+        W.fp4_record(seed, W.S_BANK, p, H, I, out=fp4_host.array[p * rb4:(p + 1) * rb4])
+    for p in need2:
+        W.int2_record(seed, W.S_INT2, p, H, I, out=int2_host.array[p * rb2:(p + 1) * rb2])
+    arena = torch.empty(S * rb4, dtype=torch.uint8, device="cuda")
+    staging = torch.empty(max(1, (b - a)) * rb2, dtype=torch.uint8, device="cuda") if b > a else None
+    cache = lib.Cache(L, E, H, I, S, k, a, b, 1, fp4_host, int2_host, arena, staging)
+    oc = O.SlotCache(L, E, S, k, a, b)
+    copy_stream = torch.cuda.Stream()
+    try:
+        layer = cache.layer()
+        lg_dev = dev(logits.reshape(T * L, E))
+        ids = torch.empty((1, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+        prec = torch.empty((1, k), dtype=torch.int8, device="cuda")
+        out = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(lib.moe_expert_workspace_bytes(H, I, 1, k, False), dtype=torch.uint8, device="cuda")
+        checked = 0
+        for t in range(T):
+            for l in range(L):
+                row = t * L + l
+                lib.moe_route(lg_dev[row:row + 1], k, ids, w)
+                cache.ensure(l, 1, ids, w, prec, copy=copy_stream)
+                xb = W.slotcache_x(seed, t, l, H)
+                lib.moe_expert_forward(layer, bf16_dev(xb), 1, k, ids, prec, w, out, ws)
+                oids, ow = O.route(logits[t, l][None, :], k)
+                oslots, oprec, owo, _ = oc.step(l, oids, ow)
+                torch.cuda.synchronize()
+                assert np.array_equal(ids.cpu().numpy(), oslots), (t, l)
+                assert np.array_equal(prec.cpu().numpy(), oprec), (t, l)
+                assert np.max(np.abs(w.cpu().numpy() - owo)) <= 1e-6, (t, l)
+                assert np.array_equal(cache.slot_map(), oc.slot_map()), (t, l)
+                if t % check_every == 0:
+                    def rec(e, p, l=l):
+                        q = l * E + int(e)
+                        return (fp4_host.array[q * rb4:(q + 1) * rb4] if p == 0
+                                else int2_host.array[q * rb2:(q + 1) * rb2])
+                    ref = O.layer_forward(O.bf16_bits_to_f64(xb), oids, owo, rec, H, I, prec=oprec)
+                    err = max_rel(out.float().cpu().numpy(), ref)
+                    assert err <= TOL_BF16_MAX_REL, (t, l, err)
+                    checked += 1
+        st = cache.stats()
+        log(f"  stats {st}; outputs checked: {checked}")
+        assert (st["hits"], st["misses"], st["int2_uses"], st["drops"]) == (oc.hits, oc.misses, oc.int2, oc.drops)
+        return st
+    finally:
+        cache.destroy()
+        fp4_host.free()
+        if int2_host is not None:
+            int2_host.free()
+
+
+def test_slotcache_loop_small(gpu_lib):
+    """Several tiles, every ladder class, evictions (16 slots for 48 pairs)."""
+    st = _run(gpu_lib, L=3, E=16, H=512, I=256, S=16, k=4, a=2, b=3, T=30, seed=71, check_every=3)
+    assert st["evictions"] > 0
+
+
+def test_slotcache_loop_fused_b1_path(gpu_lib):
+    """H = I = 2048: the batch-1 fused kernels read the arena and the staging."""
+    _run(gpu_lib, L=2, E=24, H=2048, I=2048, S=30, k=6, a=2, b=4, T=12, seed=72, check_every=4)
+
+
+def test_slotcache_loop_full_size(gpu_lib):
+    """The slot-cache decode workload's shape: 8 layers x 256 experts, H 4096,
+    I 2048, 512 slots, top-6, ladder (2,4); 16 tokens, outputs on every 4th."""
+    cfg = W.CONFIGS[4]
+    _run(gpu_lib, L=cfg["L"], E=cfg["E"], H=cfg["H"], I=cfg["I"], S=cfg["slots"], k=cfg["k"],
+         a=cfg["ladder"][0], b=cfg["ladder"][1], T=16, seed=W.config_seed(4), check_every=4)
