@@ -21,6 +21,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -36,6 +38,10 @@ def parse():
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
                     help="graph: the timed steps are captured into one HIP graph and replayed; "
                          "eager: one launch sequence per step from the host")
+    ap.add_argument("--workload", choices=("decode-b1", "decode-b64", "slotcache"), default="decode-b1",
+                    help="decode-b1 (default, the headline line): batch-1 decode of a resident 256-expert "
+                         "layer; decode-b64: 64 tokens, top-6, Zipf-skewed routing, grouped by expert; "
+                         "slotcache: 512 tokens x 8 layers through the 512-slot cache with the (2,4) ladder")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (known bytes for HBM counter scaling)")
@@ -104,8 +110,28 @@ def main():
         print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X "
               "(no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "decode-b64":
+        return bench_decode_b64(args)
+    if args.workload == "slotcache":
+        return bench_slotcache(args)
+    return bench_decode_b1(args)
 
-    import numpy as np
+
+def resident_bank(W, lib, torch, cfg, seed, dev):
+    """The layer's 256 FP4 records (slot = expert id) and the shared record, in HBM."""
+    E, H, I = cfg["E"], cfg["H"], cfg["I"]
+    rec_bytes = lib.moe_fp4_expert_bytes(H, I)
+    bank = torch.empty((E, rec_bytes), dtype=torch.uint8, device=dev)
+    host = np.empty((16, rec_bytes), np.uint8)
+    for e0 in range(0, E, 16):
+        W.fp4_bank(seed, W.S_BANK, 16, H, I, out=host, first_index=e0)
+        bank[e0:e0 + 16].copy_(torch.from_numpy(host))
+    shared = torch.from_numpy(W.fp4_record(seed, W.S_SHARED, 0, H, I)).to(dev)
+    return bank, shared, rec_bytes
+
+
+def bench_decode_b1(args):
+
     import torch
 
     from mxfp4_routed_expert_renorm_amd import binding as lib
@@ -122,12 +148,7 @@ def main():
     t0 = time.time()
     print(f"[bench] generating {E}+1 experts ({(E + 1) * rec_bytes / 1e9:.2f} GB) and {nsteps} steps of inputs",
           file=sys.stderr, flush=True)
-    bank = torch.empty((E, rec_bytes), dtype=torch.uint8, device=dev)
-    host = np.empty((16, rec_bytes), np.uint8)
-    for e0 in range(0, E, 16):
-        W.fp4_bank(seed, W.S_BANK, 16, H, I, out=host, first_index=e0)
-        bank[e0:e0 + 16].copy_(torch.from_numpy(host))
-    shared = torch.from_numpy(W.fp4_record(seed, W.S_SHARED, 0, H, I)).to(dev)
+    bank, shared, rec_bytes = resident_bank(W, lib, torch, cfg, seed, dev)
     xs = np.stack([W.make_layer_inputs(cfg, seed, s, with_bank=False)["x"][0] for s in range(nsteps)])
     lgs = np.stack([W.make_layer_inputs(cfg, seed, s, with_bank=False)["logits"][0] for s in range(nsteps)])
     x_d = torch.from_numpy(xs).to(dev).view(torch.bfloat16)          # [steps, H]
@@ -155,37 +176,7 @@ def main():
     step(0)
     torch.cuda.synchronize()
 
-    if args.mode == "graph":
-        stream = torch.cuda.Stream()
-        stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(stream):
-            for s in range(min(3, nsteps)):
-                step(s)
-        torch.cuda.current_stream().wait_stream(stream)
-        torch.cuda.synchronize()
-        g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_warm):
-            for s in range(Wm):
-                step(s)
-        with torch.cuda.graph(g_timed):
-            for s in range(Wm, nsteps):
-                step(s)
-        g_warm.replay()
-        torch.cuda.synchronize()
-        ta = time.perf_counter()
-        g_timed.replay()
-        torch.cuda.synchronize()
-        tb = time.perf_counter()
-    else:
-        for s in range(Wm):
-            step(s)
-        torch.cuda.synchronize()
-        ta = time.perf_counter()
-        for s in range(Wm, nsteps):
-            step(s)
-        torch.cuda.synchronize()
-        tb = time.perf_counter()
-    elapsed = tb - ta
+    elapsed = run_steps(args, torch, step, K, Wm)
     print(f"[bench] timed {K} steps in {elapsed * 1e3:.2f} ms ({args.mode})", file=sys.stderr, flush=True)
 
     # profiled pass over the same steps: HIP events on the launch stream around
@@ -237,6 +228,187 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def run_steps(args, torch, step, K, Wm):
+    """Warm up, then time K steps: graph-replayed (one capture of all K) or eager."""
+    nsteps = K + Wm
+    if args.mode == "graph":
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for s in range(min(3, nsteps)):
+                step(s)
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_warm):
+            for s in range(Wm):
+                step(s)
+        with torch.cuda.graph(g_timed):
+            for s in range(Wm, nsteps):
+                step(s)
+        g_warm.replay()
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        g_timed.replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - ta
+    for s in range(Wm):
+        step(s)
+    torch.cuda.synchronize()
+    ta = time.perf_counter()
+    for s in range(Wm, nsteps):
+        step(s)
+    torch.cuda.synchronize()
+    return time.perf_counter() - ta
+
+
+def bench_decode_b64(args):
+    """64 tokens per step, top-6, Zipf(1.1)-skewed routing, the shared expert;
+    the (token, rank) pairs are grouped by expert so each selected expert
+    streams once per step."""
+    import torch
+
+    from mxfp4_routed_expert_renorm_amd import binding as lib
+    from mxfp4_routed_expert_renorm_amd import workloads as W
+
+    ci = 2
+    cfg = W.CONFIGS[ci]
+    seed = W.config_seed(ci)
+    E, H, I, k, T = cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"]
+    K, Wm = args.steps, args.warmup
+    nsteps = K + Wm
+    dev = torch.device("cuda:0")
+    bank, shared, rec_bytes = resident_bank(W, lib, torch, cfg, seed, dev)
+    ins = [W.make_layer_inputs(cfg, seed, s, with_bank=False) for s in range(nsteps)]
+    x_d = torch.from_numpy(np.stack([d["x"] for d in ins])).to(dev).view(torch.bfloat16)     # [steps, T, H]
+    lg_d = torch.from_numpy(np.stack([d["logits"] for d in ins])).to(dev)                    # [steps, T, E]
+    ids_d = torch.empty((nsteps, T, k), dtype=torch.int32, device=dev)
+    w_d = torch.empty((nsteps, T, k), dtype=torch.float32, device=dev)
+    out_d = torch.empty((nsteps, T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lib.moe_expert_workspace_bytes(H, I, T, k, True), dtype=torch.uint8, device=dev)
+    layer = lib.make_layer(H, I, fp4_base=bank, fp4_stride=rec_bytes, num_slots=E, shared=shared)
+    torch.cuda.synchronize()
+
+    def step(s):
+        lib.moe_route(lg_d[s], k, ids_d[s], w_d[s])
+        lib.moe_expert_forward(layer, x_d[s], T, k, ids_d[s], None, w_d[s], out_d[s], ws)
+
+    step(0)
+    torch.cuda.synchronize()
+    elapsed = run_steps(args, torch, step, K, Wm)
+    lib.moe_profile_begin(16 * K + 16)
+    for s in range(Wm, nsteps):
+        step(s)
+    prof = lib.moe_profile_end()
+    ids_h = ids_d[Wm:].cpu().numpy()
+    distinct = np.array([len(np.unique(ids_h[s])) for s in range(K)])
+    step_bytes = (distinct + 1) * rec_bytes                       # selected experts + shared, once each
+    value = K * T / elapsed
+    gbps = step_bytes.sum() / elapsed / 1e9
+    result = {
+        "metric": "MoE-layer tokens/s + achieved HBM GB/s (% of peak), MXFP4 256-expert decode (batch 64)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(elapsed / K * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4-w/bf16-x/f32-acc",
+        "data": "synthetic (seeded; fresh Zipf-skewed logits and activations every step)",
+        "config": {"workload": cfg["name"], "experts": E, "shared_experts": 1, "hidden": H,
+                   "expert_intermediate": I, "top_k": k, "tokens_per_step": T, "launch": args.mode,
+                   "distinct_experts_per_step_mean": round(float(distinct.mean()), 2)},
+        "step_hbm_GBps": round(gbps, 1), "step_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "kernel_avg_us": {n: round(v[0] / v[1] * 1e3, 3) for n, v in prof.items()},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def bench_slotcache(args):
+    """512 batch-1 tokens through 8 layers of 256 experts with a 512-slot HBM
+    cache, the (2,4) ladder and pinned host banks; per (token, layer): route,
+    moe_cache_ensure (one host sync, miss copies on a side stream), expert
+    MLP over the slot arena.  Cold start, as the workload defines it."""
+    import torch
+
+    from mxfp4_routed_expert_renorm_amd import binding as lib
+    from mxfp4_routed_expert_renorm_amd import workloads as W
+
+    ci = 4
+    cfg = W.CONFIGS[ci]
+    seed = W.config_seed(ci)
+    L, E, H, I, k, T, S = cfg["L"], cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"], cfg["slots"]
+    a, b = cfg["ladder"]
+    dev = torch.device("cuda:0")
+    rb4, rb2 = lib.moe_fp4_expert_bytes(H, I), lib.moe_int2_expert_bytes(H, I)
+    t0 = time.time()
+    print(f"[bench] pinning {L * E * (rb4 + rb2) / 1e9:.1f} GB of host banks", file=sys.stderr, flush=True)
+    fp4_host = lib.PinnedBuffer(L * E * rb4)
+    int2_host = lib.PinnedBuffer(L * E * rb2)
+    for p in range(L * E):
+        W.fp4_record(seed, W.S_BANK, p, H, I, out=fp4_host.array[p * rb4:(p + 1) * rb4])
+        W.int2_record(seed, W.S_INT2, p, H, I, out=int2_host.array[p * rb2:(p + 1) * rb2])
+        if p % 256 == 255:
+            print(f"[bench] {p + 1}/{L * E} host records", file=sys.stderr, flush=True)
+    arena = torch.empty(S * rb4, dtype=torch.uint8, device=dev)
+    staging = torch.empty((b - a) * rb2, dtype=torch.uint8, device=dev)
+    logits = W.slotcache_logits(seed, L, E, T, cfg["zipf"]).reshape(T * L, E)
+    lg_d = torch.from_numpy(logits).to(dev)
+    xs = np.stack([W.slotcache_x(seed, t, l, H)[0] for t in range(T) for l in range(L)])
+    x_d = torch.from_numpy(xs).to(dev).view(torch.bfloat16)                               # [T*L, H]
+    ids = torch.empty((1, k), dtype=torch.int32, device=dev)
+    w = torch.empty((1, k), dtype=torch.float32, device=dev)
+    prec = torch.empty((1, k), dtype=torch.int8, device=dev)
+    out_d = torch.empty((T * L, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lib.moe_expert_workspace_bytes(H, I, 1, k, False), dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream()
+    # host-link peak for this copy pattern: 64 records back to back from the pinned bank
+    src = torch.from_numpy(fp4_host.array[:64 * rb4])
+    dst = arena[:64 * rb4]
+    torch.cuda.synchronize()
+    tc = time.perf_counter()
+    with torch.cuda.stream(copy_stream):
+        for r in range(64):
+            dst[r * rb4:(r + 1) * rb4].copy_(src[r * rb4:(r + 1) * rb4], non_blocking=True)
+    torch.cuda.synchronize()
+    h2d_peak = 64 * rb4 / (time.perf_counter() - tc) / 1e9
+    print(f"[bench] setup {time.time() - t0:.1f} s; pinned copy rate {h2d_peak:.1f} GB/s",
+          file=sys.stderr, flush=True)
+
+    cache = lib.Cache(L, E, H, I, S, k, a, b, 1, fp4_host, int2_host, arena, staging)
+    layer = cache.layer()
+    t_tok = []
+    torch.cuda.synchronize()
+    ta = time.perf_counter()
+    for t in range(T):
+        for l in range(L):
+            row = t * L + l
+            lib.moe_route(lg_d[row:row + 1], k, ids, w)
+            cache.ensure(l, 1, ids, w, prec, copy=copy_stream)
+            lib.moe_expert_forward(layer, x_d[row:row + 1], 1, k, ids, prec, w, out_d[row:row + 1], ws)
+        t_tok.append(time.perf_counter())
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - ta
+    st = cache.stats()
+    cache.destroy()
+    steady = (t_tok[-1] - t_tok[T // 2 - 1]) / (T - T // 2)
+    uses = st["hits"] + st["misses"] + st["int2_uses"] + st["drops"]
+    result = {
+        "metric": "MoE tokens/s through 8 slot-cached layers (host-link bound), MXFP4 + 2-bit ladder",
+        "value": round(T / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": T, "warmup": 0,
+        "ms_per_step": round(elapsed / T * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4+int2-w/bf16-x/f32-acc",
+        "data": "synthetic (seeded; per-layer Zipf(1.1) logits, fresh activations per token and layer)",
+        "config": {"workload": cfg["name"], "layers": L, "experts": E, "slots": S, "top_k": k, "ladder": [a, b],
+                   "tokens": T, "cold_start": True},
+        "steady_state_ms_per_token": round(steady * 1e3, 4),
+        "cache": {**st, "hit_rate": round(st["hits"] / uses, 4)},
+        "h2d_GBps": round(st["bytes_h2d"] / elapsed / 1e9, 2),
+        "h2d_bytes_per_token": int(st["bytes_h2d"] / T),
+        "pinned_copy_GBps_measured": round(h2d_peak, 1),
+        "host_syncs_per_token": L,
+    }
+    fp4_host.free()
+    int2_host.free()
     print(json.dumps(result), flush=True)
 
 

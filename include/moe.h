@@ -167,6 +167,33 @@ moe_status moe_combine(const float* y, const float* w, const int8_t* prec, int T
 moe_status moe_debug_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out,
                              moe_stream_t stream);
 
+/* ------------------------------------------------------------ prefill */
+
+/* MXFP8 quantisation of a bf16 matrix along its rows: one E8M0 scale per 32
+ * consecutive elements, shared exponent floor(log2 amax) - 8 clamped to the E8M0
+ * range, elements rounded to the nearest FP8 E4M3 (ties to even) with saturation
+ * at +-448, an all-zero block gets scale byte 0 (the OCP Microscaling rule, cited
+ * by [P2] References).  x [rows][K] bf16, codes [rows][K] uint8, scales
+ * [rows][K/32] uint8; K a multiple of 32. */
+moe_status moe_quant_mxfp8(const void* x, int rows, int K, uint8_t* codes, uint8_t* scales, moe_stream_t stream);
+
+/* Workspace bytes of moe_prefill_forward. */
+size_t moe_prefill_workspace_bytes(int H, int I, int T, int k, int has_shared);
+
+/* Prefill-sized MoE layer on the matrix cores: x [T][H] bf16 quantised to MXFP8,
+ * (token, rank) pairs grouped by expert (moe_group's order), per expert the
+ * gate/up products on scaled FP8 x FP4 MFMA with SwiGLU and MXFP8 requantisation
+ * of h in the epilogue, the down products likewise, and the rank-ordered combine
+ * with the shared expert to out [T][H] bf16.  Every expert of the resident layer
+ * is streamed once per 256-token tile of its group.
+ *   layer: fp4_base/fp4_stride/num_slots = the E resident experts (slot = expert id),
+ *          shared optional, no 2-bit copies; H and I multiples of 64.
+ *   ids [T][k] int32 expert ids (moe_route's output), w [T][k] fp32 weights.
+ * T*(k+has_shared) <= 1<<20, E <= 4095. */
+moe_status moe_prefill_forward(const moe_layer* layer, const void* x, int T, int k, const int32_t* ids,
+                               const float* w, void* out, void* workspace, size_t workspace_bytes,
+                               moe_stream_t stream);
+
 /* ------------------------------------------------------------ slot cache */
 
 /* Pinned host memory of exactly `bytes` bytes (hipHostMalloc), for the expert

@@ -66,6 +66,10 @@ _SIGS = {
                                    c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "moe_combine": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p]),
     "moe_debug_dequant": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
+    "moe_quant_mxfp8": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "moe_prefill_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+    "moe_prefill_forward": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_int, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_pinned_alloc": (c_int, [c_size_t, ctypes.POINTER(c_void_p)]),
     "moe_pinned_free": (c_int, [c_void_p]),
     "moe_cache_create": (c_int, [ctypes.POINTER(moe_cache_desc), ctypes.POINTER(c_void_p)]),
@@ -190,6 +194,26 @@ def moe_combine(y, w, prec, T, k, H, has_shared, out, stream=None):
 
 def moe_debug_dequant(record, H, I, prec, matrix, out, stream=None):
     _check("moe_debug_dequant", load().moe_debug_dequant(_p(record), H, I, prec, matrix, _p(out), _stream(stream)))
+    return out
+
+
+# -------------------------------------------------------------------- prefill
+
+def moe_quant_mxfp8(x, codes, scales, stream=None):
+    rows, K = x.shape
+    _check("moe_quant_mxfp8", load().moe_quant_mxfp8(_p(x), rows, K, _p(codes), _p(scales), _stream(stream)))
+    return codes, scales
+
+
+def moe_prefill_workspace_bytes(H, I, T, k, has_shared) -> int:
+    return load().moe_prefill_workspace_bytes(H, I, T, k, int(bool(has_shared)))
+
+
+def moe_prefill_forward(layer: moe_layer, x, k, ids, w, out, workspace, stream=None):
+    T = x.shape[0]
+    st = load().moe_prefill_forward(ctypes.byref(layer), _p(x), T, k, _p(ids), _p(w), _p(out), _p(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("moe_prefill_forward", st)
     return out
 
 

@@ -40,6 +40,10 @@ moe_status launch_router_logits(const void* x, moe_dtype xt, const float* wr, in
                                 hipStream_t s);
 moe_status launch_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out, hipStream_t s);
 bool decode_shape_ok(int H, int I);
+size_t prefill_workspace_bytes(int H, int I, int T, int k, int has_shared);
+moe_status launch_quant_mxfp8(const void* x, long rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s);
+moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int k, const int32_t* ids, const float* w,
+                          void* out, void* workspace, hipStream_t s);
 bool b1_path_ok(int H, int I, int K1, bool xbf16);
 moe_status launch_b1(const moe_layer* L, const void* x, moe_dtype xt, int k, const int32_t* slot_ids,
                      const int8_t* prec, const float* w, void* h, void* out, moe_dtype ot, hipStream_t s);
@@ -166,6 +170,44 @@ moe_status moe_combine(const float* y, const float* w, const int8_t* prec, int T
   REQUIRE(y && w && out, MOE_EINVAL, "moe_combine: NULL pointer");
   REQUIRE(aligned(y, 16) && aligned(out, 8), MOE_EINVAL, "moe_combine: y must be 16-byte, out 8-byte aligned");
   return launch_combine(y, w, prec, T, k, H, has_shared ? 1 : 0, out, ot, (hipStream_t)stream);
+}
+
+moe_status moe_quant_mxfp8(const void* x, int rows, int K, uint8_t* codes, uint8_t* scales, moe_stream_t stream) {
+  REQUIRE(rows >= 0 && K >= 32 && K % 32 == 0, MOE_ESHAPE, "moe_quant_mxfp8: rows=%d K=%d (K a multiple of 32)", rows,
+          K);
+  if (rows == 0) return MOE_OK;
+  REQUIRE(x && codes && scales, MOE_EINVAL, "moe_quant_mxfp8: NULL pointer");
+  REQUIRE(aligned(x, 16) && aligned(codes, 16), MOE_EINVAL, "moe_quant_mxfp8: x and codes must be 16-byte aligned");
+  return launch_quant_mxfp8(x, rows, K, codes, scales, (hipStream_t)stream);
+}
+
+size_t moe_prefill_workspace_bytes(int H, int I, int T, int k, int has_shared) {
+  if (H <= 0 || I <= 0 || T < 0 || k <= 0) return 0;
+  return prefill_workspace_bytes(H, I, T, k, has_shared);
+}
+
+moe_status moe_prefill_forward(const moe_layer* layer, const void* x, int T, int k, const int32_t* ids, const float* w,
+                               void* out, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  REQUIRE(layer, MOE_EINVAL, "moe_prefill_forward: layer is NULL");
+  const int H = layer->H, I = layer->I, E = layer->num_slots;
+  REQUIRE(H >= 64 && I >= 64 && H % 64 == 0 && I % 64 == 0, MOE_ESHAPE,
+          "moe_prefill_forward: H=%d I=%d must be multiples of 64", H, I);
+  REQUIRE(E >= 1 && E <= 4095, MOE_ESHAPE, "moe_prefill_forward: num_slots (experts) = %d outside 1..4095", E);
+  REQUIRE(k >= 1 && k <= E && k <= 64, MOE_EINVAL, "moe_prefill_forward: k=%d (E=%d)", k, E);
+  const int K1 = k + (layer->shared ? 1 : 0);
+  REQUIRE(T >= 0 && (long)T * K1 <= (1L << 20), MOE_ESHAPE, "moe_prefill_forward: T=%d too large", T);
+  if (T == 0) return MOE_OK;
+  REQUIRE(layer->fp4_base && x && ids && w && out && workspace, MOE_EINVAL, "moe_prefill_forward: NULL pointer");
+  const size_t fb = record_layout(H, I, 4).bytes;
+  REQUIRE(layer->fp4_stride >= fb && layer->fp4_stride % 16 == 0, MOE_EINVAL,
+          "moe_prefill_forward: fp4_stride=%zu must be >= %zu and a multiple of 16", layer->fp4_stride, fb);
+  REQUIRE(aligned(layer->fp4_base, 16) && aligned(layer->shared, 16) && aligned(x, 16) && aligned(out, 16) &&
+              aligned(workspace, 256),
+          MOE_EINVAL, "moe_prefill_forward: records, x, out 16-byte and workspace 256-byte aligned");
+  const size_t need = prefill_workspace_bytes(H, I, T, k, layer->shared ? 1 : 0);
+  REQUIRE(workspace_bytes >= need, MOE_ENOMEM, "moe_prefill_forward: workspace %zu bytes < %zu needed",
+          workspace_bytes, need);
+  return launch_prefill(layer, E, x, T, k, ids, w, out, workspace, (hipStream_t)stream);
 }
 
 moe_status moe_debug_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out,
