@@ -38,9 +38,10 @@ def parse():
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
                     help="graph: the timed steps are captured into one HIP graph and replayed; "
                          "eager: one launch sequence per step from the host")
-    ap.add_argument("--workload", choices=("decode-b1", "decode-b64", "slotcache"), default="decode-b1",
+    ap.add_argument("--workload", choices=("decode-b1", "decode-b64", "prefill", "slotcache"), default="decode-b1",
                     help="decode-b1 (default, the headline line): batch-1 decode of a resident 256-expert "
                          "layer; decode-b64: 64 tokens, top-6, Zipf-skewed routing, grouped by expert; "
+                         "prefill: 4096 tokens, top-8, MXFP8 x MXFP4 scaled MFMA; "
                          "slotcache: 512 tokens x 8 layers through the 512-slot cache with the (2,4) ladder")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -114,6 +115,8 @@ def main():
         return bench_decode_b64(args)
     if args.workload == "slotcache":
         return bench_slotcache(args)
+    if args.workload == "prefill":
+        return bench_prefill(args)
     return bench_decode_b1(args)
 
 
@@ -319,6 +322,69 @@ def bench_decode_b64(args):
                    "distinct_experts_per_step_mean": round(float(distinct.mean()), 2)},
         "step_hbm_GBps": round(gbps, 1), "step_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "kernel_avg_us": {n: round(v[0] / v[1] * 1e3, 3) for n, v in prof.items()},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(args):
+    """4096 tokens through the resident 256-expert layer (+ shared), top-8:
+    route, then MXFP8 activations x MXFP4 weights on the scaled MFMA, grouped
+    by expert, SwiGLU and requantisation fused, combine to bf16."""
+    import torch
+
+    from mxfp4_routed_expert_renorm_amd import binding as lib
+    from mxfp4_routed_expert_renorm_amd import workloads as W
+
+    ci = 3
+    cfg = W.CONFIGS[ci]
+    seed = W.config_seed(ci)
+    E, H, I, k, T = cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"]
+    K, Wm = args.steps, args.warmup
+    nsteps = K + Wm
+    dev = torch.device("cuda:0")
+    bank, shared, rec_bytes = resident_bank(W, lib, torch, cfg, seed, dev)
+    ins = [W.make_layer_inputs(cfg, seed, s, with_bank=False) for s in range(nsteps)]
+    x_d = torch.from_numpy(np.stack([d["x"] for d in ins])).to(dev).view(torch.bfloat16)     # [steps, T, H]
+    lg_d = torch.from_numpy(np.stack([d["logits"] for d in ins])).to(dev)                    # [steps, T, E]
+    ids_d = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w_d = torch.empty((T, k), dtype=torch.float32, device=dev)
+    out_d = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lib.moe_prefill_workspace_bytes(H, I, T, k, True), dtype=torch.uint8, device=dev)
+    layer = lib.make_layer(H, I, fp4_base=bank, fp4_stride=rec_bytes, num_slots=E, shared=shared)
+    torch.cuda.synchronize()
+
+    def step(s):
+        lib.moe_route(lg_d[s], k, ids_d, w_d)
+        lib.moe_prefill_forward(layer, x_d[s], k, ids_d, w_d, out_d, ws)
+
+    step(0)
+    torch.cuda.synchronize()
+    elapsed = run_steps(args, torch, step, K, Wm)
+    lib.moe_profile_begin(16 * K + 16)
+    for s in range(Wm, nsteps):
+        step(s)
+    prof = lib.moe_profile_end()
+    kus = {n: round(v[0] / v[1] * 1e3, 3) for n, v in prof.items()}
+    pairs = T * (k + 1)
+    flops = pairs * 2 * 3 * H * I                       # gate, up, down per (token, expert)
+    gemm_s = (prof["gemm_gateup"][0] / prof["gemm_gateup"][1] + prof["gemm_down"][0] / prof["gemm_down"][1]) / 1e3
+    wbytes = (E + 1) * rec_bytes
+    result = {
+        "metric": "MoE-layer prefill tokens/s + MFMA fraction, MXFP4 256-expert layer (4096 tokens)",
+        "value": round(K * T / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp8-x/mxfp4-w/f32-acc",
+        "data": "synthetic (seeded; fresh logits and activations every step)",
+        "config": {"workload": cfg["name"], "experts": E, "shared_experts": 1, "hidden": H,
+                   "expert_intermediate": I, "top_k": k, "tokens_per_step": T, "launch": args.mode},
+        "roofline": {"bound": "mfma", "kernel": "gemm_gateup_kernel + gemm_down_kernel",
+                     "achieved": round(flops / gemm_s / 1e12, 1), "peak": 5000.0, "unit": "TFLOP/s",
+                     "frac": round(flops / gemm_s / 1e12 / 5000.0, 4),
+                     "frac_vs_fp4_peak": round(flops / gemm_s / 1e12 / 10100.0, 4),
+                     "flops_per_step": flops, "traffic": None},
+        "weight_bytes_per_step": wbytes,
+        "gemm_weight_GBps": round(wbytes / gemm_s / 1e9, 1),
+        "kernel_avg_us": kus,
     }
     print(json.dumps(result), flush=True)
 

@@ -13,7 +13,8 @@
 //   current row is converted, multiplied and reduced.  A row of K = H
 //   elements is split over the 64 lanes in 32-element chunks (one 16-byte
 //   FP4 load plus one scale byte per lane and chunk); the token's activations
-//   for the lane's chunks are loaded once.  The gate and up sums are reduced
+//   are staged in LDS once per workgroup and read per row, which keeps the
+//   register count low enough for several wavefronts per SIMD.  The gate and up sums are reduced
 //   with DPP lane moves and lane 63 writes silu(g) * u.
 //
 // down_combine_b1_kernel: a workgroup owns a tile of output rows for every
@@ -32,6 +33,9 @@
 #endif
 #ifndef MOE_B1_GU_DEPTH
 #define MOE_B1_GU_DEPTH 3
+#endif
+#ifndef MOE_B1_GU_OCC
+#define MOE_B1_GU_OCC 3
 #endif
 #ifndef MOE_B1_DN_ROWS
 #define MOE_B1_DN_ROWS 2
@@ -202,19 +206,28 @@ struct GURow {
 };
 
 template <int CPL, bool XBF16, int D>
-__global__ __launch_bounds__(256) void gateup_b1_kernel(B1Args a) {
+__global__ __launch_bounds__(256, MOE_B1_GU_OCC) void gateup_b1_kernel(B1Args a) {
+  // the token's activations, staged once per workgroup; each lane reads its
+  // chunks from LDS per row instead of holding them in registers
+  __shared__ __align__(16) uint8_t xs[CPL * 64 * 32 * (XBF16 ? 2 : 4)];
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
   const int H = a.H, I = a.I;
+  {
+    const int nv = H * (XBF16 ? 2 : 4) / 16;
+    for (int v = threadIdx.x; v < nv; v += 256) ((uint4*)xs)[v] = ((const uint4*)a.x)[v];
+  }
+  __syncthreads();
   const int total = a.K1 * I;
   const int per = (total + nw - 1) / nw;
   const int j0 = gw * per, j1 = min(j0 + per, total);
   if (j0 >= j1) return;
-
-  Act<XBF16> xa[CPL];
-#pragma unroll
-  for (int q = 0; q < CPL; ++q) xa[q].load_global(a.x, (size_t)(q * 64 + lane) * 32);
+  auto xchunk = [&](int q) {
+    Act<XBF16> x;
+    x.load_lds(xs, (size_t)(q * 64 + lane) * 32);
+    return x;
+  };
 
   const size_t rowb4 = (size_t)H / 2, rowb2 = (size_t)H / 4, rows = (size_t)H / 32;
   for (int g = j0 / I; g <= (j1 - 1) / I; ++g) {
@@ -222,8 +235,9 @@ __global__ __launch_bounds__(256) void gateup_b1_kernel(B1Args a) {
     int pr;
     const uint8_t* rec = b1_group(a, g, &pr);
     if (pr < 0) continue;
-    const RecordLayout L = record_layout(H, I, pr == 0 ? 4 : 2);
-    if (pr == 0) {
+    if (pr != 0) continue;  // 2-bit groups run in gateup_int2_b1_kernel
+    const RecordLayout L = record_layout(H, I, 4);
+    {
       const uint8_t* w1 = rec + L.w1c;
       const uint8_t* w3 = rec + L.w3c;
       const uint8_t* s1 = rec + L.w1s;
@@ -244,8 +258,9 @@ __global__ __launch_bounds__(256) void gateup_b1_kernel(B1Args a) {
         float gs = 0.0f, us = 0.0f;
 #pragma unroll
         for (int q = 0; q < CPL; ++q) {
-          gs = fmaf(xa[q].fp4(s.c1[q]), e8m0_to_f32(s.s1[q]), gs);
-          us = fmaf(xa[q].fp4(s.c3[q]), e8m0_to_f32(s.s3[q]), us);
+          const Act<XBF16> xq = xchunk(q);
+          gs = fmaf(xq.fp4(s.c1[q]), e8m0_to_f32(s.s1[q]), gs);
+          us = fmaf(xq.fp4(s.c3[q]), e8m0_to_f32(s.s3[q]), us);
         }
         gs = wave_sum_to_lane63(gs);
         us = wave_sum_to_lane63(us);
@@ -275,21 +290,40 @@ __global__ __launch_bounds__(256) void gateup_b1_kernel(B1Args a) {
 #pragma unroll
       for (int u = 0; u < D; ++u)
         if (row + D + u < r1) consume(row + D + u, sl[u]);
-    } else {
-      for (int row = r0; row < r1; ++row) {
-        float gs = 0.0f, us = 0.0f;
+    }
+  }
+}
+
+// 2-bit groups of the batch-1 gate/up (the slot cache's fallback copies):
+// a separate kernel so the FP4 streaming kernel keeps its register budget.
+// One wavefront per row; the activations come from global memory (L2).
+template <int CPL, bool XBF16>
+__global__ __launch_bounds__(256) void gateup_int2_b1_kernel(B1Args a) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  const int H = a.H, I = a.I;
+  const RecordLayout L = record_layout(H, I, 2);
+  const size_t rowb2 = (size_t)H / 4, rows = (size_t)H / 32;
+  for (int g = 0; g < a.K1; ++g) {
+    int pr;
+    const uint8_t* rec = b1_group(a, g, &pr);
+    if (pr != 1) continue;
+    for (int row = gw; row < I; row += nw) {
+      float gs = 0.0f, us = 0.0f;
 #pragma unroll
-        for (int q = 0; q < CPL; ++q) {
-          const size_t c = (size_t)(q * 64 + lane);
-          const uint2 c1 = ld_stream8(rec + L.w1c + (size_t)row * rowb2 + c * 8);
-          const uint2 c3 = ld_stream8(rec + L.w3c + (size_t)row * rowb2 + c * 8);
-          gs = fmaf(xa[q].int2(c1), e4m3_to_f32(rec[L.w1s + (size_t)row * rows + c]), gs);
-          us = fmaf(xa[q].int2(c3), e4m3_to_f32(rec[L.w3s + (size_t)row * rows + c]), us);
-        }
-        gs = wave_sum_to_lane63(gs);
-        us = wave_sum_to_lane63(us);
-        if (lane == 63) store_h<XBF16>(a.h, (size_t)g * I + row, silu_mul_b1(gs, us));
+      for (int q = 0; q < CPL; ++q) {
+        const size_t c = (size_t)(q * 64 + lane);
+        const uint2 c1 = ld_stream8(rec + L.w1c + (size_t)row * rowb2 + c * 8);
+        const uint2 c3 = ld_stream8(rec + L.w3c + (size_t)row * rowb2 + c * 8);
+        Act<XBF16> xq;
+        xq.load_global(a.x, c * 32);
+        gs = fmaf(xq.int2(c1), e4m3_to_f32(rec[L.w1s + (size_t)row * rows + c]), gs);
+        us = fmaf(xq.int2(c3), e4m3_to_f32(rec[L.w3s + (size_t)row * rows + c]), us);
       }
+      gs = wave_sum_to_lane63(gs);
+      us = wave_sum_to_lane63(us);
+      if (lane == 63) store_h<XBF16>(a.h, (size_t)g * I + row, silu_mul_b1(gs, us));
     }
   }
 }
@@ -445,6 +479,13 @@ void launch_gateup_b1(const B1Args& a, bool xbf16, hipStream_t s) {
     hipLaunchKernelGGL((gateup_b1_kernel<CPL, true, MOE_B1_GU_DEPTH>), dim3(grid), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((gateup_b1_kernel<CPL, false, MOE_B1_GU_DEPTH>), dim3(grid), dim3(256), 0, s, a);
+  if (a.prec) {  // 2-bit copies can only appear when precisions are given
+    const int grid2 = std::max(1, std::min(a.I / 4, 1024));
+    if (xbf16)
+      hipLaunchKernelGGL((gateup_int2_b1_kernel<CPL, true>), dim3(grid2), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gateup_int2_b1_kernel<CPL, false>), dim3(grid2), dim3(256), 0, s, a);
+  }
 }
 
 template <int CPL, bool HBF16>

@@ -32,7 +32,11 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kMT = 256;      // token rows per GEMM item (8 MFMA row blocks, 2 per wave)
+#ifndef MOE_PF_WAVES
+#define MOE_PF_WAVES 8
+#endif
+constexpr int kWaves = MOE_PF_WAVES;  // wavefronts per GEMM workgroup, one 32-row block each
+constexpr int kMT = 32 * kWaves;      // grouped token rows per GEMM item
 constexpr int kNT = 64;       // weight rows per GEMM item (2 MFMA column blocks)
 constexpr int kMaxKeys = 4096;
 
@@ -179,23 +183,6 @@ __device__ __forceinline__ int virtual_block() {
   return (blockIdx.x % 8) * per + blockIdx.x / 8;
 }
 
-__device__ __forceinline__ v8i load_a(const uint8_t* row, int k0, int h) {
-  const uint4 lo = *(const uint4*)(row + k0 + 16 * h);
-  const uint4 hi = *(const uint4*)(row + k0 + 32 + 16 * h);
-  v8i r;
-  r[0] = (int)lo.x, r[1] = (int)lo.y, r[2] = (int)lo.z, r[3] = (int)lo.w;
-  r[4] = (int)hi.x, r[5] = (int)hi.y, r[6] = (int)hi.z, r[7] = (int)hi.w;
-  return r;
-}
-
-__device__ __forceinline__ v8i load_b(const uint8_t* wrow, int k0, int h) {
-  const uint4 q = ld_stream16(wrow + (k0 + 32 * h) / 2);
-  v8i r;
-  r[0] = (int)q.x, r[1] = (int)q.y, r[2] = (int)q.z, r[3] = (int)q.w;
-  r[4] = 0, r[5] = 0, r[6] = 0, r[7] = 0;
-  return r;
-}
-
 __device__ __forceinline__ v16f mfma_fp8_fp4(v8i a, v8i b, v16f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
 }
@@ -210,97 +197,192 @@ __device__ __forceinline__ float half_wave_max(float v) {
   return v;
 }
 
-// ------------------------------------------------------------- gate / up GEMM
+// ------------------------------------------------------------- grouped GEMM
+//
+// One template for both products.  An item is (M tile = up to 256 grouped rows
+// of one expert, N tile = 64 weight rows of each of NMAT matrices).  The
+// workgroup's 8 wavefronts own one 32-row block of the M tile each and every
+// 32x32 output block of the N tile.  K advances 128 at a time through a
+// double-buffered LDS stage: each thread's share of the next stage's
+// activation rows, weight rows and their scale bytes is loaded into registers
+// while the current stage feeds the MFMAs, then written to the other buffer.
+// LDS rows are padded by 16 bytes so the 32 rows a fragment read touches fall
+// in different banks.  Items run N tile innermost and each XCD takes a
+// contiguous range, so the N tiles of one M tile share its activation rows in
+// one L2 while the expert's weights stream from HBM once per M tile.
 
-// item = (M tile of one expert's grouped rows, 64 intermediate rows); wave w owns
-// row blocks w and w+4 of the M tile and both 32-row column blocks, for W1 and W3
-__global__ __launch_bounds__(256) void gemm_gateup_kernel(PrefillArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+constexpr int kKS = 128;                 // K per stage
+constexpr int kArow = kKS + 16;          // padded bytes per activation row in LDS
+constexpr int kBrow = kKS / 2 + 16;      // padded bytes per weight row in LDS
+
+template <int NMAT>
+struct GemmSmem {
+  uint8_t a[2][kMT * kArow];
+  uint8_t b[2][NMAT * kNT * kBrow];
+  uint32_t as[2][kMT];                  // 4 scale bytes (this stage's 4 blocks) per row
+  uint32_t bs[2][NMAT * kNT];
+};
+
+// 16-byte pieces of the weight tile per thread (4 pieces per 64-byte row)
+template <int NMAT>
+constexpr int pieces_b() { return (NMAT * kNT * 4 + kWaves * 64 - 1) / (kWaves * 64); }
+
+template <int NMAT>
+struct StageRegs {
+  uint4 a[4];              // 64 activation bytes: half of row tid/2
+  uint4 b[pieces_b<NMAT>()];  // weight pieces tid + j*threads
+  uint32_t as, bs;         // scale dwords of activation row tid and weight row tid
+};
+
+// thread tid loads, for K [k0, k0+kKS): 64 bytes of activation row tid/2, the 4
+// scale bytes of activation row tid (tid < kMT), 16-byte pieces p = tid +
+// j*threads of the weight tile (row p/4, quarter p%4) and the 4 scale bytes of
+// weight row tid (tid < NMAT*kNT)
+template <int NMAT>
+__device__ __forceinline__ void stage_load(StageRegs<NMAT>& r, const uint8_t* arow, const uint8_t* asrow,
+                                           const uint8_t* const* brow, const uint8_t* bsrow, int k0, int tid,
+                                           bool arow_live, bool asrow_live) {
+  if (arow_live) {  // rows past the group's end feed only discarded outputs: not loaded
+    const uint4* ap = (const uint4*)(arow + k0 + 64 * (tid & 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.a[i] = ap[i];
+  }
+  if (tid < kMT && asrow_live) r.as = *(const uint32_t*)(asrow + k0 / 32);
+#pragma unroll
+  for (int j = 0; j < pieces_b<NMAT>(); ++j) {
+    const int p = tid + j * kWaves * 64;
+    if (p < NMAT * kNT * 4) r.b[j] = ld_stream16(brow[j] + k0 / 2 + 16 * (p & 3));
+  }
+  if (tid < NMAT * kNT) r.bs = *(const uint32_t*)(bsrow + k0 / 32);
+}
+
+template <int NMAT>
+__device__ __forceinline__ void stage_store(GemmSmem<NMAT>& sm, int buf, const StageRegs<NMAT>& r, int tid,
+                                            bool arow_live, bool asrow_live) {
+  if (arow_live) {
+    uint4* ad = (uint4*)(sm.a[buf] + (tid >> 1) * kArow + 64 * (tid & 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ad[i] = r.a[i];
+  }
+  if (tid < kMT && asrow_live) sm.as[buf][tid] = r.as;
+#pragma unroll
+  for (int j = 0; j < pieces_b<NMAT>(); ++j) {
+    const int p = tid + j * kWaves * 64;
+    if (p < NMAT * kNT * 4) *(uint4*)(sm.b[buf] + (p >> 2) * kBrow + 16 * (p & 3)) = r.b[j];
+  }
+  if (tid < NMAT * kNT) sm.bs[buf][tid] = r.bs;
+}
+
+// NMAT = 2: gate/up (W1, W3 of the expert, K = H), SwiGLU + MXFP8 epilogue into hq/hs.
+// NMAT = 1: down (W2, K = I), bf16 epilogue into y at each row's (token, rank) pair.
+template <int NMAT>
+__global__ __launch_bounds__(kWaves * 64) void gemm_kernel(PrefillArgs a) {
+  __shared__ GemmSmem<NMAT> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, h = lane >> 5;
   const int H = a.H, I = a.I;
-  const int ntiles = I / kNT;
+  const int K = NMAT == 2 ? H : I;        // reduction length
+  const int Nall = NMAT == 2 ? I : H;     // weight rows per matrix
+  const int ntiles = Nall / kNT;
   const int nitems = a.items[0] * ntiles;
   const RecordLayout L = record_layout(H, I, 4);
-  const size_t rowb = (size_t)H / 2, rows = (size_t)H / 32;
+  const size_t wrowb = (size_t)K / 2, wrows = (size_t)K / 32;
 
   for (int item = virtual_block(); item < nitems; item += gridDim.x) {
     const int mi = item / ntiles, nt = item - mi * ntiles;
     const int key = a.items[1 + 2 * mi], row0 = a.items[2 + 2 * mi];
     const int start = a.offsets[key], count = a.offsets[key + 1] - start;
     const uint8_t* rec = key_record(a, key);
-    // the wave's two row blocks (token rows) and their activation rows
-    int nrb = 0;
-    const uint8_t* arow[2];
-    const uint8_t* srow[2];
-    bool live[2];
+    // this thread's load rows: activation row tid/2 (codes) and tid (scales),
+    // weight row tid/4 (codes) and tid (scales)
+    auto act_rows = [&](int i, const uint8_t** codes, const uint8_t** scales) {
+      const int ri = min(row0 + i, count - 1);
+      if (NMAT == 2) {
+        const int t = a.perm[start + ri] / a.K1;
+        *codes = a.xq + (size_t)t * H;
+        *scales = a.xs + (size_t)t * (H / 32);
+      } else {
+        *codes = a.hq + (size_t)(start + ri) * I;
+        *scales = a.hs + (size_t)(start + ri) * (I / 32);
+      }
+    };
+    auto weight_rows = [&](int wr, const uint8_t** codes, const uint8_t** scales) {
+      wr = min(wr, NMAT * kNT - 1);
+      const int mat = wr / kNT;
+      const size_t n = (size_t)(nt * kNT + (wr % kNT));
+      const size_t code_off = NMAT == 2 ? (mat == 0 ? L.w1c : L.w3c) : L.w2c;
+      const size_t scale_off = NMAT == 2 ? (mat == 0 ? L.w1s : L.w3s) : L.w2s;
+      *codes = rec + code_off + n * wrowb;
+      *scales = rec + scale_off + n * wrows;
+    };
+    const uint8_t *arow, *asrow, *bsrow, *unused;
+    const uint8_t* brow[pieces_b<NMAT>()];
+    act_rows(tid >> 1, &arow, &unused);
+    act_rows(min(tid, kMT - 1), &unused, &asrow);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = row0 + (wave + 4 * j) * 32;  // first row of the block
-      live[j] = r < count;
-      nrb += live[j] ? 1 : 0;
-      const int pos = min(r + c, count - 1);
-      const int t = a.perm[start + pos] / a.K1;
-      arow[j] = a.xq + (size_t)t * H;
-      srow[j] = a.xs + (size_t)t * (H / 32);
-    }
-    if (nrb == 0) continue;
-    const uint8_t* w1r[2];
-    const uint8_t* w3r[2];
-    const uint8_t* s1r[2];
-    const uint8_t* s3r[2];
+    for (int j = 0; j < pieces_b<NMAT>(); ++j) weight_rows((tid + j * kWaves * 64) >> 2, &brow[j], &unused);
+    weight_rows(tid, &unused, &bsrow);
+    const bool live = row0 + wave * 32 < count;
+    const bool arow_live = row0 + (tid >> 1) < count;
+    const bool asrow_live = row0 + tid < count;
+
+    v16f acc[NMAT][2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const size_t n = (size_t)(nt * kNT + nb * 32 + c);
-      w1r[nb] = rec + L.w1c + n * rowb;
-      w3r[nb] = rec + L.w3c + n * rowb;
-      s1r[nb] = rec + L.w1s + n * rows;
-      s3r[nb] = rec + L.w3s + n * rows;
-    }
-    v16f acc_g[2][2], acc_u[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc_g[j][nb][i] = 0.0f, acc_u[j][nb][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) acc[m][nb][i] = 0.0f;
 
-    for (int k0 = 0; k0 < H; k0 += 64) {
-      const int kb = k0 / 32 + h;
-      v8i bg[2], bu[2];
-      int sg[2], su[2];
+    StageRegs<NMAT> st;
+    stage_load<NMAT>(st, arow, asrow, brow, bsrow, 0, tid, arow_live, asrow_live);
+    __syncthreads();  // the previous item's last stage reads are done
+    stage_store<NMAT>(sm, 0, st, tid, arow_live, asrow_live);
+    __syncthreads();
+    const int nstage = K / kKS;
+    for (int s = 0; s < nstage; ++s) {
+      const int buf = s & 1;
+      if (s + 1 < nstage) stage_load<NMAT>(st, arow, asrow, brow, bsrow, (s + 1) * kKS, tid, arow_live, asrow_live);
+      if (live) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        bg[nb] = load_b(w1r[nb], k0, h);
-        bu[nb] = load_b(w3r[nb], k0, h);
-        sg[nb] = s1r[nb][kb];
-        su[nb] = s3r[nb][kb];
-      }
+        for (int kc = 0; kc < kKS / 64; ++kc) {
+          const uint8_t* ar = sm.a[buf] + (wave * 32 + c) * kArow + kc * 64;
+          const uint4 lo = *(const uint4*)(ar + 16 * h);
+          const uint4 hi = *(const uint4*)(ar + 32 + 16 * h);
+          v8i av;
+          av[0] = (int)lo.x, av[1] = (int)lo.y, av[2] = (int)lo.z, av[3] = (int)lo.w;
+          av[4] = (int)hi.x, av[5] = (int)hi.y, av[6] = (int)hi.z, av[7] = (int)hi.w;
+          const int sa = (int)((sm.as[buf][wave * 32 + c] >> (8 * (2 * kc + h))) & 0xffu);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (!live[j]) continue;
-        const v8i av = load_a(arow[j], k0, h);
-        const int sa = srow[j][kb];
+          for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          acc_g[j][nb] = mfma_fp8_fp4(av, bg[nb], acc_g[j][nb], sa, sg[nb]);
-          acc_u[j][nb] = mfma_fp8_fp4(av, bu[nb], acc_u[j][nb], sa, su[nb]);
+            for (int nb = 0; nb < 2; ++nb) {
+              const int r = m * kNT + nb * 32 + c;
+              const uint4 q = *(const uint4*)(sm.b[buf] + r * kBrow + kc * 32 + 16 * h);
+              v8i bv;
+              bv[0] = (int)q.x, bv[1] = (int)q.y, bv[2] = (int)q.z, bv[3] = (int)q.w;
+              bv[4] = 0, bv[5] = 0, bv[6] = 0, bv[7] = 0;
+              const int sb = (int)((sm.bs[buf][r] >> (8 * (2 * kc + h))) & 0xffu);
+              acc[m][nb] = mfma_fp8_fp4(av, bv, acc[m][nb], sa, sb);
+            }
         }
       }
+      if (s + 1 < nstage) stage_store<NMAT>(sm, buf ^ 1, st, tid, arow_live, asrow_live);
+      __syncthreads();
     }
-    // SwiGLU, MXFP8 requantisation along I (a 32-column block is one half-wave row)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (!live[j]) continue;
+    if (!live) continue;
+    if (NMAT == 2) {
+      // SwiGLU, MXFP8 requantisation along I (a 32-column block is one half-wave row)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int col = nt * kNT + nb * 32 + c;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float g = acc_g[j][nb][i], u = acc_u[j][nb][i];
+          const float g = acc[0][nb][i], u = acc[NMAT - 1][nb][i];
           const float hv = g / (1.0f + expf(-g)) * u;
           const float amax = half_wave_max(fabsf(hv));
           const int sh = mx_shared_exp(amax);
-          const int r = row0 + (wave + 4 * j) * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+          const int r = row0 + wave * 32 + 8 * (i / 4) + 4 * h + (i % 4);
           if (r < count) {
             const size_t pos = (size_t)(start + r);
             a.hq[pos * I + col] = (uint8_t)e4m3_encode(ldexpf(hv, -sh));
@@ -308,85 +390,14 @@ __global__ __launch_bounds__(256) void gemm_gateup_kernel(PrefillArgs a) {
           }
         }
       }
-    }
-  }
-}
-
-// ----------------------------------------------------------------- down GEMM
-
-// item = (M tile of grouped rows, 64 output columns of H); the grouped h rows are
-// contiguous; each result goes to its (token, rank) pair as bf16
-__global__ __launch_bounds__(256) void gemm_down_kernel(PrefillArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 31, h = lane >> 5;
-  const int H = a.H, I = a.I;
-  const int ntiles = H / kNT;
-  const int nitems = a.items[0] * ntiles;
-  const RecordLayout L = record_layout(H, I, 4);
-  const size_t rowb = (size_t)I / 2, rows = (size_t)I / 32;
-
-  for (int item = virtual_block(); item < nitems; item += gridDim.x) {
-    const int mi = item / ntiles, nt = item - mi * ntiles;
-    const int key = a.items[1 + 2 * mi], row0 = a.items[2 + 2 * mi];
-    const int start = a.offsets[key], count = a.offsets[key + 1] - start;
-    const uint8_t* rec = key_record(a, key);
-    const uint8_t* arow[2];
-    const uint8_t* srow[2];
-    bool live[2];
-    int nrb = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = row0 + (wave + 4 * j) * 32;
-      live[j] = r < count;
-      nrb += live[j] ? 1 : 0;
-      const size_t pos = (size_t)(start + min(r + c, count - 1));
-      arow[j] = a.hq + pos * I;
-      srow[j] = a.hs + pos * (I / 32);
-    }
-    if (nrb == 0) continue;
-    const uint8_t* wr[2];
-    const uint8_t* sr[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const size_t n = (size_t)(nt * kNT + nb * 32 + c);
-      wr[nb] = rec + L.w2c + n * rowb;
-      sr[nb] = rec + L.w2s + n * rows;
-    }
-    v16f acc[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[j][nb][i] = 0.0f;
-    for (int k0 = 0; k0 < I; k0 += 64) {
-      const int kb = k0 / 32 + h;
-      v8i bw[2];
-      int sw[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        bw[nb] = load_b(wr[nb], k0, h);
-        sw[nb] = sr[nb][kb];
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (!live[j]) continue;
-        const v8i av = load_a(arow[j], k0, h);
-        const int sa = srow[j][kb];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[j][nb] = mfma_fp8_fp4(av, bw[nb], acc[j][nb], sa, sw[nb]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (!live[j]) continue;
+    } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = row0 + (wave + 4 * j) * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+        const int r = row0 + wave * 32 + 8 * (i / 4) + 4 * h + (i % 4);
         if (r < count) {
           const size_t pair = (size_t)a.perm[start + r];
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) a.y[pair * H + nt * kNT + nb * 32 + c] = f32_to_bf16(acc[j][nb][i]);
+          for (int nb = 0; nb < 2; ++nb) a.y[pair * H + nt * kNT + nb * 32 + c] = f32_to_bf16(acc[0][nb][i]);
         }
       }
     }
@@ -495,18 +506,20 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
     hipLaunchKernelGGL(prefill_items_kernel, dim3(1), dim3(64), 0, s, a.counts, E + 1, a.items);
     MOE_LAUNCH_CHECK();
   }
-  // persistent grids, a multiple of 8 workgroups (one share per XCD)
+  // persistent grids: as many workgroups as fit per CU (LDS-limited: one of 8
+  // wavefronts or two of 4), a multiple of 8 (one share per XCD)
+  const long per_cu = kWaves >= 8 ? 1 : 2;
   const int max_items_m = P / kMT + E + 1;
-  const int grid_gu = (int)std::min<long>((long)max_items_m * (I / kNT), 256L * 8) / 8 * 8;
-  const int grid_dn = (int)std::min<long>((long)max_items_m * (H / kNT), 256L * 8) / 8 * 8;
+  const int grid_gu = (int)std::min<long>((long)max_items_m * (I / kNT), 256L * per_cu) / 8 * 8;
+  const int grid_dn = (int)std::min<long>((long)max_items_m * (H / kNT), 256L * per_cu) / 8 * 8;
   {
     ProfScope prof(MOE_PROF_GEMM_GATEUP, s);
-    hipLaunchKernelGGL(gemm_gateup_kernel, dim3(std::max(grid_gu, 8)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gemm_kernel<2>, dim3(std::max(grid_gu, 8)), dim3(kWaves * 64), 0, s, a);
     MOE_LAUNCH_CHECK();
   }
   {
     ProfScope prof(MOE_PROF_GEMM_DOWN, s);
-    hipLaunchKernelGGL(gemm_down_kernel, dim3(std::max(grid_dn, 8)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gemm_kernel<1>, dim3(std::max(grid_dn, 8)), dim3(kWaves * 64), 0, s, a);
     MOE_LAUNCH_CHECK();
   }
   {
