@@ -5,8 +5,9 @@ Workload (the layer the pages' model uses at decode: 256 routed experts plus
 one shared expert, hidden 4096, expert intermediate 2048, top-8, 13,369,344
 bytes per FP4 expert): one step = route one token's fp32 logits (top-8,
 renormalised) + the SwiGLU MLP of the 8 selected experts and the shared
-expert on MXFP4 weights + the weighted combine to a bf16 output.  Each step
-uses fresh seeded logits and activations; every expert is resident in HBM.
+expert on MXFP4 weights + the weighted combine to a bf16 output, issued as one
+moe_layer_decode call (two kernels).  Each step uses fresh seeded logits and
+activations; every expert is resident in HBM.
 
 Prints one JSON line: tokens/s of the whole step, the achieved HBM bandwidth
 of the dominant kernel (gate/up GEMV) against the 8 TB/s peak, and the CPU
@@ -53,7 +54,7 @@ def parse():
 
 def kernel_hash() -> str:
     h = hashlib.sha256()
-    for f in ("decode_b1.hip", "common.h"):
+    for f in ("decode_b1.hip", "route_dev.h", "common.h"):
         with open(os.path.join(ROOT, "mxfp4_routed_expert_renorm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -165,8 +166,8 @@ def bench_decode_b1(args):
     print(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     def step(s):
-        lib.moe_route(lg_d[s:s + 1], k, ids_d[s], w_d[s])
-        lib.moe_expert_forward(layer, x_d[s:s + 1], T, k, ids_d[s], None, w_d[s], out_d[s:s + 1], ws)
+        # route + expert MLP + combine of one token: two kernel launches
+        lib.moe_layer_decode(layer, lg_d[s], x_d[s:s + 1], k, ids_d[s], w_d[s], out_d[s:s + 1], ws)
 
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
@@ -192,8 +193,14 @@ def bench_decode_b1(args):
     gu_avg_s = gu_ms / gu_n / 1e3
     k1 = k + 1
     # algorithmic bytes of one gate/up launch: w1 and w3 (codes + scales) of the
-    # 9 experts, the activation row, and the fp32 SwiGLU outputs
-    gu_bytes = k1 * 2 * (H * I // 2 + H * I // 32) + H * 2 + k1 * I * 4
+    # 9 experts, the logits row it routes, the activation row, and the bf16
+    # SwiGLU outputs
+    gu_bytes = k1 * 2 * (H * I // 2 + H * I // 32) + E * 4 + H * 2 + k1 * I * 2
+    dn_ms, dn_n = prof["down"]
+    # down + combine: w2 (codes + scales) of the 9 experts, the bf16 SwiGLU
+    # outputs, the weights and ids, the bf16 output row
+    dn_bytes = k1 * (H * I // 2 + H * I // 32) + k1 * I * 2 + k * 8 + H * 2
+    dn_achieved = dn_bytes / (dn_ms / dn_n / 1e3) / 1e9
     achieved = gu_bytes / gu_avg_s / 1e9
     khash = kernel_hash()
     traffic = traffic_from_profiles(khash)
@@ -221,11 +228,15 @@ def bench_decode_b1(args):
                    "expert_bytes": rec_bytes, "weight_bytes_per_step": step_bytes, "launch": args.mode},
         "step_hbm_GBps": round(step_bytes * value / 1e9, 1),
         "step_hbm_frac": round(step_bytes * value / 1e9 / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": "gateup_b1_kernel (batch-1 gate/up GEMV + SwiGLU)",
+        "roofline": {"bound": "hbm", "kernel": "gateup_b1_kernel (routing + batch-1 gate/up GEMV + SwiGLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 3),
                      "kernel_hash": khash},
+        "down_kernel": {"kernel": "down_combine_b1_kernel (W2 GEMV + weighted rank sum)",
+                        "achieved_GBps": round(dn_achieved, 1), "frac": round(dn_achieved / HBM_PEAK_GBPS, 4),
+                        "algorithmic_bytes_per_launch": dn_bytes,
+                        "avg_launch_us": round(dn_ms / dn_n * 1e3, 3)},
         "kernel_avg_us": per_kernel,
     }
     if not args.no_cpu_baseline:

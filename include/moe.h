@@ -152,6 +152,24 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype x
                               void* out, moe_dtype ot, void* workspace, size_t workspace_bytes,
                               moe_stream_t stream);
 
+/* One decode token through a fully resident layer: routing (as moe_route) and
+ * the expert MLP with the weighted combine (as moe_expert_forward with w), in
+ * one call ([P1] §What the expert cache actually does: router picks, then the
+ * expert GEMM over the slot buffers; [P2] §The number: at batch 1 the layer is
+ * a stream of expert bytes).  For bf16 activations and output with H, I in
+ * {2048, 4096} and k + has_shared <= 12, the routing runs inside the gate/up
+ * kernel, so the whole layer is two launches; otherwise moe_route then
+ * moe_expert_forward run.
+ *   layer: expert e in slot e (num_slots >= E), shared optional, no 2-bit copies
+ *   logits [E] fp32, x [1][H] in xt
+ *   ids [k] int32 out, w [k] fp32 out (rank order, as moe_route)
+ *   out [1][H] in ot
+ *   workspace: >= moe_expert_workspace_bytes(H, I, 1, k, has_shared), 256-byte aligned.
+ * Errors: MOE_ECACHE_SMALL when num_slots < E. */
+moe_status moe_layer_decode(const moe_layer* layer, const float* logits, int E, const void* x, moe_dtype xt,
+                            int k, int32_t* ids, float* w, void* out, moe_dtype ot, void* workspace,
+                            size_t workspace_bytes, moe_stream_t stream);
+
 /* Weighted combine ([P1] §What the expert cache actually does: the expert GEMM
  * takes topk_weights; [P2] §Not all six experts matter equally: survivors
  * renormalised):  out[t] = sum_{r < k, prec[t][r] >= 0} w[t][r] * y[t][r]

@@ -64,6 +64,8 @@ _SIGS = {
     "moe_expert_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "moe_expert_forward": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
+    "moe_layer_decode": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_void_p, c_int, c_int, c_void_p,
+                                 c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "moe_combine": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p]),
     "moe_debug_dequant": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
     "moe_quant_mxfp8": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]),
@@ -182,6 +184,16 @@ def moe_expert_forward(layer: moe_layer, x, T, k, slot_ids, prec, w, out, worksp
                                    _p(out), ot, _p(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream))
     _check("moe_expert_forward", st)
+    return out
+
+
+def moe_layer_decode(layer: moe_layer, logits, x, k, ids, w, out, workspace, stream=None):
+    """One token: route logits [E] (or [1, E]) and run the resident layer; ids/w [k] out."""
+    E = logits.shape[-1]
+    st = load().moe_layer_decode(ctypes.byref(layer), _p(logits), E, _p(x), _dt(x), k, _p(ids), _p(w), _p(out),
+                                 _dt(out), _p(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    _check("moe_layer_decode", st)
     return out
 
 

@@ -44,9 +44,10 @@ size_t prefill_workspace_bytes(int H, int I, int T, int k, int has_shared);
 moe_status launch_quant_mxfp8(const void* x, long rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s);
 moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int k, const int32_t* ids, const float* w,
                           void* out, void* workspace, hipStream_t s);
-bool b1_path_ok(int H, int I, int K1, bool xbf16);
-moe_status launch_b1(const moe_layer* L, const void* x, moe_dtype xt, int k, const int32_t* slot_ids,
-                     const int8_t* prec, const float* w, void* h, void* out, moe_dtype ot, hipStream_t s);
+bool b1_path_ok(int H, int I, int K1, bool xbf16, bool obf16);
+bool b1_route_ok(int E, int num_slots);
+moe_status launch_b1(const moe_layer* L, const float* logits, int E, const void* x, int k, int32_t* slot_ids,
+                     const int8_t* prec, float* w, uint16_t* h, void* out, hipStream_t s);
 size_t decode_plan_ints(int P);
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -154,12 +155,41 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype x
   int32_t* plan = (int32_t*)(ws + align256(P * layer->I * 4) + align256(P * layer->H * 4));
   float* yout = w ? y : (float*)out;
   hipStream_t s = (hipStream_t)stream;
-  if (T == 1 && w && b1_path_ok(layer->H, layer->I, K1, xt == MOE_BF16))
-    return launch_b1(layer, x, xt, k, slot_ids, prec, w, h, out, ot, s);
+  if (T == 1 && w && b1_path_ok(layer->H, layer->I, K1, xt == MOE_BF16, ot == MOE_BF16))  // reads slot_ids and w only
+    return launch_b1(layer, nullptr, 0, x, k, const_cast<int32_t*>(slot_ids), prec, const_cast<float*>(w),
+                     (uint16_t*)h, out, s);
   st = launch_expert_decode(layer, x, xt, T, k, slot_ids, prec, h, yout, plan, s);
   if (st != MOE_OK) return st;
   if (w) return launch_combine(y, w, prec, T, k, layer->H, has_shared, out, ot, s);
   return MOE_OK;
+}
+
+moe_status moe_layer_decode(const moe_layer* layer, const float* logits, int E, const void* x, moe_dtype xt, int k,
+                            int32_t* ids, float* w, void* out, moe_dtype ot, void* workspace, size_t workspace_bytes,
+                            moe_stream_t stream) {
+  moe_status st = check_layer(layer, "moe_layer_decode");
+  if (st != MOE_OK) return st;
+  REQUIRE(E >= 1 && E <= 1024, MOE_ESHAPE, "moe_layer_decode: E=%d outside 1..1024", E);
+  REQUIRE(k >= 1 && k <= E && k <= 64, MOE_EINVAL, "moe_layer_decode: k=%d must satisfy 1 <= k <= min(E=%d, 64)", k,
+          E);
+  REQUIRE(layer->num_slots >= E, MOE_ECACHE_SMALL,
+          "moe_layer_decode: the layer must hold every expert (num_slots=%d < E=%d); use the slot cache instead",
+          layer->num_slots, E);
+  REQUIRE(xt == MOE_F32 || xt == MOE_BF16, MOE_EINVAL, "moe_layer_decode: bad activation dtype %d", (int)xt);
+  REQUIRE(ot == MOE_F32 || ot == MOE_BF16, MOE_EINVAL, "moe_layer_decode: bad output dtype %d", (int)ot);
+  REQUIRE(logits && x && ids && w && out && workspace, MOE_EINVAL, "moe_layer_decode: NULL pointer");
+  REQUIRE(aligned(x, 16) && aligned(out, 16) && aligned(workspace, 256), MOE_EINVAL,
+          "moe_layer_decode: x/out must be 16-byte and workspace 256-byte aligned");
+  const int has_shared = layer->shared ? 1 : 0;
+  const size_t need = moe_expert_workspace_bytes(layer->H, layer->I, 1, k, has_shared);
+  REQUIRE(workspace_bytes >= need, MOE_ENOMEM, "moe_layer_decode: workspace %zu bytes < %zu needed", workspace_bytes,
+          need);
+  hipStream_t s = (hipStream_t)stream;
+  if (b1_path_ok(layer->H, layer->I, k + has_shared, xt == MOE_BF16, ot == MOE_BF16) && b1_route_ok(E, layer->num_slots))
+    return launch_b1(layer, logits, E, x, k, ids, nullptr, w, (uint16_t*)workspace, out, s);
+  st = launch_route(logits, 1, E, k, ids, w, s);
+  if (st != MOE_OK) return st;
+  return moe_expert_forward(layer, x, xt, 1, k, ids, nullptr, w, out, ot, workspace, workspace_bytes, stream);
 }
 
 moe_status moe_combine(const float* y, const float* w, const int8_t* prec, int T, int k, int H, int has_shared,

@@ -107,6 +107,14 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t dw) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// the same convert with a block scale applied: bf16(E2M1 value * scale);
+// exact for a power-of-two scale (including 2^-127 and NaN, every E8M0 byte)
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2_scaled(uint32_t dw, float scale) {
+  v2bf r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, SEL);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), c, false);
 }

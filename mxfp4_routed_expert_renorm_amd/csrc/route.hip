@@ -1,16 +1,7 @@
-// Router: top-k selection with renormalised weights, and the small router
-// GEMV of the tiny configuration.
-//
-// Top-k follows "Running DeepSeek-V4-Flash across four free GPUs", §What the
-// expert cache actually does (the router picks top_k experts per token) and
-// "An elephant through a straw", §Not all six experts matter equally (weights
-// per token, renormalised).  One 64-lane wavefront owns one token: each lane
-// holds E/64 logits in registers, and k rounds of a wavefront argmax
-// (butterfly over (value, id) pairs, ties to the lower id) pick the experts
-// in rank order; the butterflies run on DPP lane moves over a packed 64-bit
-// (value, inverted id) key.  The renormalised softmax over the selected experts equals a
-// softmax over their logits alone, so the full-E denominator is never formed.
-#include "common.h"
+// Router kernels: top-k selection with renormalised weights (one wavefront
+// per token, see route_dev.h), and the small router GEMV of the tiny
+// configuration.
+#include "route_dev.h"
 
 namespace moe {
 
@@ -19,81 +10,18 @@ namespace {
 constexpr int kMaxE = 1024;
 constexpr int kMaxEPL = kMaxE / 64;  // logits per lane
 
-// Selection key of (logit v, expert e): the order-preserving unsigned image
-// of v in the high word (-0 folded onto +0, NaN onto -inf) and the inverted
-// id in the low word, so the largest key is the largest logit with ties to
-// the lower id.  Key 0 means "no candidate".
-__device__ __forceinline__ uint64_t sel_key(float v, int e) {
-  v = (v == v) ? v + 0.0f : -INFINITY;
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)hi << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
-}
-
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t hi = (uint32_t)(key >> 32);
-  return __uint_as_float((hi & 0x80000000u) ? (hi ^ 0x80000000u) : ~hi);
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
-  const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
-  const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
-  const bool take = (h2 > hi) || (h2 == hi && l2 > lo);
-  hi = take ? h2 : hi;
-  lo = take ? l2 : lo;
-}
-
-// maximum key over the wavefront, returned uniformly
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
-  uint32_t hi = (uint32_t)(key >> 32), lo = (uint32_t)key;
-  dpp_max_step<dpp::kQuadXor1, 0xF>(hi, lo);
-  dpp_max_step<dpp::kQuadXor2, 0xF>(hi, lo);
-  dpp_max_step<dpp::kRowHalfMirror, 0xF>(hi, lo);
-  dpp_max_step<dpp::kRowMirror, 0xF>(hi, lo);
-  dpp_max_step<dpp::kRowBcast15, 0xA>(hi, lo);
-  dpp_max_step<dpp::kRowBcast31, 0xC>(hi, lo);
-  const uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
-  const uint32_t l = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
-  return ((uint64_t)h << 32) | l;
-}
-
 template <int EPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                     int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wavefront exits together
-  const float* row = logits + (size_t)t * E;
-  uint64_t key[EPL];
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = (e < E) ? sel_key(row[e], e) : 0ull;
-  }
-  float my_v = -INFINITY;  // lane r keeps the r-th selected logit
-  int my_e = 0;
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0ull;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) best = key[j] > best ? key[j] : best;
-    best = wave_max_key(best);
-    const int be = (int)(0xffffffffu - (uint32_t)best);
-    // the owner retires the winner
-#pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (key[j] == best) key[j] = 0ull;
-    if (lane == r) {
-      my_v = key_value(best);
-      my_e = be;
-    }
-  }
-  const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
-  const float z = (lane < k) ? expf(my_v - vmax) : 0.0f;
-  const float s = wave_sum(z);
+  int e;
+  float wt;
+  route_wave<EPL>(logits + (size_t)t * E, E, k, &e, &wt);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_e;
-    w[(size_t)t * k + lane] = z / s;
+    ids[(size_t)t * k + lane] = e;
+    w[(size_t)t * k + lane] = wt;
   }
 }
 

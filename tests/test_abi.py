@@ -95,6 +95,26 @@ def test_expert_forward_validation(lib):
     assert st == 1 and "layer is NULL" in msg
 
 
+def test_layer_decode_validation(lib):
+    rb = lib.moe_fp4_expert_bytes(2048, 2048)
+    ws = lib.moe_expert_workspace_bytes(2048, 2048, 1, 8, 0)
+    wsp = ctypes.c_void_p(0x10000)
+    call = lambda layer, E=64, k=8, xt=1, wsb=ws: _status(
+        lib, "moe_layer_decode", ctypes.byref(layer), FAKE, E, FAKE, xt, k, FAKE, FAKE, FAKE, 1, wsp, wsb, None)
+    small = B.moe_layer(2048, 2048, 0x1000, rb, 32, None, 0, 0, None)
+    st, msg = call(small)
+    assert st == 3 and "num_slots=32 < E=64" in msg          # MOE_ECACHE_SMALL
+    full = B.moe_layer(2048, 2048, 0x1000, rb, 64, None, 0, 0, None)
+    st, msg = call(full, k=65)
+    assert st == 1 and "k=65" in msg
+    st, msg = call(full, E=2000)
+    assert st == 2 and "E=2000" in msg
+    st, msg = call(full, wsb=ws - 1)
+    assert st == 4 and "workspace" in msg
+    st, msg = call(full, xt=9)
+    assert st == 1 and "dtype" in msg
+
+
 def test_last_error_is_thread_local(lib):
     import threading
     _status(lib, "moe_route", FAKE, 1, 8, 9, FAKE, FAKE, None)

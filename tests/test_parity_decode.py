@@ -380,8 +380,9 @@ def test_combine_standalone(gpu_lib):
 
 @pytest.mark.parametrize("xbf16", [True, False])
 def test_layer_b1_fused_path_mixed_precision(gpu_lib, xbf16):
-    """Batch 1 at H = I = 2048 takes the fused streaming kernels; mix FP4,
-    2-bit copies and drops, with the shared expert."""
+    """Batch 1 at H = I = 2048: bf16 activations take the batch-1 streaming
+    kernels, fp32 the generic ones; mix FP4, 2-bit copies and drops, with the
+    shared expert."""
     torch = _torch()
     H, I, E, k, NI = 2048, 2048, 12, 6, 3
     seed = 31 + int(xbf16)
@@ -420,3 +421,81 @@ def test_layer_b1_fused_path_mixed_precision(gpu_lib, xbf16):
         err = rel_l2(got, ref)
         log(f"b1 fused path fp32: rel-L2 {err:.3e}")
         assert err <= TOL_F32_REL_L2
+
+
+# ------------------------------------------------------------ moe_layer_decode
+
+def _tiled_bank(seed, E, H, I, distinct=8):
+    """E resident experts built from `distinct` seeded records (expert e uses
+    record e % distinct): a full-size bank without generating E records."""
+    recs = W.fp4_bank(seed, W.S_BANK, distinct, H, I)
+    torch = _torch()
+    d = dev(recs)
+    bank = torch.cat([d] * ((E + distinct - 1) // distinct))[:E].contiguous()
+    return recs, bank
+
+
+def _layer_decode_case(gpu_lib, E, H, I, k, with_shared, seed, out_f32=False):
+    torch = _torch()
+    recs, bank = _tiled_bank(seed, E, H, I)
+    rb = recs.shape[1]
+    shared = W.fp4_record(seed, W.S_SHARED, 0, H, I) if with_shared else None
+    sh_dev = dev(shared) if with_shared else None
+    desc = gpu_lib.make_layer(H, I, fp4_base=bank, fp4_stride=rb, num_slots=E, shared=sh_dev)
+    lg = W.router_logits(seed, (W.S_LOGITS,), 1, E)
+    xb = W.bf16_normal(seed, (W.S_X,), (1, H))
+    x_dev = bf16_dev(xb)
+    odt = torch.float32 if out_f32 else torch.bfloat16
+    ws = torch.empty(gpu_lib.moe_expert_workspace_bytes(H, I, 1, k, with_shared), dtype=torch.uint8, device="cuda")
+    ids = torch.full((k,), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((k,), -7.0, dtype=torch.float32, device="cuda")
+    out = torch.empty((1, H), dtype=odt, device="cuda")
+    gpu_lib.moe_layer_decode(desc, dev(lg[0]), x_dev, k, ids, w, out, ws)
+    # the same token through the separate calls
+    ids2 = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    w2 = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    out2 = torch.empty((1, H), dtype=odt, device="cuda")
+    gpu_lib.moe_route(dev(lg), k, ids2, w2)
+    gpu_lib.moe_expert_forward(desc, x_dev, 1, k, ids2, None, w2, out2, ws)
+    torch.cuda.synchronize()
+    oids, ow = O.route(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), oids[0])
+    assert np.array_equal(ids2.cpu().numpy()[0], oids[0])
+    assert np.array_equal(w.cpu().numpy(), w2.cpu().numpy()[0])          # one routing code path
+    assert np.max(np.abs(w.cpu().numpy() - ow[0])) <= 1e-6
+    # routing inside the gate/up kernel changes nothing downstream
+    assert torch.equal(out, out2)
+    ref = O.layer_forward(O.bf16_bits_to_f64(xb), oids, ow, lambda e: recs[int(e) % recs.shape[0]], H, I,
+                          shared_rec=shared)
+    got = to_f64(out)
+    if out_f32:
+        err = rel_l2(got, ref)
+        log(f"layer_decode E={E} H={H} I={I} k={k} shared={with_shared}: rel-L2 {err:.3e}")
+        assert err <= TOL_F32_REL_L2
+    else:
+        err = max_rel(got, ref)
+        log(f"layer_decode E={E} H={H} I={I} k={k} shared={with_shared}: max-rel {err:.3e}")
+        assert err <= TOL_BF16_MAX_REL
+
+
+def test_layer_decode_full_shape(gpu_lib):
+    """The decode workload's shape (256 experts + shared, H 4096, I 2048,
+    top-8) through the single-call path, routed inside the gate/up kernel."""
+    _layer_decode_case(gpu_lib, 256, 4096, 2048, 8, True, seed=81)
+
+
+@pytest.mark.parametrize("E,k,with_shared,out_f32", [
+    (100, 8, True, False),     # E not a multiple of 64: clamped logit loads
+    (300, 6, False, False),    # E > 256: 16 logits per lane, no shared expert
+    (64, 8, True, True),       # fp32 output: moe_route + the generic kernels
+    (64, 1, True, False),      # k = 1
+    (64, 11, True, False),     # 12 groups: the largest batch of the down kernel
+])
+def test_layer_decode_shapes(gpu_lib, E, k, with_shared, out_f32):
+    _layer_decode_case(gpu_lib, E, 2048, 2048, k, with_shared, seed=90 + E + k, out_f32=out_f32)
+
+
+def test_layer_decode_generic_shape(gpu_lib):
+    """A shape outside the batch-1 kernels (H 512) runs moe_route then the
+    generic expert kernels; same contract."""
+    _layer_decode_case(gpu_lib, 40, 512, 256, 4, True, seed=95)
