@@ -160,7 +160,7 @@ def bench_decode_b1(args):
     ids_d = torch.empty((nsteps, k), dtype=torch.int32, device=dev)
     w_d = torch.empty((nsteps, k), dtype=torch.float32, device=dev)
     out_d = torch.empty((nsteps, H), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(lib.moe_expert_workspace_bytes(H, I, T, k, True), dtype=torch.uint8, device=dev)
+    ws = lib.expert_workspace(H, I, T, k, True, device=dev)
     layer = lib.make_layer(H, I, fp4_base=bank, fp4_stride=rec_bytes, num_slots=E, shared=shared)
     torch.cuda.synchronize()
     print(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
@@ -189,23 +189,20 @@ def bench_decode_b1(args):
     for s in range(Wm, nsteps):
         step(s)
     prof = lib.moe_profile_end()
-    gu_ms, gu_n = prof["gateup"]
-    gu_avg_s = gu_ms / gu_n / 1e3
     k1 = k + 1
-    # algorithmic bytes of one gate/up launch: w1 and w3 (codes + scales) of the
-    # 9 experts, the logits row it routes, the activation row, and the bf16
-    # SwiGLU outputs
-    gu_bytes = k1 * 2 * (H * I // 2 + H * I // 32) + E * 4 + H * 2 + k1 * I * 2
-    dn_ms, dn_n = prof["down"]
-    # down + combine: w2 (codes + scales) of the 9 experts, the bf16 SwiGLU
-    # outputs, the weights and ids, the bf16 output row
-    dn_bytes = k1 * (H * I // 2 + H * I // 32) + k1 * I * 2 + k * 8 + H * 2
-    dn_achieved = dn_bytes / (dn_ms / dn_n / 1e3) / 1e9
-    achieved = gu_bytes / gu_avg_s / 1e9
+    # algorithmic bytes of one step: the 9 experts' records (codes + scales of
+    # w1, w3, w2), the logits row, the activation row, the bf16 SwiGLU outputs
+    # written and read back, the ids and weights, the bf16 output row
+    step_alg_bytes = k1 * rec_bytes + E * 4 + H * 2 + 2 * k1 * I * 2 + k * 8 + H * 2
     khash = kernel_hash()
     traffic = traffic_from_profiles(khash)
     per_kernel = {n: round(v[0] / v[1] * 1e3, 3) for n, v in prof.items()}
     print(f"[bench] kernel averages (us): {per_kernel}", file=sys.stderr, flush=True)
+    ms, n = prof["gateup"]      # the dominant kernel of the two launches
+    dom_kernel = "gateup_b1_kernel (routing + batch-1 gate/up GEMV + SwiGLU)"
+    dom_bytes = k1 * 2 * (H * I // 2 + H * I // 32) + E * 4 + H * 2 + k1 * I * 2
+    dom_avg_s = ms / n / 1e3
+    achieved = dom_bytes / dom_avg_s / 1e9
 
     tokens = K * T
     value = tokens / elapsed
@@ -228,15 +225,11 @@ def bench_decode_b1(args):
                    "expert_bytes": rec_bytes, "weight_bytes_per_step": step_bytes, "launch": args.mode},
         "step_hbm_GBps": round(step_bytes * value / 1e9, 1),
         "step_hbm_frac": round(step_bytes * value / 1e9 / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": "gateup_b1_kernel (routing + batch-1 gate/up GEMV + SwiGLU)",
+        "roofline": {"bound": "hbm", "kernel": dom_kernel,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 3),
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_avg_s * 1e6, 3),
                      "kernel_hash": khash},
-        "down_kernel": {"kernel": "down_combine_b1_kernel (W2 GEMV + weighted rank sum)",
-                        "achieved_GBps": round(dn_achieved, 1), "frac": round(dn_achieved / HBM_PEAK_GBPS, 4),
-                        "algorithmic_bytes_per_launch": dn_bytes,
-                        "avg_launch_us": round(dn_ms / dn_n * 1e3, 3)},
         "kernel_avg_us": per_kernel,
     }
     if not args.no_cpu_baseline:
@@ -302,7 +295,7 @@ def bench_decode_b64(args):
     ids_d = torch.empty((nsteps, T, k), dtype=torch.int32, device=dev)
     w_d = torch.empty((nsteps, T, k), dtype=torch.float32, device=dev)
     out_d = torch.empty((nsteps, T, H), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(lib.moe_expert_workspace_bytes(H, I, T, k, True), dtype=torch.uint8, device=dev)
+    ws = lib.expert_workspace(H, I, T, k, True, device=dev)
     layer = lib.make_layer(H, I, fp4_base=bank, fp4_stride=rec_bytes, num_slots=E, shared=shared)
     torch.cuda.synchronize()
 
@@ -436,7 +429,7 @@ def bench_slotcache(args):
     w = torch.empty((1, k), dtype=torch.float32, device=dev)
     prec = torch.empty((1, k), dtype=torch.int8, device=dev)
     out_d = torch.empty((T * L, H), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(lib.moe_expert_workspace_bytes(H, I, 1, k, False), dtype=torch.uint8, device=dev)
+    ws = lib.expert_workspace(H, I, 1, k, False, device=dev)
     copy_stream = torch.cuda.Stream()
     # host-link peak for this copy pattern: 64 records back to back from the pinned bank
     src = torch.from_numpy(fp4_host.array[:64 * rb4])

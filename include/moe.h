@@ -129,8 +129,8 @@ moe_status moe_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int
 
 /* ------------------------------------------------------------ expert MLP */
 
-/* Workspace bytes moe_expert_forward needs for T tokens, top-k, with or without
- * the shared expert. */
+/* Workspace bytes moe_expert_forward and moe_layer_decode need for T tokens,
+ * top-k, with or without the shared expert. */
 size_t moe_expert_workspace_bytes(int H, int I, int T, int k, int has_shared);
 
 /* SwiGLU expert MLP for every selected (token, rank) and the shared expert:

@@ -148,6 +148,12 @@ def moe_expert_workspace_bytes(H, I, T, k, has_shared) -> int:
     return load().moe_expert_workspace_bytes(H, I, T, k, int(bool(has_shared)))
 
 
+def expert_workspace(H, I, T, k, has_shared, device="cuda"):
+    """A device workspace for moe_expert_forward / moe_layer_decode."""
+    import torch
+    return torch.empty(moe_expert_workspace_bytes(H, I, T, k, has_shared), dtype=torch.uint8, device=device)
+
+
 # -------------------------------------------------------------------- routing
 
 def moe_router_logits(x, w_router, logits, stream=None):
@@ -174,8 +180,12 @@ def moe_group(keys, nkeys, counts, offsets, perm, stream=None):
 
 def make_layer(H, I, fp4_base=None, fp4_stride=0, num_slots=0, int2_base=None, int2_stride=0, num_int2=0,
                shared=None) -> moe_layer:
-    """A moe_layer descriptor from device tensors (uint8 records)."""
-    return moe_layer(H, I, _p(fp4_base), fp4_stride, num_slots, _p(int2_base), int2_stride, num_int2, _p(shared))
+    """A moe_layer descriptor from device tensors (uint8 records).  The
+    descriptor holds raw device pointers, so it keeps references to the tensors:
+    they cannot be freed (and their memory unmapped) while it is alive."""
+    lay = moe_layer(H, I, _p(fp4_base), fp4_stride, num_slots, _p(int2_base), int2_stride, num_int2, _p(shared))
+    lay._tensors = (fp4_base, int2_base, shared)
+    return lay
 
 
 def moe_expert_forward(layer: moe_layer, x, T, k, slot_ids, prec, w, out, workspace, stream=None):
@@ -265,7 +275,7 @@ def _addr(x):
 
 class Cache:
     """moe_cache handle.  Host banks and device buffers are supplied by the
-    caller and must outlive the handle."""
+    caller; the handle keeps references to them, so they outlive it."""
 
     def __init__(self, L, E, H, I, num_slots, k, a, b, max_tokens=1, fp4_host=None, int2_host=None,
                  fp4_arena=None, int2_staging=None):
@@ -274,6 +284,7 @@ class Cache:
         h = c_void_p()
         _check("moe_cache_create", load().moe_cache_create(ctypes.byref(d), ctypes.byref(h)))
         self.h, self.L, self.E, self.k = h, L, E, k
+        self._buffers = (fp4_host, int2_host, fp4_arena, int2_staging)
 
     def destroy(self):
         if self.h:
@@ -315,6 +326,7 @@ class Cache:
     def layer(self) -> moe_layer:
         lay = moe_layer()
         _check("moe_cache_layer", load().moe_cache_layer(self.h, ctypes.byref(lay)))
+        lay._tensors = self._buffers
         return lay
 
 

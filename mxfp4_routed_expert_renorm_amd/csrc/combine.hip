@@ -67,3 +67,4 @@ moe_status launch_combine(const float* y, const float* w, const int8_t* prec, in
 }
 
 }  // namespace moe
+

@@ -212,8 +212,7 @@ class Layer:
 
     def forward(self, x_dev, T, k, slots, prec, w, out):
         torch = _torch()
-        nb = self.lib.moe_expert_workspace_bytes(self.H, self.I, T, k, self.shared is not None)
-        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+        ws = self.lib.expert_workspace(self.H, self.I, T, k, self.shared is not None)
         self.lib.moe_expert_forward(self.desc, x_dev, T, k, slots, prec, w, out, ws)
         return out
 
@@ -446,7 +445,7 @@ def _layer_decode_case(gpu_lib, E, H, I, k, with_shared, seed, out_f32=False):
     xb = W.bf16_normal(seed, (W.S_X,), (1, H))
     x_dev = bf16_dev(xb)
     odt = torch.float32 if out_f32 else torch.bfloat16
-    ws = torch.empty(gpu_lib.moe_expert_workspace_bytes(H, I, 1, k, with_shared), dtype=torch.uint8, device="cuda")
+    ws = gpu_lib.expert_workspace(H, I, 1, k, with_shared)
     ids = torch.full((k,), -7, dtype=torch.int32, device="cuda")
     w = torch.full((k,), -7.0, dtype=torch.float32, device="cuda")
     out = torch.empty((1, H), dtype=odt, device="cuda")
@@ -499,3 +498,41 @@ def test_layer_decode_generic_shape(gpu_lib):
     """A shape outside the batch-1 kernels (H 512) runs moe_route then the
     generic expert kernels; same contract."""
     _layer_decode_case(gpu_lib, 40, 512, 256, 4, True, seed=95)
+
+
+
+def test_layer_decode_graph_replays(gpu_lib):
+    """moe_layer_decode captured in a HIP graph and replayed, with eager calls
+    between the replays: every replay equals the eager result."""
+    torch = _torch()
+    E, H, I, k, steps, seed = 40, 2048, 2048, 6, 6, 98
+    recs, bank = _tiled_bank(seed, E, H, I)
+    shared = dev(W.fp4_record(seed, W.S_SHARED, 0, H, I))
+    desc = gpu_lib.make_layer(H, I, fp4_base=bank, fp4_stride=recs.shape[1], num_slots=E, shared=shared)
+    ws = gpu_lib.expert_workspace(H, I, 1, k, True)
+    lg = dev(W.router_logits(seed, (W.S_LOGITS,), steps, E))
+    xs = bf16_dev(W.bf16_normal(seed, (W.S_X,), (steps, H)))
+    ids = torch.empty((steps, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((steps, k), dtype=torch.float32, device="cuda")
+    ref = torch.empty((steps, H), dtype=torch.bfloat16, device="cuda")
+    for s in range(steps):
+        gpu_lib.moe_layer_decode(desc, lg[s], xs[s:s + 1], k, ids[s], w[s], ref[s:s + 1], ws)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(ref)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for s in range(steps):
+                gpu_lib.moe_layer_decode(desc, lg[s], xs[s:s + 1], k, ids[s], w[s], out[s:s + 1], ws)
+    torch.cuda.current_stream().wait_stream(stream)
+    scratch = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
+        gpu_lib.moe_layer_decode(desc, lg[rep], xs[rep:rep + 1], k, ids[rep], w[rep], scratch, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(scratch, ref[rep:rep + 1]), rep

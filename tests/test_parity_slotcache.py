@@ -47,7 +47,7 @@ def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1):
         w = torch.empty((1, k), dtype=torch.float32, device="cuda")
         prec = torch.empty((1, k), dtype=torch.int8, device="cuda")
         out = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(lib.moe_expert_workspace_bytes(H, I, 1, k, False), dtype=torch.uint8, device="cuda")
+        ws = lib.expert_workspace(H, I, 1, k, False)
         checked = 0
         for t in range(T):
             for l in range(L):
