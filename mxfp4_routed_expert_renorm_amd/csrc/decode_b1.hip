@@ -7,13 +7,14 @@
 // a few tens of KiB per wavefront, so each kernel requests everything it
 // will read up front and then consumes it in arrival order:
 //
-// gateup_b1_kernel: every wavefront owns NR consecutive rows of the
-//   flattened (FP4 expert, gate/up row) space.  It issues the activation
-//   loads, then (optionally) routes the token itself from the logits row,
-//   stages the activation in LDS (once per workgroup), then issues all NR
-//   rows of W1 and W3 (codes and E8M0 scales) at once.  Each row's gate and
-//   up sums are reduced with DPP lane moves and lane 63 writes
-//   silu(g) * u in bf16.  The shared expert comes first in the row order.
+// gateup_b1_kernel: wavefront i owns gate/up row i of every expert of the
+//   token (the shared expert first, then the FP4 ranks).  It requests the
+//   activation, then the routing inputs, then the shared expert's row, which
+//   needs no routing; routes the token itself from the logits row (or reads
+//   ids); stages the activation in LDS (once per workgroup); then requests
+//   row i of every routed expert at once.  Each row's gate and up sums are
+//   reduced with DPP lane moves, and the SwiGLU of the row for all experts
+//   runs in one lane-parallel pass (lane g takes expert g).
 //
 // down_combine_b1_kernel: a wavefront owns one output row for every active
 //   expert at once, so the weighted combine is fused: each lane accumulates
@@ -29,15 +30,6 @@
 #include "common.h"
 #include "route_dev.h"
 
-#ifndef MOE_B1_GU_ROWS
-#define MOE_B1_GU_ROWS 6
-#endif
-#ifndef MOE_B1_GU_OCC
-#define MOE_B1_GU_OCC 3
-#endif
-#ifndef MOE_B1_DN_ORDER
-#define MOE_B1_DN_ORDER 1
-#endif
 
 namespace moe {
 
@@ -162,98 +154,87 @@ struct GURow {
   uint32_t s1[CPL], s3[CPL];
 };
 
-template <int CPL, int NR, int EPL>
-__global__ __launch_bounds__(256, MOE_B1_GU_OCC) void gateup_b1_kernel(B1Args a) {
-  static_assert(NR >= 1 && NR <= 64, "rows per wavefront");
+template <int CPL, int NB, int EPL, bool SH>
+__global__ __launch_bounds__(256, 2) void gateup_b1_kernel(B1Args a) {
   constexpr int XBYTES = CPL * 64 * 32 * 2;  // H bf16 activations
-  constexpr int XV = XBYTES / 16 / 256;      // 16-byte pieces per thread
-  static_assert(XV == 1 || XV == 2, "H is 2048 or 4096");
+  static_assert(CPL == 1 || CPL == 2, "H is 2048 or 4096");
+  static_assert(NB >= 1 + (SH ? 1 : 0), "batch holds the shared expert and at least one rank");
   __shared__ __align__(16) uint8_t xs[XBYTES];
   __shared__ float stab[256];  // E8M0 byte -> scale
   const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // < I: the grid tiles I
   const int I = a.I, k = a.k;
-
-  // activations first in this wavefront's memory queue (named registers, not
-  // an array, so they stay in VGPRs)
-  const uint4 xv0 = ((const uint4*)a.x)[threadIdx.x];
-  const uint4 xv1 = XV == 2 ? ((const uint4*)a.x)[threadIdx.x + 256] : make_uint4(0u, 0u, 0u, 0u);
-  stab[threadIdx.x] = e8m0_to_f32(threadIdx.x);
-
-  // lane r < k: slot and precision of rank r (routed here when logits are given)
-  int my_slot = -1, my_prec = -1;
-  if constexpr (EPL > 0) {
-    float my_w;
-    route_wave<EPL>(a.logits, a.E, k, &my_slot, &my_w);
-    my_prec = 0;
-    if (gw == 0 && lane < k) {
-      a.slot_ids[lane] = my_slot;
-      a.w[lane] = my_w;
+  const size_t rowb4 = (size_t)a.H / 2, rows4 = (size_t)a.H / 32;
+  const RecordLayout L = record_layout(a.H, I, 4);
+  GURow<CPL> sl[NB];
+  auto issue = [&](GURow<CPL>& s, const uint8_t* rec) {
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const size_t c = (size_t)(q * 64 + lane);
+      s.c1[q] = ld_stream16(rec + L.w1c + (size_t)row * rowb4 + c * 16);
+      s.c3[q] = ld_stream16(rec + L.w3c + (size_t)row * rowb4 + c * 16);
+      s.s1[q] = rec[L.w1s + (size_t)row * rows4 + c];
+      s.s3[q] = rec[L.w3s + (size_t)row * rows4 + c];
     }
+  };
+
+  // 1. the activation, then the routing inputs, then the shared expert's
+  // row (it needs no routing): the routing inputs return ahead of the
+  // weights, and the weight stream starts before the routing is done
+  const uint4 xv0 = ((const uint4*)a.x)[threadIdx.x];
+  const uint4 xv1 = CPL == 2 ? ((const uint4*)a.x)[threadIdx.x + 256] : make_uint4(0u, 0u, 0u, 0u);
+  int my_slot = -1, my_prec = -1;
+  float lv[EPL > 0 ? EPL : 1];
+  if constexpr (EPL > 0) {
+    route_load<EPL>(a.logits, a.E, lv);
   } else {
     if (lane < k) {
       my_slot = a.slot_ids[lane];
       my_prec = a.prec ? (int)a.prec[lane] : 0;
     }
   }
-  // FP4 groups in row order: the shared expert, then the FP4 ranks
-  const bool fp4 = lane < k && my_prec == 0 && my_slot >= 0 && my_slot < a.num_slots;
-  const uint64_t m = __ballot(fp4);
-  const int nsh = a.shared ? 1 : 0;
-  const int total = (nsh + __popcll(m)) * I;
-  const int j0 = gw * NR;
-  const bool live = j0 < total;
+  __builtin_amdgcn_sched_barrier(0);  // the routing inputs stay ahead of the shared row in the queue
+  if constexpr (SH) issue(sl[0], a.shared);
+  stab[threadIdx.x] = e8m0_to_f32(threadIdx.x);
 
-  // the activation has long arrived (the routing inputs came after it); it
-  // goes to LDS before the weight loads, so no wait below covers them, and
-  // the barrier comes first too, so loads and their consumers share one block
-  ((uint4*)xs)[threadIdx.x] = xv0;
-  if (XV == 2) ((uint4*)xs)[threadIdx.x + 256] = xv1;
-  __syncthreads();
-  if (!live) return;
-
-  // the NR rows span at most two groups: g0 (from row r0) and g0 + 1
-  const int g0 = j0 / I, r0 = j0 - g0 * I, last = total - 1;
-  auto group = [&](int gi, int* kx) -> const uint8_t* {
-    if (gi < nsh) {
-      *kx = k;
-      return a.shared;
-    }
-    const int r = nth_set_bit(m, gi - nsh);
-    *kx = r;
-    return a.fp4_base + (size_t)__builtin_amdgcn_readlane(my_slot, r) * a.fp4_stride;
-  };
-  int kx0, kx1 = k;
-  const uint8_t* rec0 = group(g0, &kx0);
-  const uint8_t* rec1 = (j0 + NR - 1 >= (g0 + 1) * I && last >= (g0 + 1) * I) ? group(g0 + 1, &kx1) : rec0;
-
-  const size_t rowb4 = (size_t)a.H / 2, rows = (size_t)a.H / 32;
-  const RecordLayout L = record_layout(a.H, I, 4);
-  GURow<CPL> sl[NR];
-#pragma unroll
-  for (int u = 0; u < NR; ++u) {
-    const int j = min(j0 + u, last);  // rows past the end repeat the last (not stored)
-    const bool second = j - g0 * I >= I;
-    const int row = second ? j - g0 * I - I : j - g0 * I;
-    const uint8_t* rec = second ? rec1 : rec0;
-#pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-      const size_t c = (size_t)(q * 64 + lane);
-      sl[u].c1[q] = ld_stream16(rec + L.w1c + (size_t)row * rowb4 + c * 16);
-      sl[u].c3[q] = ld_stream16(rec + L.w3c + (size_t)row * rowb4 + c * 16);
-      sl[u].s1[q] = rec[L.w1s + (size_t)row * rows + c];
-      sl[u].s3[q] = rec[L.w3s + (size_t)row * rows + c];
+  // 2. the token's FP4 ranks (routed here when logits are given)
+  if constexpr (EPL > 0) {
+    float my_w;
+    route_select<EPL>(lv, a.E, k, &my_slot, &my_w);
+    my_prec = 0;
+    if (row == 0 && lane < k) {
+      a.slot_ids[lane] = my_slot;
+      a.w[lane] = my_w;
     }
   }
+  const bool fp4 = lane < k && my_prec == 0 && my_slot >= 0 && my_slot < a.num_slots;
+  const uint64_t m = __ballot(fp4);
+  const int nf = __popcll(m);
+  constexpr int S0 = SH ? 1 : 0;
+  const int nact = S0 + nf;
+  ((uint4*)xs)[threadIdx.x] = xv0;
+  if (CPL == 2) ((uint4*)xs)[threadIdx.x + 256] = xv1;
+  __syncthreads();
+  if (nact == 0) return;
 
-  // every load above is issued before any row is consumed
-  __builtin_amdgcn_sched_barrier(0);
-
-  // rows in arrival order; the block scale rides in the convert, so each row
-  // is one accumulation chain per matrix (two for instruction overlap)
-  float gsum[NR], usum[NR];
+  // 3. this row of every FP4 rank (batch slots past the active groups repeat
+  // the last one and are not stored)
+  int kx[NB];
+  if constexpr (SH) kx[0] = k;
 #pragma unroll
-  for (int u = 0; u < NR; ++u) {
+  for (int u = S0; u < NB; ++u) {
+    const int r = nf > 0 ? nth_set_bit(m, min(u - S0, nf - 1)) : -1;
+    kx[u] = r;
+    const uint8_t* rec = r >= 0 ? a.fp4_base + (size_t)__builtin_amdgcn_readlane(my_slot, r) * a.fp4_stride : a.shared;
+    issue(sl[u], rec);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load above is out before the first row is consumed
+
+  // 4. rows in arrival order; the block scale rides in the convert, so each
+  // row is one accumulation chain per matrix (two for instruction overlap)
+  float gsum[NB], usum[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
     float g0a = 0.0f, g1a = 0.0f, u0a = 0.0f, u1a = 0.0f;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
@@ -265,21 +246,18 @@ __global__ __launch_bounds__(256, MOE_B1_GU_OCC) void gateup_b1_kernel(B1Args a)
     gsum[u] = wave_sum_to_lane63(g0a + g1a);
     usum[u] = wave_sum_to_lane63(u0a + u1a);
   }
-  // SwiGLU of all NR rows at once: lane t < NR takes row t
+  // 5. SwiGLU of the row for every group at once: lane u takes group u
   float gv = 0.0f, uv = 0.0f;
+  int kv = 0;
 #pragma unroll
-  for (int u = 0; u < NR; ++u) {
+  for (int u = 0; u < NB; ++u) {
     const float gu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gsum[u]), 63));
     const float uu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(usum[u]), 63));
     gv = lane == u ? gu : gv;
     uv = lane == u ? uu : uv;
+    kv = lane == u ? kx[u] : kv;
   }
-  const int rl = r0 + lane;
-  if (lane < NR && j0 + lane <= last) {
-    const bool second = rl >= I;
-    const size_t hrow = second ? (size_t)kx1 * I + (rl - I) : (size_t)kx0 * I + rl;
-    a.h[hrow] = f32_to_bf16(silu_mul_b1(gv, uv));
-  }
+  if (lane < nact) a.h[(size_t)kv * I + row] = f32_to_bf16(silu_mul_b1(gv, uv));
 }
 
 // 2-bit groups of the batch-1 gate/up (the slot cache's fallback copies):
@@ -324,119 +302,123 @@ struct DNRow {
   uint32_t s[CPL];
 };
 
-template <int CPL, int NB, bool HAS2>
+template <int CPL, int NB, bool HAS2, bool SH>
 __global__ __launch_bounds__(256) void down_combine_b1_kernel(B1Args a) {
-  extern __shared__ __align__(16) uint8_t lds[];  // [NB][I] bf16 SwiGLU outputs
+  extern __shared__ __align__(16) uint8_t lds[];  // [NB][I] bf16: the SwiGLU outputs of group g at slot g
   __shared__ float stab[256];                      // E8M0 byte -> scale
+  constexpr int S0 = SH ? 1 : 0;
+  constexpr int NR = NB - S0;  // rank slots
   const int tid = threadIdx.x, lane = tid & 63;
-  stab[tid] = e8m0_to_f32(tid);
   const int orow = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);  // < H: the grid tiles H exactly
-  const int I = a.I;
-
-  // active groups in rank order, shared last (lane g < K1 holds group g);
-  // the three small loads go out together
-  int pr = -1, slot = 0;
-  float wg = 0.0f;
-  if (lane < a.k) {
-    const int p = a.prec ? (int)a.prec[lane] : 0;
-    slot = a.slot_ids[lane];
-    wg = a.w[lane];
-    pr = (p == 0 && slot >= 0 && slot < a.num_slots) ? 0 : (p == 1 && slot >= 0 && slot < a.num_int2) ? 1 : -1;
-  } else if (lane == a.k && a.shared) {
-    pr = 0;
-    wg = 1.0f;
-  }
-  const uint64_t m = __ballot(lane < a.K1 && pr >= 0);
-  const int nact = __popcll(m);
-  if (nact == 0) {  // every expert dropped and no shared expert
-    if (lane == 63) ((uint16_t*)a.out)[orow] = 0;
-    return;
-  }
-  int gi[NB], pi[NB];
-  const uint8_t* ri[NB];
-  float wi[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int g = nth_set_bit(m, min(i, nact - 1));
-    gi[i] = g;
-    pi[i] = __builtin_amdgcn_readlane(pr, g);
-    const size_t sl_g = (size_t)__builtin_amdgcn_readlane(slot, g);
-    // pointers rebuilt from the kernel arguments stay in the global address space
-    ri[i] = g == a.k ? a.shared : pi[i] == 0 ? a.fp4_base + sl_g * a.fp4_stride : a.int2_base + sl_g * a.int2_stride;
-    wi[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wg), g));
-  }
-
-  // The SwiGLU outputs of the batch, staged in LDS, and this wavefront's W2
-  // row of every active group, all in flight before the first wait.
+  const int I = a.I, k = a.k;
   const size_t rowb4 = (size_t)I / 2, rowb2 = (size_t)I / 4, rows = (size_t)I / 32;
   const RecordLayout L4 = record_layout(a.H, I, 4), L2 = record_layout(a.H, I, 2);
-  DNRow<CPL> sl[NB];
-  auto issue_w2 = [&](int i) {
-    if (!HAS2 || pi[i] == 0) {
+  auto issue4 = [&](DNRow<CPL>& d, const uint8_t* rec) {
 #pragma unroll
-      for (int q = 0; q < CPL; ++q) {
-        const size_t c = (size_t)(q * 64 + lane);
-        sl[i].c[q] = ld_stream16(ri[i] + L4.w2c + (size_t)orow * rowb4 + c * 16);
-        sl[i].s[q] = ri[i][L4.w2s + (size_t)orow * rows + c];
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < CPL; ++q) {
-        const size_t c = (size_t)(q * 64 + lane);
-        const uint2 v = ld_stream8(ri[i] + L2.w2c + (size_t)orow * rowb2 + c * 8);
-        sl[i].c[q] = make_uint4(v.x, v.y, 0u, 0u);
-        sl[i].s[q] = ri[i][L2.w2s + (size_t)orow * rows + c];
-      }
+    for (int q = 0; q < CPL; ++q) {
+      const size_t c = (size_t)(q * 64 + lane);
+      d.c[q] = ld_stream16(rec + L4.w2c + (size_t)orow * rowb4 + c * 16);
+      d.s[q] = rec[L4.w2s + (size_t)orow * rows + c];
     }
   };
-  auto stage_h = [&]() {  // I * 2 / 16 / 256 = CPL pieces per thread and group
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const uint4* src = (const uint4*)(a.h + (size_t)gi[i] * I);
-      uint4* dst = (uint4*)(lds + (size_t)i * I * 2);
-      dst[tid] = src[tid];
-      if (CPL == 2) dst[tid + 256] = src[tid + 256];
-    }
-  };
-#if MOE_B1_DN_ORDER == 0
-  // h first: its loads come back from L2/MALL long before the weights would
-  stage_h();
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NB; ++i) issue_w2(i);
-#else
-  // the first half of the weights, then h (whose wait covers only that
-  // half), then the rest
-  constexpr int NH = (NB + 1) / 2;
-#pragma unroll
-  for (int i = 0; i < NH; ++i) issue_w2(i);
-  stage_h();
-#pragma unroll
-  for (int i = NH; i < NB; ++i) issue_w2(i);
-  __syncthreads();
-#endif
 
-  // 4. consume in rank order.  Straight-line code: a batch slot past the
-  // active groups (a repeat of the last one) is computed and then selected
-  // away, so no load is sunk into a branch below the barrier.
-  int nact_v;  // nact in a vector register: the selects stay selects
-  asm volatile("v_mov_b32 %0, %1" : "=v"(nact_v) : "s"(nact));
-  float acc = 0.0f;
+  // 1. the ranks' ids, precisions and weights (the small loads go out
+  // together), then the SwiGLU outputs of every group (by group index, so
+  // independent of the ids) and the shared expert's W2 row
+  int p = 0, slot = -1;
+  float wg = 0.0f;
+  if (lane < k) {
+    if constexpr (HAS2) p = (int)a.prec[lane];  // precisions are given exactly when 2-bit copies may appear
+    slot = a.slot_ids[lane];
+    wg = a.w[lane];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 h0[NB], h1[NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    float part = 0.0f, part2 = 0.0f;
+  for (int g = 0; g < NB; ++g) {
+    const uint4* src = (const uint4*)(a.h + (size_t)min(g, a.K1 - 1) * I);
+    h0[g] = src[tid];
+    if (CPL == 2) h1[g] = src[tid + 256];
+  }
+  DNRow<CPL> sl[NB];  // slot 0: the shared expert when present, then the ranks
+  if constexpr (SH) issue4(sl[0], a.shared);
+  stab[tid] = e8m0_to_f32(tid);
+#pragma unroll
+  for (int g = 0; g < NB; ++g) {  // waits for the ids and h, not for the shared row
+    ((uint4*)(lds + (size_t)g * I * 2))[tid] = h0[g];
+    if (CPL == 2) ((uint4*)(lds + (size_t)g * I * 2))[tid + 256] = h1[g];
+  }
+
+  // 2. the surviving ranks in rank order, and their W2 rows (batch slots
+  // past them repeat the last one and are not summed)
+  const int pr = lane >= k ? -1
+                 : (p == 0 && slot >= 0 && slot < a.num_slots) ? 0
+                 : (HAS2 && p == 1 && slot >= 0 && slot < a.num_int2) ? 1 : -1;
+  const uint64_t m = __ballot(pr >= 0);
+  const int nr = __popcll(m);
+  int gi[NB], pi[NB];
+  float wi[NB];
+  if constexpr (SH) {
+    gi[0] = k;
+    pi[0] = 0;
+    wi[0] = 1.0f;
+  }
+  auto part_of = [&](int u) {
+    float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
       XChunk hq;
-      hq.load_lds(lds + (size_t)i * I * 2, (size_t)(q * 64 + lane) * 32);
-      if (!HAS2 || pi[i] == 0)
-        hq.fp4_acc(sl[i].c[q], stab[sl[i].s[q]], part, part2);
+      hq.load_lds(lds + (size_t)gi[u] * I * 2, (size_t)(q * 64 + lane) * 32);
+      if (!HAS2 || pi[u] == 0)
+        hq.fp4_acc(sl[u].c[q], stab[sl[u].s[q]], p0, p1);
       else
-        part = fmaf(hq.int2(make_uint2(sl[i].c[q].x, sl[i].c[q].y)), e4m3_to_f32(sl[i].s[q]), part);
+        p0 = fmaf(hq.int2(make_uint2(sl[u].c[q].x, sl[u].c[q].y)), e4m3_to_f32(sl[u].s[q]), p0);
     }
-    const float t = fmaf(wi[i], part + part2, acc);
-    acc = (i < nact_v) ? t : acc;
+    return p0 + p1;
+  };
+  if (nr == 0) {  // every rank dropped: the shared expert alone, or nothing
+    __syncthreads();
+    float acc = 0.0f;
+    if constexpr (SH) acc = part_of(0);
+    const float v = wave_sum_to_lane63(acc);
+    if (lane == 63) ((uint16_t*)a.out)[orow] = f32_to_bf16(v);
+    return;
   }
+#pragma unroll
+  for (int u = S0; u < NB; ++u) {
+    const int g = nth_set_bit(m, min(u - S0, nr - 1));
+    gi[u] = g;
+    pi[u] = __builtin_amdgcn_readlane(pr, g);
+    wi[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wg), g));
+    const size_t sg = (size_t)__builtin_amdgcn_readlane(slot, g);
+    if (HAS2 && pi[u] == 1) {
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const size_t c = (size_t)(q * 64 + lane);
+        const uint8_t* rec = a.int2_base + sg * a.int2_stride;
+        const uint2 v = ld_stream8(rec + L2.w2c + (size_t)orow * rowb2 + c * 8);
+        sl[u].c[q] = make_uint4(v.x, v.y, 0u, 0u);
+        sl[u].s[q] = rec[L2.w2s + (size_t)orow * rows + c];
+      }
+    } else {
+      issue4(sl[u], a.fp4_base + sg * a.fp4_stride);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every W2 load is out before the first wait
+  __syncthreads();
+
+  // 3. the weighted sum in rank order, then the shared expert (weight 1).
+  // Straight-line code: slots past the survivors are computed and selected
+  // away, so no load is sunk into a branch.
+  int nr_v;  // the survivor count in a vector register: the selects stay selects
+  asm volatile("v_mov_b32 %0, %1" : "=v"(nr_v) : "s"(nr));
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = S0; u < NB; ++u) {
+    const float t = fmaf(wi[u], part_of(u), acc);
+    acc = (u - S0 < nr_v) ? t : acc;
+  }
+  if constexpr (SH) acc += part_of(0);
   const float v = wave_sum_to_lane63(acc);
   if (lane == 63) ((uint16_t*)a.out)[orow] = f32_to_bf16(v);
 }
@@ -447,44 +429,70 @@ __global__ __launch_bounds__(256) void down_combine_b1_kernel(B1Args a) {
 // plus the shared expert are exact; other counts repeat the last group)
 int down_batch(int K1) { return K1 <= 4 ? 4 : K1 <= 7 ? 7 : K1 <= 9 ? 9 : kMaxGroups; }
 
+template <int CPL, int NB, bool SH>
+void launch_gateup_nb(const B1Args& a, hipStream_t s) {
+  const int grid = a.I / 4;  // one wavefront per gate/up row
+  if (!a.logits)
+    hipLaunchKernelGGL((gateup_b1_kernel<CPL, NB, 0, SH>), dim3(grid), dim3(256), 0, s, a);
+  else if (a.E <= 256)
+    hipLaunchKernelGGL((gateup_b1_kernel<CPL, NB, 4, SH>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gateup_b1_kernel<CPL, NB, kMaxE / 64, SH>), dim3(grid), dim3(256), 0, s, a);
+}
+
+template <int CPL, bool SH>
+void launch_gateup_sh(const B1Args& a, hipStream_t s) {
+  const int nb = down_batch(a.K1);
+  if (nb == 4)
+    launch_gateup_nb<CPL, 4, SH>(a, s);
+  else if (nb == 7)
+    launch_gateup_nb<CPL, 7, SH>(a, s);
+  else if (nb == 9)
+    launch_gateup_nb<CPL, 9, SH>(a, s);
+  else if constexpr (CPL == 1)
+    launch_gateup_nb<CPL, kMaxGroups, SH>(a, s);
+}
+
 template <int CPL>
 void launch_gateup_b1(const B1Args& a, hipStream_t s) {
-  constexpr int NR = MOE_B1_GU_ROWS;
-  const int waves = (a.K1 * a.I + NR - 1) / NR;
-  const int grid = std::max(1, (waves + 3) / 4);
-  if (!a.logits)
-    hipLaunchKernelGGL((gateup_b1_kernel<CPL, NR, 0>), dim3(grid), dim3(256), 0, s, a);
-  else if (a.E <= 256)
-    hipLaunchKernelGGL((gateup_b1_kernel<CPL, NR, 4>), dim3(grid), dim3(256), 0, s, a);
+  if (a.shared)
+    launch_gateup_sh<CPL, true>(a, s);
   else
-    hipLaunchKernelGGL((gateup_b1_kernel<CPL, NR, kMaxE / 64>), dim3(grid), dim3(256), 0, s, a);
+    launch_gateup_sh<CPL, false>(a, s);
   if (a.prec) {  // 2-bit copies can only appear when precisions are given
     const int grid2 = std::max(1, std::min(a.I / 4, 1024));
     hipLaunchKernelGGL((gateup_int2_b1_kernel<CPL>), dim3(grid2), dim3(256), 0, s, a);
   }
 }
 
-template <int CPL, bool HAS2>
+template <int CPL, bool HAS2, bool SH>
 void launch_down_nb(const B1Args& a, hipStream_t s) {
   const int grid = a.H / 4;
   const int nb = down_batch(a.K1);
   const size_t lds = (size_t)nb * a.I * 2;
   if (nb == 4)
-    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, 4, HAS2>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, 4, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
   else if (nb == 7)
-    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, 7, HAS2>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, 7, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
   else if (nb == 9)
-    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, 9, HAS2>), dim3(grid), dim3(256), lds, s, a);
-  else
-    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, kMaxGroups, HAS2>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, 9, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
+  else if constexpr (CPL == 1)
+    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, kMaxGroups, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
 }
 
 template <int CPL>
 void launch_down_b1(const B1Args& a, hipStream_t s) {
-  if (a.prec)
-    launch_down_nb<CPL, true>(a, s);
-  else
-    launch_down_nb<CPL, false>(a, s);
+  if (a.prec) {
+    if (a.shared)
+      launch_down_nb<CPL, true, true>(a, s);
+    else
+      launch_down_nb<CPL, true, false>(a, s);
+  } else {
+    if (a.shared)
+      launch_down_nb<CPL, false, true>(a, s);
+    else
+      launch_down_nb<CPL, false, false>(a, s);
+  }
 }
 
 }  // namespace
@@ -497,7 +505,7 @@ void launch_down_b1(const B1Args& a, hipStream_t s) {
 bool b1_path_ok(int H, int I, int K1, bool xbf16, bool obf16) {
   if (!xbf16 || !obf16) return false;
   if (!(H == 2048 || H == 4096) || !(I == 2048 || I == 4096)) return false;
-  if (K1 < 1 || K1 > kMaxGroups) return false;
+  if (K1 < 1 || K1 > (H == 2048 ? kMaxGroups : 9)) return false;  // the gate/up rows of a wavefront fit its registers
   return (size_t)down_batch(K1) * I * 2 <= 64 * 1024;
 }
 

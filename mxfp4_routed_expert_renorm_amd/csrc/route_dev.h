@@ -50,15 +50,33 @@ __device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
 // Each round takes the wavefront maximum of the 32-bit images; among the
 // positions holding it the lowest expert id wins (a ballot settles the
 // common single-holder case, a wavefront minimum over ids the rest).
+// The two halves of route_wave, for callers that issue other loads between
+// the logits loads and the selection: lane l loads experts l + 64 j.
+template <int EPL>
+__device__ __forceinline__ void route_load(const float* __restrict__ row, int E, float (&v)[EPL]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) v[j] = row[min(lane + 64 * j, E - 1)];  // unconditional (clamped)
+}
+
+template <int EPL>
+__device__ __forceinline__ void route_select(const float (&v)[EPL], int E, int k, int* my_e, float* my_w);
+
 template <int EPL>
 __device__ __forceinline__ void route_wave(const float* __restrict__ row, int E, int k, int* my_e, float* my_w) {
+  float v[EPL];
+  route_load<EPL>(row, E, v);
+  route_select<EPL>(v, E, k, my_e, my_w);
+}
+
+template <int EPL>
+__device__ __forceinline__ void route_select(const float (&lv)[EPL], int E, int k, int* my_e, float* my_w) {
   const int lane = threadIdx.x & 63;
   uint32_t key[EPL];
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) {  // unconditional (clamped) loads, all in flight together
+  for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    const float v = row[min(e, E - 1)];
-    key[j] = sel_key(v) & (0u - (uint32_t)(e < E));  // arithmetic mask: no branch around the load
+    key[j] = sel_key(lv[j]) & (0u - (uint32_t)(e < E));  // arithmetic mask: no branch around the load
   }
   uint32_t kv = 0;  // lane r keeps the r-th selected image
   int ee = 0;
