@@ -57,11 +57,10 @@ moe_status launch_combine(const float* y, const float* w, const int8_t* prec, in
   if (T == 0) return MOE_OK;
   const long n = (long)T * (H / 4);
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
-  ProfScope prof(MOE_PROF_COMBINE, s);
   if (ot == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, y, w, prec, T, k, H, has_shared, out);
+    launch(MOE_PROF_COMBINE, combine_kernel<true>, grid, block, 0, s, y, w, prec, T, k, H, has_shared, out);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, y, w, prec, T, k, H, has_shared, out);
+    launch(MOE_PROF_COMBINE, combine_kernel<false>, grid, block, 0, s, y, w, prec, T, k, H, has_shared, out);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

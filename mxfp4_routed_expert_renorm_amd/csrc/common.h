@@ -2,6 +2,7 @@
 // wavefront reductions, the expert record layout and host error plumbing.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -183,17 +184,22 @@ moe_status fail(moe_status st, const char* fmt, ...);
   } while (0)
 
 // ---------------------------------------------------------------------------
-// event timing of the library's launches (off unless moe_profile_begin ran)
+// launches, timed when profiling is on (moe_profile_begin): each launch then
+// gets its own event pair, recorded by the dispatch itself at the kernel's
+// start and end (hipExtLaunchKernel), so the elapsed time is the kernel's
+// duration on the device, not the gap between two stream commands
 
-class ProfScope {
- public:
-  ProfScope(int kind, hipStream_t s);
-  ~ProfScope();
+// a fresh event pair for a launch of `kind`; false when profiling is off
+bool prof_events(int kind, hipEvent_t* start, hipEvent_t* stop);
 
- private:
-  int idx_;
-  hipStream_t s_;
-};
+template <typename F, typename... Args>
+inline void launch(int kind, F kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (prof_events(kind, &e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)shmem, s, e0, e1, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
 
 // ---------------------------------------------------------------------------
 // internal launchers (each validates nothing: the C entry points do)

@@ -41,8 +41,7 @@ moe_status launch_dequant(const uint8_t* record, int H, int I, int prec, int mat
   const size_t coff[3] = {L.w1c, L.w3c, L.w2c}, soff[3] = {L.w1s, L.w3s, L.w2s};
   const int rows = matrix == 2 ? H : I, cols = matrix == 2 ? I : H;
   const long ndw = (long)rows * cols / (32 / bits);
-  ProfScope prof(MOE_PROF_DEQUANT, s);
-  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0, s, record + coff[matrix],
+  launch(MOE_PROF_DEQUANT, dequant_kernel, dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0, s, record + coff[matrix],
                      record + soff[matrix], rows, cols, bits, out);
   MOE_LAUNCH_CHECK();
   return MOE_OK;

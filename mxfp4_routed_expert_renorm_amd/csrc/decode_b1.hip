@@ -433,11 +433,11 @@ template <int CPL, int NB, bool SH>
 void launch_gateup_nb(const B1Args& a, hipStream_t s) {
   const int grid = a.I / 4;  // one wavefront per gate/up row
   if (!a.logits)
-    hipLaunchKernelGGL((gateup_b1_kernel<CPL, NB, 0, SH>), dim3(grid), dim3(256), 0, s, a);
+    launch(MOE_PROF_GATEUP, (gateup_b1_kernel<CPL, NB, 0, SH>), dim3(grid), dim3(256), 0, s, a);
   else if (a.E <= 256)
-    hipLaunchKernelGGL((gateup_b1_kernel<CPL, NB, 4, SH>), dim3(grid), dim3(256), 0, s, a);
+    launch(MOE_PROF_GATEUP, (gateup_b1_kernel<CPL, NB, 4, SH>), dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gateup_b1_kernel<CPL, NB, kMaxE / 64, SH>), dim3(grid), dim3(256), 0, s, a);
+    launch(MOE_PROF_GATEUP, (gateup_b1_kernel<CPL, NB, kMaxE / 64, SH>), dim3(grid), dim3(256), 0, s, a);
 }
 
 template <int CPL, bool SH>
@@ -461,7 +461,7 @@ void launch_gateup_b1(const B1Args& a, hipStream_t s) {
     launch_gateup_sh<CPL, false>(a, s);
   if (a.prec) {  // 2-bit copies can only appear when precisions are given
     const int grid2 = std::max(1, std::min(a.I / 4, 1024));
-    hipLaunchKernelGGL((gateup_int2_b1_kernel<CPL>), dim3(grid2), dim3(256), 0, s, a);
+    launch(MOE_PROF_GATEUP, (gateup_int2_b1_kernel<CPL>), dim3(grid2), dim3(256), 0, s, a);
   }
 }
 
@@ -471,13 +471,13 @@ void launch_down_nb(const B1Args& a, hipStream_t s) {
   const int nb = down_batch(a.K1);
   const size_t lds = (size_t)nb * a.I * 2;
   if (nb == 4)
-    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, 4, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
+    launch(MOE_PROF_DOWN, (down_combine_b1_kernel<CPL, 4, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
   else if (nb == 7)
-    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, 7, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
+    launch(MOE_PROF_DOWN, (down_combine_b1_kernel<CPL, 7, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
   else if (nb == 9)
-    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, 9, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
+    launch(MOE_PROF_DOWN, (down_combine_b1_kernel<CPL, 9, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
   else if constexpr (CPL == 1)
-    hipLaunchKernelGGL((down_combine_b1_kernel<CPL, kMaxGroups, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
+    launch(MOE_PROF_DOWN, (down_combine_b1_kernel<CPL, kMaxGroups, HAS2, SH>), dim3(grid), dim3(256), lds, s, a);
 }
 
 template <int CPL>
@@ -537,7 +537,6 @@ moe_status launch_b1(const moe_layer* L, const float* logits, int E, const void*
   a.h = h;
   a.out = out;
   {
-    ProfScope prof(MOE_PROF_GATEUP, s);
     if (a.H == 2048)
       launch_gateup_b1<1>(a, s);
     else
@@ -545,7 +544,6 @@ moe_status launch_b1(const moe_layer* L, const float* logits, int E, const void*
     MOE_LAUNCH_CHECK();
   }
   {
-    ProfScope prof(MOE_PROF_DOWN, s);
     if (a.I == 2048)
       launch_down_b1<1>(a, s);
     else

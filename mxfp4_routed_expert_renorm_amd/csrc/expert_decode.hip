@@ -446,14 +446,14 @@ struct Launcher {
   static void gateup(const DecodeArgs& a, bool xbf16, int grid, hipStream_t s) {
     constexpr int U = (LPR == 64) ? 2 : 1;
     if (xbf16)
-      hipLaunchKernelGGL((gateup_kernel<LPR, CPL, U, true, TABLE>), dim3(grid), dim3(256), 0, s, a);
+      launch(MOE_PROF_GATEUP, (gateup_kernel<LPR, CPL, U, true, TABLE>), dim3(grid), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((gateup_kernel<LPR, CPL, U, false, TABLE>), dim3(grid), dim3(256), 0, s, a);
+      launch(MOE_PROF_GATEUP, (gateup_kernel<LPR, CPL, U, false, TABLE>), dim3(grid), dim3(256), 0, s, a);
   }
   template <int LPR, int CPL>
   static void down(const DecodeArgs& a, int grid, hipStream_t s) {
     constexpr int U = (LPR == 64) ? 2 : 1;
-    hipLaunchKernelGGL((down_kernel<LPR, CPL, U, TABLE>), dim3(grid), dim3(256), 0, s, a);
+    launch(MOE_PROF_DOWN, (down_kernel<LPR, CPL, U, TABLE>), dim3(grid), dim3(256), 0, s, a);
   }
 };
 
@@ -533,13 +533,11 @@ moe_status launch_expert_decode(const moe_layer* L, const void* x, moe_dtype xt,
 
   if (T == 1) {
     {
-      ProfScope prof(MOE_PROF_GATEUP, s);
       if (!dispatch_gateup<false>(lpr_gu, cpl_gu, a, xbf16, K1 * tiles_gu, s))
         return fail(MOE_ESHAPE, "H=%d unsupported", a.H);
       MOE_LAUNCH_CHECK();
     }
     {
-      ProfScope prof(MOE_PROF_DOWN, s);
       if (!dispatch_down<false>(lpr_dn, cpl_dn, a, K1 * tiles_dn, s)) return fail(MOE_ESHAPE, "I=%d unsupported", a.I);
       MOE_LAUNCH_CHECK();
     }
@@ -552,15 +550,13 @@ moe_status launch_expert_decode(const moe_layer* L, const void* x, moe_dtype xt,
   int32_t* perm = offsets + 4097;
   int32_t* active = perm + P;
   {
-    ProfScope prof(MOE_PROF_PLAN, s);
-    hipLaunchKernelGGL(pair_keys_kernel, dim3(P), dim3(256), 0, s, a, keys);
+    launch(MOE_PROF_PLAN, pair_keys_kernel, dim3(P), dim3(256), 0, s, a, keys);
     MOE_LAUNCH_CHECK();
   }
   moe_status st = launch_group(keys, P, nkeys, counts, offsets, perm, s);
   if (st != MOE_OK) return st;
   {
-    ProfScope prof(MOE_PROF_PLAN, s);
-    hipLaunchKernelGGL(active_keys_kernel, dim3(1), dim3(64), 0, s, counts, nkeys, active);
+    launch(MOE_PROF_PLAN, active_keys_kernel, dim3(1), dim3(64), 0, s, counts, nkeys, active);
     MOE_LAUNCH_CHECK();
   }
   a.offsets = offsets;
@@ -571,12 +567,10 @@ moe_status launch_expert_decode(const moe_layer* L, const void* x, moe_dtype xt,
   const int grid_gu = (int)std::min<long>((long)max_groups * tiles_gu, 4096);
   const int grid_dn = (int)std::min<long>((long)max_groups * tiles_dn, 4096);
   {
-    ProfScope prof(MOE_PROF_GATEUP, s);
     if (!dispatch_gateup<true>(lpr_gu, cpl_gu, a, xbf16, grid_gu, s)) return fail(MOE_ESHAPE, "H=%d unsupported", a.H);
     MOE_LAUNCH_CHECK();
   }
   {
-    ProfScope prof(MOE_PROF_DOWN, s);
     if (!dispatch_down<true>(lpr_dn, cpl_dn, a, grid_dn, s)) return fail(MOE_ESHAPE, "I=%d unsupported", a.I);
     MOE_LAUNCH_CHECK();
   }

@@ -89,8 +89,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
 
 moe_status launch_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int32_t* offsets, int32_t* perm,
                         hipStream_t s) {
-  ProfScope prof(MOE_PROF_GROUP, s);
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), 0, s, keys, n, nkeys, counts, offsets, perm);
+  launch(MOE_PROF_GROUP, group_kernel, dim3(1), dim3(kGroupThreads), 0, s, keys, n, nkeys, counts, offsets, perm);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -461,8 +461,7 @@ size_t prefill_workspace_bytes(int H, int I, int T, int k, int has_shared) {
 moe_status launch_quant_mxfp8(const void* x, long rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s) {
   const long nblk = rows * (K / 32);
   if (nblk == 0) return MOE_OK;
-  ProfScope prof(MOE_PROF_QUANT, s);
-  hipLaunchKernelGGL(quant_mxfp8_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, (const uint16_t*)x,
+  launch(MOE_PROF_QUANT, quant_mxfp8_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, (const uint16_t*)x,
                      nblk, codes, scales);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
@@ -495,15 +494,13 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
   moe_status st = launch_quant_mxfp8(x, T, H, (uint8_t*)a.xq, (uint8_t*)a.xs, s);
   if (st != MOE_OK) return st;
   {
-    ProfScope prof(MOE_PROF_PLAN, s);
-    hipLaunchKernelGGL(prefill_keys_kernel, dim3((P + 255) / 256), dim3(256), 0, s, a);
+    launch(MOE_PROF_PLAN, prefill_keys_kernel, dim3((P + 255) / 256), dim3(256), 0, s, a);
     MOE_LAUNCH_CHECK();
   }
   st = launch_group(a.keys, P, E + 1, a.counts, a.offsets, a.perm, s);
   if (st != MOE_OK) return st;
   {
-    ProfScope prof(MOE_PROF_PLAN, s);
-    hipLaunchKernelGGL(prefill_items_kernel, dim3(1), dim3(64), 0, s, a.counts, E + 1, a.items);
+    launch(MOE_PROF_PLAN, prefill_items_kernel, dim3(1), dim3(64), 0, s, a.counts, E + 1, a.items);
     MOE_LAUNCH_CHECK();
   }
   // persistent grids: as many workgroups as fit per CU (LDS-limited: one of 8
@@ -513,19 +510,16 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
   const int grid_gu = (int)std::min<long>((long)max_items_m * (I / kNT), 256L * per_cu) / 8 * 8;
   const int grid_dn = (int)std::min<long>((long)max_items_m * (H / kNT), 256L * per_cu) / 8 * 8;
   {
-    ProfScope prof(MOE_PROF_GEMM_GATEUP, s);
-    hipLaunchKernelGGL(gemm_kernel<2>, dim3(std::max(grid_gu, 8)), dim3(kWaves * 64), 0, s, a);
+    launch(MOE_PROF_GEMM_GATEUP, gemm_kernel<2>, dim3(std::max(grid_gu, 8)), dim3(kWaves * 64), 0, s, a);
     MOE_LAUNCH_CHECK();
   }
   {
-    ProfScope prof(MOE_PROF_GEMM_DOWN, s);
-    hipLaunchKernelGGL(gemm_kernel<1>, dim3(std::max(grid_dn, 8)), dim3(kWaves * 64), 0, s, a);
+    launch(MOE_PROF_GEMM_DOWN, gemm_kernel<1>, dim3(std::max(grid_dn, 8)), dim3(kWaves * 64), 0, s, a);
     MOE_LAUNCH_CHECK();
   }
   {
-    ProfScope prof(MOE_PROF_COMBINE, s);
     const long n = (long)T * (H / 8);
-    hipLaunchKernelGGL(combine_bf16y_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, w, T, k, K1,
+    launch(MOE_PROF_COMBINE, combine_bf16y_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, w, T, k, K1,
                        H, (uint16_t*)out);
     MOE_LAUNCH_CHECK();
   }

@@ -1,8 +1,8 @@
 // Event timing of the library's own kernels.  When enabled, every launch the
-// library makes is bracketed by two HIP events recorded on the stream the
-// kernel is launched on, so the elapsed time between them is that kernel's
-// duration on the device.  Used by the benchmark to time the dominant kernel
-// live; off by default (no events are recorded).
+// library makes goes out through hipExtLaunchKernel with its own pair of HIP
+// events, which the dispatch records at the kernel's start and end, so the
+// elapsed time between them is that kernel's duration on the device.  Used by
+// the benchmark to time the dominant kernel live; off by default.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -35,23 +35,16 @@ ProfState& prof() {
 
 }  // namespace
 
-ProfScope::ProfScope(int kind, hipStream_t s) : idx_(-1), s_(s) {
+bool prof_events(int kind, hipEvent_t* start, hipEvent_t* stop) {
   ProfState& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
-  if (!p.on || p.next + 2 > p.pool.size()) return;
+  if (!p.on || p.next + 2 > p.pool.size()) return false;
   Record r{kind, p.pool[p.next], p.pool[p.next + 1]};
   p.next += 2;
-  if (hipEventRecord(r.start, s) != hipSuccess) return;
   p.recs.push_back(r);
-  idx_ = (int)p.recs.size() - 1;
-}
-
-ProfScope::~ProfScope() {
-  if (idx_ < 0) return;
-  ProfState& p = prof();
-  std::lock_guard<std::mutex> g(p.mu);
-  if (!p.on || idx_ >= (int)p.recs.size()) return;
-  (void)hipEventRecord(p.recs[idx_].stop, s_);
+  *start = r.start;
+  *stop = r.stop;
+  return true;
 }
 
 }  // namespace moe

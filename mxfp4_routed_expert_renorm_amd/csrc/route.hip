@@ -55,17 +55,16 @@ moe_status launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
   if (T == 0) return MOE_OK;
   const int epl = (E + 63) / 64;
   const dim3 grid((T + 3) / 4), block(256);
-  ProfScope prof(MOE_PROF_ROUTE, s);
   if (epl <= 1) {
-    hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, s, logits, T, E, k, ids, w);
+    launch(MOE_PROF_ROUTE, route_kernel<1>, grid, block, 0, s, logits, T, E, k, ids, w);
   } else if (epl <= 2) {
-    hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, s, logits, T, E, k, ids, w);
+    launch(MOE_PROF_ROUTE, route_kernel<2>, grid, block, 0, s, logits, T, E, k, ids, w);
   } else if (epl <= 4) {
-    hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, s, logits, T, E, k, ids, w);
+    launch(MOE_PROF_ROUTE, route_kernel<4>, grid, block, 0, s, logits, T, E, k, ids, w);
   } else if (epl <= 8) {
-    hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, s, logits, T, E, k, ids, w);
+    launch(MOE_PROF_ROUTE, route_kernel<8>, grid, block, 0, s, logits, T, E, k, ids, w);
   } else {
-    hipLaunchKernelGGL(route_kernel<kMaxEPL>, grid, block, 0, s, logits, T, E, k, ids, w);
+    launch(MOE_PROF_ROUTE, route_kernel<kMaxEPL>, grid, block, 0, s, logits, T, E, k, ids, w);
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
@@ -76,11 +75,10 @@ moe_status launch_router_logits(const void* x, moe_dtype xt, const float* wr, in
   if (T == 0) return MOE_OK;
   const long items = (long)T * E;
   const dim3 grid((unsigned)((items + 3) / 4)), block(256);
-  ProfScope prof(MOE_PROF_ROUTER_LOGITS, s);
   if (xt == MOE_BF16) {
-    hipLaunchKernelGGL(router_logits_kernel<true>, grid, block, 0, s, x, wr, T, E, H, logits);
+    launch(MOE_PROF_ROUTER_LOGITS, router_logits_kernel<true>, grid, block, 0, s, x, wr, T, E, H, logits);
   } else {
-    hipLaunchKernelGGL(router_logits_kernel<false>, grid, block, 0, s, x, wr, T, E, H, logits);
+    launch(MOE_PROF_ROUTER_LOGITS, router_logits_kernel<false>, grid, block, 0, s, x, wr, T, E, H, logits);
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
