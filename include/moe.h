@@ -203,11 +203,11 @@ size_t moe_prefill_workspace_bytes(int H, int I, int T, int k, int has_shared);
  * gate/up products on scaled FP8 x FP4 MFMA with SwiGLU and MXFP8 requantisation
  * of h in the epilogue, the down products likewise, and the rank-ordered combine
  * with the shared expert to out [T][H] bf16.  Every expert of the resident layer
- * is streamed once per 256-token tile of its group.
+ * is streamed once per tile of up to 192 rows of its group.
  *   layer: fp4_base/fp4_stride/num_slots = the E resident experts (slot = expert id),
- *          shared optional, no 2-bit copies; H and I multiples of 64.
+ *          shared optional, no 2-bit copies; H a multiple of 256, I a multiple of 128.
  *   ids [T][k] int32 expert ids (moe_route's output), w [T][k] fp32 weights.
- * T*(k+has_shared) <= 1<<20, E <= 4095. */
+ * T*(k+has_shared) <= 1<<20, T*H and T*(k+has_shared)*I < 2^31, E <= 4095. */
 moe_status moe_prefill_forward(const moe_layer* layer, const void* x, int T, int k, const int32_t* ids,
                                const float* w, void* out, void* workspace, size_t workspace_bytes,
                                moe_stream_t stream);

@@ -220,12 +220,14 @@ moe_status moe_prefill_forward(const moe_layer* layer, const void* x, int T, int
                                void* out, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
   REQUIRE(layer, MOE_EINVAL, "moe_prefill_forward: layer is NULL");
   const int H = layer->H, I = layer->I, E = layer->num_slots;
-  REQUIRE(H >= 64 && I >= 64 && H % 64 == 0 && I % 64 == 0, MOE_ESHAPE,
-          "moe_prefill_forward: H=%d I=%d must be multiples of 64", H, I);
+  REQUIRE(H >= 256 && I >= 128 && H % 256 == 0 && I % 128 == 0, MOE_ESHAPE,
+          "moe_prefill_forward: H=%d must be a multiple of 256 and I=%d a multiple of 128", H, I);
   REQUIRE(E >= 1 && E <= 4095, MOE_ESHAPE, "moe_prefill_forward: num_slots (experts) = %d outside 1..4095", E);
   REQUIRE(k >= 1 && k <= E && k <= 64, MOE_EINVAL, "moe_prefill_forward: k=%d (E=%d)", k, E);
   const int K1 = k + (layer->shared ? 1 : 0);
   REQUIRE(T >= 0 && (long)T * K1 <= (1L << 20), MOE_ESHAPE, "moe_prefill_forward: T=%d too large", T);
+  REQUIRE((long)T * K1 * I < (1L << 31) && (long)T * H < (1L << 31), MOE_ESHAPE,
+          "moe_prefill_forward: T=%d: activations beyond 2 GiB per matrix", T);
   if (T == 0) return MOE_OK;
   REQUIRE(layer->fp4_base && x && ids && w && out && workspace, MOE_EINVAL, "moe_prefill_forward: NULL pointer");
   const size_t fb = record_layout(H, I, 4).bytes;

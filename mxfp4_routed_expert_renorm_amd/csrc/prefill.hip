@@ -22,6 +22,7 @@
 // the lane's A scale is the row's block h.  Output: acc[i] is row
 // 8*(i/4) + 4*h + i%4, column c.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -33,40 +34,42 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 #ifndef MOE_PF_WAVES
-#define MOE_PF_WAVES 8
+#define MOE_PF_WAVES 4
 #endif
-constexpr int kWaves = MOE_PF_WAVES;  // wavefronts per GEMM workgroup, one 32-row block each
-constexpr int kMT = 32 * kWaves;      // grouped token rows per GEMM item
-constexpr int kNT = 64;       // weight rows per GEMM item (2 MFMA column blocks)
+constexpr int kWaves = MOE_PF_WAVES;  // wavefronts per GEMM workgroup (4: one per SIMD, or 8)
+constexpr int kMB = 6;        // 32-row M blocks per item at most
+constexpr int kMT = 32 * kMB; // grouped rows per item at most
+constexpr int kNR = 256;      // weight rows per item (8 MFMA column blocks)
+#ifndef MOE_PF_DEPTH
+#define MOE_PF_DEPTH 1
+#endif
+constexpr int kDepth = MOE_PF_DEPTH;  // K stages held in registers ahead of the LDS stage
 constexpr int kMaxKeys = 4096;
 
 // ------------------------------------------------------------------ MXFP8
 
-// nearest E4M3 (OCP E4M3FN) code of a value, ties to even, saturating at 448
+// nearest E4M3 (OCP E4M3FN) code of a value, ties to even, saturating at
+// +-448: gfx950's convert rounds to nearest even, and clamping first turns
+// its overflow into the saturation the MX rule asks for
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fminf(fabsf(v), 448.0f);
-  uint32_t code;
-  if (a < 0.015625f) {  // below 2^-6: subnormal steps of 2^-9 (code 8 is the smallest normal)
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
-    const float mant = a * __uint_as_float((uint32_t)(127 - e) << 23);  // in [1, 2)
-    uint32_t m3 = (uint32_t)__builtin_rintf((mant - 1.0f) * 8.0f);
-    if (m3 == 8u) {
-      m3 = 0u;
-      e += 1;
-    }
-    code = ((uint32_t)(e + 7) << 3) | m3;
-  }
-  return sign | code;
+  const float c = fminf(fmaxf(v, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false) & 0xffu;
+}
+
+// four codes packed low byte first
+__device__ __forceinline__ uint32_t e4m3_encode4(float v0, float v1, float v2, float v3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(v0, -448.0f), 448.0f), fminf(fmaxf(v1, -448.0f), 448.0f),
+                                                 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(v2, -448.0f), 448.0f),
+                                                   fminf(fmaxf(v3, -448.0f), 448.0f), lo, true);
 }
 
 // shared exponent of a 32-block with maximum magnitude amax: floor(log2 amax) - 8,
 // clamped to the E8M0 range; an all-zero block gets -127 (scale byte 0)
 __device__ __forceinline__ int mx_shared_exp(float amax) {
   if (!(amax > 0.0f)) return -127;
-  const int e = ilogbf(amax) - 8;
+  const int f = (int)((__float_as_uint(amax) >> 23) & 0xffu);  // subnormal: 0, clamps to -127 below
+  const int e = (f == 255 ? 255 : f - 127) - 8;
   return max(-127, min(127, e));
 }
 
@@ -94,11 +97,9 @@ __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __rest
   const int sh = mx_shared_exp(amax);
   uint32_t out[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    out[i] = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[i] |= e4m3_encode(ldexpf(v[4 * i + j], -sh)) << (8 * j);
-  }
+  for (int i = 0; i < 8; ++i)
+    out[i] = e4m3_encode4(ldexpf(v[4 * i], -sh), ldexpf(v[4 * i + 1], -sh), ldexpf(v[4 * i + 2], -sh),
+                          ldexpf(v[4 * i + 3], -sh));
   uint4* dst = (uint4*)(codes + b * 32);
   dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
   dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
@@ -145,7 +146,9 @@ __global__ __launch_bounds__(256) void prefill_keys_kernel(PrefillArgs a) {
   }
 }
 
-// items[0] = number of (key, row0) M-tiles; tiles of kMT rows per non-empty key
+// items[0] = number of M tiles, then (key, row0, rows) per tile.  A key with c
+// rows gets ceil(c / kMT) tiles of equal size rounded up to whole 32-row
+// blocks (the last one takes the rest), so e.g. 140 rows run as one tile.
 __global__ __launch_bounds__(64) void prefill_items_kernel(const int32_t* __restrict__ counts, int nkeys,
                                                            int32_t* __restrict__ items) {
   const int lane = threadIdx.x;
@@ -161,9 +164,11 @@ __global__ __launch_bounds__(64) void prefill_items_kernel(const int32_t* __rest
       if (lane >= off) incl += o;
     }
     const int first = n + incl - tiles;
+    const int sz = tiles ? ((c + tiles - 1) / tiles + 31) / 32 * 32 : 0;
     for (int i = 0; i < tiles; ++i) {
-      items[1 + 2 * (first + i)] = key;
-      items[2 + 2 * (first + i)] = i * kMT;
+      items[1 + 3 * (first + i)] = key;
+      items[2 + 3 * (first + i)] = i * sz;
+      items[3 + 3 * (first + i)] = min(sz, c - i * sz);
     }
     n += __shfl(incl, 63, 64);
   }
@@ -193,213 +198,307 @@ __device__ __forceinline__ float half_wave_max(float v) {
   v = fmaxf(v, dpp_f32<dpp::kQuadXor2>(v));
   v = fmaxf(v, dpp_f32<dpp::kRowHalfMirror>(v));
   v = fmaxf(v, dpp_f32<dpp::kRowMirror>(v));
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return v;
+  // rows 2j and 2j+1 of 16 lanes swap: p[0] holds the even row's value, p[1] the odd row's
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
 // ------------------------------------------------------------- grouped GEMM
 //
-// One template for both products.  An item is (M tile = up to 256 grouped rows
-// of one expert, N tile = 64 weight rows of each of NMAT matrices).  The
-// workgroup's 8 wavefronts own one 32-row block of the M tile each and every
-// 32x32 output block of the N tile.  K advances 128 at a time through a
-// double-buffered LDS stage: each thread's share of the next stage's
-// activation rows, weight rows and their scale bytes is loaded into registers
-// while the current stage feeds the MFMAs, then written to the other buffer.
-// LDS rows are padded by 16 bytes so the 32 rows a fragment read touches fall
-// in different banks.  Items run N tile innermost and each XCD takes a
-// contiguous range, so the N tiles of one M tile share its activation rows in
-// one L2 while the expert's weights stream from HBM once per M tile.
+// One template for both products.  An item is (M tile = up to 192 grouped
+// rows of one expert, 256 weight rows): for gate/up, 128 rows of w1 and the
+// same 128 rows of w3 (128 columns of h); for down, 256 rows of w2.  The
+// workgroup's 4 wavefronts (one per SIMD) split the item's 32x32 output
+// blocks: wavefront w takes the M blocks of parity w / 2 (blocks w/2, w/2 + 2,
+// w/2 + 4; blocks past the tile's rows are skipped) and the column blocks of
+// half w % 2 — for gate/up the gate blocks and the up blocks of the same 64
+// columns, so SwiGLU pairs them in registers.
+//
+// K advances kKS at a time.  Every thread loads its share of a stage (16-byte
+// pieces of the activation and weight rows, and the stage's scale bytes of
+// one activation row and one weight row) into registers kDepth stages ahead
+// and stores it to one of two LDS buffers one stage ahead of the MFMAs.
+// Loads are unconditional (row indices are clamped to the tile), so the
+// compiler's in-order wait counts make each store wait for its own stage
+// only and kDepth stages stay in flight.  LDS rows are padded by 16 bytes so
+// the 32 rows a fragment read touches fall in different banks.  Items run N
+// tile innermost and each XCD takes a contiguous range of them, so the N
+// tiles of one M tile share its activation rows in one L2 while the
+// expert's weights stream from HBM once per M tile.
 
-constexpr int kKS = 128;                 // K per stage
-constexpr int kArow = kKS + 16;          // padded bytes per activation row in LDS
-constexpr int kBrow = kKS / 2 + 16;      // padded bytes per weight row in LDS
+#ifndef MOE_PF_KS
+#define MOE_PF_KS 128
+#endif
+#ifndef MOE_PF_BNT
+#define MOE_PF_BNT 0
+#endif
+constexpr int kKS = MOE_PF_KS;           // K per stage (64 or 128)
+#ifndef MOE_PF_PADA
+#define MOE_PF_PADA 16
+#endif
+#ifndef MOE_PF_PADB
+#define MOE_PF_PADB 16
+#endif
+constexpr int kArow = kKS + MOE_PF_PADA;      // padded bytes per activation row in LDS
+constexpr int kBrow = kKS / 2 + MOE_PF_PADB;  // padded bytes per weight row in LDS
+constexpr int kNB = 16 / kWaves;              // column blocks per wavefront (the M blocks split in 2)
+constexpr int kThreads = kWaves * 64;
+constexpr int kCA = kKS / 16;            // 16-byte pieces per activation row and stage
+constexpr int kCB = kKS / 32;            // 16-byte pieces per weight row and stage
+constexpr int kPiecesA = kMT * kCA / kThreads;  // activation pieces per thread and stage
+constexpr int kPiecesB = kNR * kCB / kThreads;  // weight pieces per thread and stage
+static_assert(kPiecesA * kThreads == kMT * kCA && kPiecesB * kThreads == kNR * kCB,
+              "stage pieces must divide evenly over the workgroup");
+static_assert(kKS == 64 || kKS == 128, "a stage is one or two MFMA K steps");
+static_assert(kThreads >= kMT && kThreads >= kNR, "one scale entry per thread covers every row");
+// the stage's scale bytes of one row: one per 32 elements of K
+typedef std::conditional<kKS == 64, uint16_t, uint32_t>::type StageScales;
 
-template <int NMAT>
-struct GemmSmem {
+struct alignas(16) GemmSmem {
   uint8_t a[2][kMT * kArow];
-  uint8_t b[2][NMAT * kNT * kBrow];
-  uint32_t as[2][kMT];                  // 4 scale bytes (this stage's 4 blocks) per row
-  uint32_t bs[2][NMAT * kNT];
+  uint8_t b[2][kNR * kBrow];
+  StageScales as[2][kThreads];  // entry i: the stage's scale bytes of activation row i (i < kMT used)
+  StageScales bs[2][kThreads];  // entry i: the stage's scale bytes of weight row i % kNR
+  int32_t pm[kMT];              // down: the (token, rank) pair of each tile row
 };
 
-// 16-byte pieces of the weight tile per thread (4 pieces per 64-byte row)
-template <int NMAT>
-constexpr int pieces_b() { return (NMAT * kNT * 4 + kWaves * 64 - 1) / (kWaves * 64); }
-
-template <int NMAT>
+// native vectors, not uint4: a struct copy of a register array goes through scratch
 struct StageRegs {
-  uint4 a[4];              // 64 activation bytes: half of row tid/2
-  uint4 b[pieces_b<NMAT>()];  // weight pieces tid + j*threads
-  uint32_t as, bs;         // scale dwords of activation row tid and weight row tid
+  u32x4_t a[kPiecesA];
+  u32x4_t b[kPiecesB];
+  StageScales as, bs;
 };
 
-// thread tid loads, for K [k0, k0+kKS): 64 bytes of activation row tid/2, the 4
-// scale bytes of activation row tid (tid < kMT), 16-byte pieces p = tid +
-// j*threads of the weight tile (row p/4, quarter p%4) and the 4 scale bytes of
-// weight row tid (tid < NMAT*kNT)
-template <int NMAT>
-__device__ __forceinline__ void stage_load(StageRegs<NMAT>& r, const uint8_t* arow, const uint8_t* asrow,
-                                           const uint8_t* const* brow, const uint8_t* bsrow, int k0, int tid,
-                                           bool arow_live, bool asrow_live) {
-  if (arow_live) {  // rows past the group's end feed only discarded outputs: not loaded
-    const uint4* ap = (const uint4*)(arow + k0 + 64 * (tid & 1));
+// this thread's load offsets at K = 0 for one item (32-bit, from wave-uniform bases)
+struct LoadOffs {
+  uint32_t a[kPiecesA];  // piece p = tid + j*kThreads: activation row p/kCA (clamped), 16 bytes at 16*(p%kCA)
+  uint32_t b[kPiecesB];  // piece p = tid + j*kThreads: weight row p/kCB, 16 bytes at 16*(p%kCB)
+  uint32_t as;           // scale row of activation row min(tid, rows-1)
+  uint32_t bs;           // scale row of weight row tid % kNR
+};
+
+__device__ __forceinline__ void stage_load(StageRegs& r, const LoadOffs& o, const uint8_t* abase,
+                                           const uint8_t* asbase, const uint8_t* rec, int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.a[i] = ap[i];
-  }
-  if (tid < kMT && asrow_live) r.as = *(const uint32_t*)(asrow + k0 / 32);
+  for (int j = 0; j < kPiecesA; ++j) r.a[j] = *(const u32x4_t*)(abase + (o.a[j] + k0));
 #pragma unroll
-  for (int j = 0; j < pieces_b<NMAT>(); ++j) {
-    const int p = tid + j * kWaves * 64;
-    if (p < NMAT * kNT * 4) r.b[j] = ld_stream16(brow[j] + k0 / 2 + 16 * (p & 3));
+  for (int j = 0; j < kPiecesB; ++j) {
+#if MOE_PF_BNT
+    r.b[j] = __builtin_nontemporal_load((const u32x4_t*)(rec + (o.b[j] + k0 / 2)));
+#else
+    r.b[j] = *(const u32x4_t*)(rec + (o.b[j] + k0 / 2));
+#endif
   }
-  if (tid < NMAT * kNT) r.bs = *(const uint32_t*)(bsrow + k0 / 32);
+  r.as = *(const StageScales*)(asbase + (o.as + k0 / 32));
+  r.bs = *(const StageScales*)(rec + (o.bs + k0 / 32));
 }
 
-template <int NMAT>
-__device__ __forceinline__ void stage_store(GemmSmem<NMAT>& sm, int buf, const StageRegs<NMAT>& r, int tid,
-                                            bool arow_live, bool asrow_live) {
-  if (arow_live) {
-    uint4* ad = (uint4*)(sm.a[buf] + (tid >> 1) * kArow + 64 * (tid & 1));
+__device__ __forceinline__ void stage_store(GemmSmem& sm, int buf, const StageRegs& r, int tid) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ad[i] = r.a[i];
+  for (int j = 0; j < kPiecesA; ++j) {
+    const int p = tid + j * kThreads;
+    *(u32x4_t*)(sm.a[buf] + (p / kCA) * kArow + 16 * (p % kCA)) = r.a[j];
   }
-  if (tid < kMT && asrow_live) sm.as[buf][tid] = r.as;
 #pragma unroll
-  for (int j = 0; j < pieces_b<NMAT>(); ++j) {
-    const int p = tid + j * kWaves * 64;
-    if (p < NMAT * kNT * 4) *(uint4*)(sm.b[buf] + (p >> 2) * kBrow + 16 * (p & 3)) = r.b[j];
+  for (int j = 0; j < kPiecesB; ++j) {
+    const int p = tid + j * kThreads;
+    *(u32x4_t*)(sm.b[buf] + (p / kCB) * kBrow + 16 * (p % kCB)) = r.b[j];
   }
-  if (tid < NMAT * kNT) sm.bs[buf][tid] = r.bs;
+  sm.as[buf][tid] = r.as;
+  sm.bs[buf][tid] = r.bs;
 }
 
-// NMAT = 2: gate/up (W1, W3 of the expert, K = H), SwiGLU + MXFP8 epilogue into hq/hs.
-// NMAT = 1: down (W2, K = I), bf16 epilogue into y at each row's (token, rank) pair.
+struct ItemCtx {
+  LoadOffs O;
+  const uint8_t *abase, *asbase, *rec;
+  int tid, c, h, mp, nh, nstage, rows, start, nt;
+};
+
+// LDS weight-tile block of column block j (0..kNB-1) of the wavefront's
+// column group nh: for gate/up the first kNB/2 are gate blocks and the rest
+// the up blocks of the same columns (gate block b pairs with up block 4 + b);
+// for down, kNB consecutive blocks
 template <int NMAT>
-__global__ __launch_bounds__(kWaves * 64) void gemm_kernel(PrefillArgs a) {
-  __shared__ GemmSmem<NMAT> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 31, h = lane >> 5;
-  const int H = a.H, I = a.I;
-  const int K = NMAT == 2 ? H : I;        // reduction length
-  const int Nall = NMAT == 2 ? I : H;     // weight rows per matrix
-  const int ntiles = Nall / kNT;
-  const int nitems = a.items[0] * ntiles;
-  const RecordLayout L = record_layout(H, I, 4);
-  const size_t wrowb = (size_t)K / 2, wrows = (size_t)K / 32;
+__device__ __forceinline__ int col_block(int nh, int j) {
+  constexpr int half = kNB / 2;
+  return NMAT == 2 ? (j < half ? half * nh + j : 4 + half * nh + (j - half)) : kNB * nh + j;
+}
 
-  for (int item = virtual_block(); item < nitems; item += gridDim.x) {
-    const int mi = item / ntiles, nt = item - mi * ntiles;
-    const int key = a.items[1 + 2 * mi], row0 = a.items[2 + 2 * mi];
-    const int start = a.offsets[key], count = a.offsets[key + 1] - start;
-    const uint8_t* rec = key_record(a, key);
-    // this thread's load rows: activation row tid/2 (codes) and tid (scales),
-    // weight row tid/4 (codes) and tid (scales)
-    auto act_rows = [&](int i, const uint8_t** codes, const uint8_t** scales) {
-      const int ri = min(row0 + i, count - 1);
-      if (NMAT == 2) {
-        const int t = a.perm[start + ri] / a.K1;
-        *codes = a.xq + (size_t)t * H;
-        *scales = a.xs + (size_t)t * (H / 32);
-      } else {
-        *codes = a.hq + (size_t)(start + ri) * I;
-        *scales = a.hs + (size_t)(start + ri) * (I / 32);
-      }
-    };
-    auto weight_rows = [&](int wr, const uint8_t** codes, const uint8_t** scales) {
-      wr = min(wr, NMAT * kNT - 1);
-      const int mat = wr / kNT;
-      const size_t n = (size_t)(nt * kNT + (wr % kNT));
-      const size_t code_off = NMAT == 2 ? (mat == 0 ? L.w1c : L.w3c) : L.w2c;
-      const size_t scale_off = NMAT == 2 ? (mat == 0 ? L.w1s : L.w3s) : L.w2s;
-      *codes = rec + code_off + n * wrowb;
-      *scales = rec + scale_off + n * wrows;
-    };
-    const uint8_t *arow, *asrow, *bsrow, *unused;
-    const uint8_t* brow[pieces_b<NMAT>()];
-    act_rows(tid >> 1, &arow, &unused);
-    act_rows(min(tid, kMT - 1), &unused, &asrow);
+// One item for a wavefront with NL live M blocks (mp, mp + 2, ...).  Every
+// wavefront runs the same loads, stores and barriers whatever its NL; the
+// live count only selects how many MFMA rows it computes, so the accumulators
+// stay in fixed registers.
+template <int NMAT, int NL>
+__device__ __forceinline__ void gemm_item(GemmSmem& sm, const PrefillArgs& a, const ItemCtx& x) {
+  const int tid = x.tid, c = x.c, h = x.h, nstage = x.nstage;
+  v16f acc[NL > 0 ? NL : 1][kNB];
 #pragma unroll
-    for (int j = 0; j < pieces_b<NMAT>(); ++j) weight_rows((tid + j * kWaves * 64) >> 2, &brow[j], &unused);
-    weight_rows(tid, &unused, &bsrow);
-    const bool live = row0 + wave * 32 < count;
-    const bool arow_live = row0 + (tid >> 1) < count;
-    const bool asrow_live = row0 + tid < count;
+  for (int i = 0; i < NL; ++i)
+#pragma unroll
+    for (int j = 0; j < kNB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    v16f acc[NMAT][2];
+  // R[j] holds stage j mod kDepth.  nstage is a multiple of kDepth (checked
+  // at launch), so the unrolled body needs no guards: at the tail the loads are
+  // clamped to the last stage and the last store fills a buffer nobody reads.
+  StageRegs R[kDepth];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[m][nb][i] = 0.0f;
+  for (int d = 0; d < kDepth; ++d) stage_load(R[d], x.O, x.abase, x.asbase, x.rec, d * kKS);
+  __syncthreads();  // the previous item's last stage reads and epilogue are done
+  stage_store(sm, 0, R[0], tid);
+  if (NMAT == 1 && tid < kMT) sm.pm[tid] = a.perm[x.start + min(tid, x.rows - 1)];
+  stage_load(R[0], x.O, x.abase, x.asbase, x.rec, min(kDepth, nstage - 1) * kKS);
+  __syncthreads();
 
-    StageRegs<NMAT> st;
-    stage_load<NMAT>(st, arow, asrow, brow, bsrow, 0, tid, arow_live, asrow_live);
-    __syncthreads();  // the previous item's last stage reads are done
-    stage_store<NMAT>(sm, 0, st, tid, arow_live, asrow_live);
-    __syncthreads();
-    const int nstage = K / kKS;
-    for (int s = 0; s < nstage; ++s) {
-      const int buf = s & 1;
-      if (s + 1 < nstage) stage_load<NMAT>(st, arow, asrow, brow, bsrow, (s + 1) * kKS, tid, arow_live, asrow_live);
-      if (live) {
+  for (int s0 = 0; s0 < nstage; s0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int s = s0 + d;
+      const int buf = (kDepth % 2 == 0) ? (d & 1) : (s & 1);
+      if (NL > 0) {
 #pragma unroll
         for (int kc = 0; kc < kKS / 64; ++kc) {
-          const uint8_t* ar = sm.a[buf] + (wave * 32 + c) * kArow + kc * 64;
-          const uint4 lo = *(const uint4*)(ar + 16 * h);
-          const uint4 hi = *(const uint4*)(ar + 32 + 16 * h);
-          v8i av;
-          av[0] = (int)lo.x, av[1] = (int)lo.y, av[2] = (int)lo.z, av[3] = (int)lo.w;
-          av[4] = (int)hi.x, av[5] = (int)hi.y, av[6] = (int)hi.z, av[7] = (int)hi.w;
-          const int sa = (int)((sm.as[buf][wave * 32 + c] >> (8 * (2 * kc + h))) & 0xffu);
+          v8i bv[kNB];
+          int sb[kNB];
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m)
+          for (int j = 0; j < kNB; ++j) {
+            const int r = col_block<NMAT>(x.nh, j) * 32 + c;
+            const u32x4_t q = *(const u32x4_t*)(sm.b[buf] + r * kBrow + kc * 32 + 16 * h);
+            bv[j][0] = (int)q.x, bv[j][1] = (int)q.y, bv[j][2] = (int)q.z, bv[j][3] = (int)q.w;
+            bv[j][4] = 0, bv[j][5] = 0, bv[j][6] = 0, bv[j][7] = 0;
+            sb[j] = (int)(((uint32_t)sm.bs[buf][r] >> (8 * (2 * kc + h))) & 0xffu);
+          }
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              const int r = m * kNT + nb * 32 + c;
-              const uint4 q = *(const uint4*)(sm.b[buf] + r * kBrow + kc * 32 + 16 * h);
-              v8i bv;
-              bv[0] = (int)q.x, bv[1] = (int)q.y, bv[2] = (int)q.z, bv[3] = (int)q.w;
-              bv[4] = 0, bv[5] = 0, bv[6] = 0, bv[7] = 0;
-              const int sb = (int)((sm.bs[buf][r] >> (8 * (2 * kc + h))) & 0xffu);
-              acc[m][nb] = mfma_fp8_fp4(av, bv, acc[m][nb], sa, sb);
-            }
+          for (int i = 0; i < NL; ++i) {
+            const int r = 32 * (x.mp + 2 * i) + c;
+            const uint8_t* ar = sm.a[buf] + r * kArow + kc * 64;
+            const u32x4_t lo = *(const u32x4_t*)(ar + 16 * h);
+            const u32x4_t hi = *(const u32x4_t*)(ar + 32 + 16 * h);
+            v8i av;
+            av[0] = (int)lo.x, av[1] = (int)lo.y, av[2] = (int)lo.z, av[3] = (int)lo.w;
+            av[4] = (int)hi.x, av[5] = (int)hi.y, av[6] = (int)hi.z, av[7] = (int)hi.w;
+            const int sa = (int)(((uint32_t)sm.as[buf][r] >> (8 * (2 * kc + h))) & 0xffu);
+#pragma unroll
+            for (int j = 0; j < kNB; ++j) acc[i][j] = mfma_fp8_fp4(av, bv[j], acc[i][j], sa, sb[j]);
+          }
         }
       }
-      if (s + 1 < nstage) stage_store<NMAT>(sm, buf ^ 1, st, tid, arow_live, asrow_live);
+      stage_store(sm, buf ^ 1, R[(d + 1) % kDepth], tid);
+      stage_load(R[(d + 1) % kDepth], x.O, x.abase, x.asbase, x.rec, min(s + 1 + kDepth, nstage - 1) * kKS);
       __syncthreads();
     }
-    if (!live) continue;
+  }
+
+  // the epilogue's lane indices pass through an empty asm so the compiler
+  // cannot hoist its address arithmetic into registers held across the loop
+  int ce = c, he = h;
+  asm volatile("" : "+v"(ce), "+v"(he));
+  const int H = a.H, I = a.I;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int rb = 32 * (x.mp + 2 * i);
     if (NMAT == 2) {
       // SwiGLU, MXFP8 requantisation along I (a 32-column block is one half-wave row)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = nt * kNT + nb * 32 + c;
+      for (int q = 0; q < kNB / 2; ++q) {
+        const int col = x.nt * (kNR / 2) + 32 * col_block<2>(x.nh, q) + ce;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float g = acc[0][nb][i], u = acc[NMAT - 1][nb][i];
-          const float hv = g / (1.0f + expf(-g)) * u;
+        for (int e = 0; e < 16; ++e) {
+          const float g = acc[i][q][e], u = acc[i][kNB / 2 + q][e];
+          // silu(g) * u with the hardware exp2 and reciprocal (the result is
+          // requantised to 8 bits next)
+          const float hv = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * g)) * u;
           const float amax = half_wave_max(fabsf(hv));
           const int sh = mx_shared_exp(amax);
-          const int r = row0 + wave * 32 + 8 * (i / 4) + 4 * h + (i % 4);
-          if (r < count) {
-            const size_t pos = (size_t)(start + r);
-            a.hq[pos * I + col] = (uint8_t)e4m3_encode(ldexpf(hv, -sh));
-            if (c == 0) a.hs[pos * (I / 32) + col / 32] = (uint8_t)(sh + 127);
+          const int r = rb + 8 * (e / 4) + 4 * he + (e % 4);
+          if (r < x.rows) {
+            const size_t pos = (size_t)(x.start + r);
+            a.hq[pos * I + col] = (uint8_t)e4m3_encode(__builtin_amdgcn_ldexpf(hv, -sh));
+            if (ce == 0) a.hs[pos * (I / 32) + col / 32] = (uint8_t)(sh + 127);
           }
         }
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = row0 + wave * 32 + 8 * (i / 4) + 4 * h + (i % 4);
-        if (r < count) {
-          const size_t pair = (size_t)a.perm[start + r];
+      for (int e = 0; e < 16; ++e) {
+        const int r = rb + 8 * (e / 4) + 4 * he + (e % 4);
+        if (r < x.rows) {
+          const size_t pair = (size_t)sm.pm[r];
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) a.y[pair * H + nt * kNT + nb * 32 + c] = f32_to_bf16(acc[0][nb][i]);
+          for (int j = 0; j < kNB; ++j)
+            a.y[pair * H + (size_t)x.nt * kNR + col_block<1>(x.nh, j) * 32 + ce] = f32_to_bf16(acc[i][j][e]);
         }
       }
+    }
+  }
+}
+
+// NMAT = 2: gate/up (w1, w3 of the expert, K = H), SwiGLU + MXFP8 epilogue into hq/hs.
+// NMAT = 1: down (w2, K = I), bf16 epilogue into y at each row's (token, rank) pair.
+template <int NMAT>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(PrefillArgs a) {
+  __shared__ GemmSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31, h = lane >> 5;
+  const int mp = wave / (kWaves / 2), nh = wave % (kWaves / 2);
+  const int H = a.H, I = a.I;
+  const int K = NMAT == 2 ? H : I;                      // reduction length
+  const int ncol = NMAT == 2 ? I / (kNR / 2) : H / kNR; // N tiles per M tile
+  const int nitems = a.items[0] * ncol;
+  const int nstage = K / kKS;
+  const RecordLayout L = record_layout(H, I, 4);
+  const uint32_t wrowb = (uint32_t)K / 2, wrows = (uint32_t)K / 32;
+
+  for (int item = virtual_block(); item < nitems; item += gridDim.x) {
+    const int mi = item / ncol, nt = item - mi * ncol;
+    const int key = a.items[1 + 3 * mi], row0 = a.items[2 + 3 * mi], rows = a.items[3 + 3 * mi];
+    const int start = a.offsets[key] + row0;  // first grouped position of the tile
+    const uint8_t* rec = key_record(a, key);
+    // activation rows: x (gathered by token) for gate/up, h (grouped) for down
+    const uint8_t* abase = NMAT == 2 ? a.xq : a.hq;
+    const uint8_t* asbase = NMAT == 2 ? a.xs : a.hs;
+    auto act_row = [&](int r) -> uint32_t {  // row index into abase / asbase
+      r = min(r, rows - 1);
+      return NMAT == 2 ? (uint32_t)(a.perm[start + r] / a.K1) : (uint32_t)(start + r);
+    };
+    // weight rows of the item: offsets of codes or scales inside the record
+    auto weight_row = [&](int wr, bool scales) -> uint32_t {
+      uint32_t n, off;
+      if (NMAT == 2) {
+        const int mat = wr / (kNR / 2);
+        n = (uint32_t)(nt * (kNR / 2) + wr % (kNR / 2));
+        off = (uint32_t)(scales ? (mat == 0 ? L.w1s : L.w3s) : (mat == 0 ? L.w1c : L.w3c));
+      } else {
+        n = (uint32_t)(nt * kNR + wr);
+        off = (uint32_t)(scales ? L.w2s : L.w2c);
+      }
+      return off + n * (scales ? wrows : wrowb);
+    };
+    ItemCtx x;
+#pragma unroll
+    for (int j = 0; j < kPiecesA; ++j) {
+      const int p = tid + j * kThreads;
+      x.O.a[j] = act_row(p / kCA) * (uint32_t)K + 16u * (p % kCA);
+    }
+    x.O.as = act_row(tid) * (uint32_t)(K / 32);
+#pragma unroll
+    for (int j = 0; j < kPiecesB; ++j) {
+      const int p = tid + j * kThreads;
+      x.O.b[j] = weight_row(p / kCB, false) + 16u * (p % kCB);
+    }
+    x.O.bs = weight_row(tid % kNR, true);
+    x.abase = abase, x.asbase = asbase, x.rec = rec;
+    x.tid = tid, x.c = c, x.h = h, x.mp = mp, x.nh = nh, x.nstage = nstage;
+    x.rows = rows, x.start = start, x.nt = nt;
+    // the wavefront's live M blocks: mp, mp + 2, mp + 4 while below the tile's rows
+    const int nl = max(0, min(3, (rows - 32 * mp + 63) / 64));
+    switch (nl) {
+      case 0: gemm_item<NMAT, 0>(sm, a, x); break;
+      case 1: gemm_item<NMAT, 1>(sm, a, x); break;
+      case 2: gemm_item<NMAT, 2>(sm, a, x); break;
+      default: gemm_item<NMAT, 3>(sm, a, x); break;
     }
   }
 }
@@ -444,7 +543,7 @@ PrefillWs prefill_ws_layout(int H, int I, int T, int K1) {
   w.counts = o; o += align256((size_t)kMaxKeys * 4);
   w.offsets = o; o += align256((size_t)(kMaxKeys + 1) * 4);
   w.perm = o; o += align256(P * 4);
-  w.items = o; o += align256((1 + 2 * (P / kMT + kMaxKeys + 1)) * 4);
+  w.items = o; o += align256((1 + 3 * (P / kMT + kMaxKeys + 1)) * 4);
   w.hq = o; o += align256(P * I);
   w.hs = o; o += align256(P * I / 32);
   w.y = o; o += align256(P * H * 2);
@@ -491,6 +590,8 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
   a.hs = (uint8_t*)(ws + lay.hs);
   a.y = (uint16_t*)(ws + lay.y);
 
+  if ((H / kKS) % kDepth != 0 || (I / kKS) % kDepth != 0)
+    return fail(MOE_ESHAPE, "moe_prefill_forward: H=%d and I=%d must be multiples of %d", H, I, kKS * kDepth);
   moe_status st = launch_quant_mxfp8(x, T, H, (uint8_t*)a.xq, (uint8_t*)a.xs, s);
   if (st != MOE_OK) return st;
   {
@@ -503,18 +604,17 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
     launch(MOE_PROF_PLAN, prefill_items_kernel, dim3(1), dim3(64), 0, s, a.counts, E + 1, a.items);
     MOE_LAUNCH_CHECK();
   }
-  // persistent grids: as many workgroups as fit per CU (LDS-limited: one of 8
-  // wavefronts or two of 4), a multiple of 8 (one share per XCD)
-  const long per_cu = kWaves >= 8 ? 1 : 2;
-  const int max_items_m = P / kMT + E + 1;
-  const int grid_gu = (int)std::min<long>((long)max_items_m * (I / kNT), 256L * per_cu) / 8 * 8;
-  const int grid_dn = (int)std::min<long>((long)max_items_m * (H / kNT), 256L * per_cu) / 8 * 8;
+  // persistent grids, one workgroup per CU (each wavefront holds a SIMD's 512
+  // registers), a multiple of 8 (one share per XCD)
+  const long max_items_m = (long)P / kMT + E + 1;
+  const int grid_gu = (int)std::min<long>(max_items_m * (I / (kNR / 2)), 256L) / 8 * 8;
+  const int grid_dn = (int)std::min<long>(max_items_m * (H / kNR), 256L) / 8 * 8;
   {
-    launch(MOE_PROF_GEMM_GATEUP, gemm_kernel<2>, dim3(std::max(grid_gu, 8)), dim3(kWaves * 64), 0, s, a);
+    launch(MOE_PROF_GEMM_GATEUP, gemm_kernel<2>, dim3(std::max(grid_gu, 8)), dim3(kThreads), 0, s, a);
     MOE_LAUNCH_CHECK();
   }
   {
-    launch(MOE_PROF_GEMM_DOWN, gemm_kernel<1>, dim3(std::max(grid_dn, 8)), dim3(kWaves * 64), 0, s, a);
+    launch(MOE_PROF_GEMM_DOWN, gemm_kernel<1>, dim3(std::max(grid_dn, 8)), dim3(kThreads), 0, s, a);
     MOE_LAUNCH_CHECK();
   }
   {

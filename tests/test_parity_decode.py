@@ -163,7 +163,8 @@ def test_router_logits_and_decisions_tiny(gpu_lib):
 def test_group_bit_exact(gpu_lib):
     torch = _torch()
     rng = np.random.default_rng(17)
-    for n, nk in [(384, 257), (32768, 257), (5, 3), (1000, 4096), (64, 1)]:
+    for n, nk in [(384, 257), (32768, 257), (36864, 257), (5, 3), (1000, 4096), (100000, 4096), (70001, 1000),
+                  (64, 1), (0, 7)]:
         keys = rng.integers(0, nk, n).astype(np.int32)
         counts = torch.empty(nk, dtype=torch.int32, device="cuda")
         offsets = torch.empty(nk + 1, dtype=torch.int32, device="cuda")
