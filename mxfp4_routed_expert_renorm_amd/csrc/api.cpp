@@ -4,6 +4,7 @@
 // rather than producing wrong math, the behaviour "Running DeepSeek-V4-Flash
 // across four free GPUs" (§Step 2, Check it divides; §Step 7, the slot-count
 // floor) asks of a serving runtime.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -49,6 +50,10 @@ bool b1_route_ok(int E, int num_slots);
 moe_status launch_b1(const moe_layer* L, const float* logits, int E, const void* x, int k, int32_t* slot_ids,
                      const int8_t* prec, float* w, uint16_t* h, void* out, hipStream_t s);
 size_t decode_plan_ints(int P);
+bool decode_mfma_ok(int H, int I);
+size_t decode_mfma_plan_ints(int P);
+moe_status launch_decode_mfma(const moe_layer* Lr, const void* x, int T, int k, const int32_t* slot_ids, const float* w,
+                              void* out, uint16_t* h, float* y, int32_t* plan, hipStream_t s);
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -106,7 +111,8 @@ moe_status moe_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int
 size_t moe_expert_workspace_bytes(int H, int I, int T, int k, int has_shared) {
   if (H <= 0 || I <= 0 || T < 0 || k <= 0) return 0;
   const size_t P = (size_t)T * (size_t)(k + (has_shared ? 1 : 0));
-  return align256(P * I * 4) + align256(P * H * 4) + align256(decode_plan_ints((int)P) * 4);
+  return align256(P * I * 4) + align256(P * H * 4) +
+         align256(std::max(decode_plan_ints((int)P), decode_mfma_plan_ints((int)P)) * 4);
 }
 
 static moe_status check_layer(const moe_layer* L, const char* who) {
@@ -158,6 +164,10 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype x
   if (T == 1 && w && b1_path_ok(layer->H, layer->I, K1, xt == MOE_BF16, ot == MOE_BF16))  // reads slot_ids and w only
     return launch_b1(layer, nullptr, 0, x, k, const_cast<int32_t*>(slot_ids), prec, const_cast<float*>(w),
                      (uint16_t*)h, out, s);
+  // batches of bf16 tokens, all FP4, weighted output: bf16 MFMA on weights dequantised in registers
+  if (T >= 2 && w && !prec && xt == MOE_BF16 && ot == MOE_BF16 && decode_mfma_ok(layer->H, layer->I) &&
+      P * (size_t)layer->I * 2 < ((size_t)1 << 31) && (size_t)T * layer->H * 2 < ((size_t)1 << 31))
+    return launch_decode_mfma(layer, x, T, k, slot_ids, w, out, (uint16_t*)h, y, plan, s);
   st = launch_expert_decode(layer, x, xt, T, k, slot_ids, prec, h, yout, plan, s);
   if (st != MOE_OK) return st;
   if (w) return launch_combine(y, w, prec, T, k, layer->H, has_shared, out, ot, s);

@@ -126,6 +126,10 @@ struct PrefillArgs {
   uint8_t* hq;          // [P][I] E4M3, grouped order
   uint8_t* hs;          // [P][I/32]
   uint16_t* y;          // [P][H] bf16, pair order
+  // decode batches (bf16 activations on bf16 MFMA)
+  const uint16_t* xb;   // [T][H] bf16
+  uint16_t* hb;         // [P][I] bf16, grouped order
+  float* yf;            // [P][H] fp32, pair order (when non-null, instead of y)
 };
 
 __global__ __launch_bounds__(256) void prefill_keys_kernel(PrefillArgs a) {
@@ -141,14 +145,17 @@ __global__ __launch_bounds__(256) void prefill_keys_kernel(PrefillArgs a) {
   }
   a.keys[p] = key;
   if (key < 0) {  // an out-of-range id contributes nothing: its output row is zero
-    uint4* yrow = (uint4*)(a.y + (size_t)p * a.H);
-    for (int j = 0; j < a.H / 8; ++j) yrow[j] = make_uint4(0u, 0u, 0u, 0u);
+    uint4* yrow = a.yf ? (uint4*)(a.yf + (size_t)p * a.H) : (uint4*)(a.y + (size_t)p * a.H);
+    const int n16 = a.yf ? a.H / 4 : a.H / 8;
+    for (int j = 0; j < n16; ++j) yrow[j] = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
 // items[0] = number of M tiles, then (key, row0, rows) per tile.  A key with c
-// rows gets ceil(c / kMT) tiles of equal size rounded up to whole 32-row
-// blocks (the last one takes the rest), so e.g. 140 rows run as one tile.
+// rows gets ceil(c / MT) tiles of equal size rounded up to whole 32-row
+// blocks (the last one takes the rest), so e.g. 140 rows run as one tile of
+// the prefill GEMM (MT 192).
+template <int MT>
 __global__ __launch_bounds__(64) void prefill_items_kernel(const int32_t* __restrict__ counts, int nkeys,
                                                            int32_t* __restrict__ items) {
   const int lane = threadIdx.x;
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(64) void prefill_items_kernel(const int32_t* __rest
   for (int base = 0; base < nkeys; base += 64) {
     const int key = base + lane;
     const int c = key < nkeys ? counts[key] : 0;
-    const int tiles = (c + kMT - 1) / kMT;
+    const int tiles = (c + MT - 1) / MT;
     int incl = tiles;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -503,6 +510,246 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(PrefillArgs a) {
   }
 }
 
+// ------------------------------------------------ decode-batch grouped GEMM
+//
+// A decode batch of tens of tokens gives each selected expert a handful of
+// rows: too few for FP8 activations to pay off, and per-token GEMVs would
+// convert the same weights once per token.  Here each 16-byte FP4 piece is
+// dequantised once per item to bf16 by the scaled FP4 converts (exact: the
+// block scale is a power of two) and multiplied on v_mfma_f32_32x32x16_bf16
+// against the bf16 activations, so the products are exact as on the batch-1
+// path.  Items are (M tile of up to 64 grouped rows of one record, 256 weight
+// rows) and run the prefill GEMM's stage pipeline; wavefront w takes M block
+// w / 2 and column half w % 2 (for gate/up, 64 gate and the same 64 up
+// columns).  A K step of the MFMA takes, per lane, 8 consecutive elements of
+// the 32 its FP4 piece covers; the activation fragment is read at the same K.
+
+constexpr int kDMT = 64;                      // grouped rows per item at most
+constexpr int kDKS = 128;                     // K per stage
+constexpr int kDThreads = 256;                // 4 wavefronts
+constexpr int kDArow = 2 * kDKS + 16;         // padded bytes of a bf16 activation row per stage
+constexpr int kDBrow = kDKS / 2 + 16;         // padded bytes of an FP4 weight row per stage
+constexpr int kDCA = 2 * kDKS / 16;           // 16-byte pieces per activation row and stage
+constexpr int kDCB = kDKS / 32;               // 16-byte pieces per weight row and stage
+constexpr int kDPiecesA = kDMT * kDCA / kDThreads;
+constexpr int kDPiecesB = kNR * kDCB / kDThreads;
+static_assert(kDPiecesA * kDThreads == kDMT * kDCA && kDPiecesB * kDThreads == kNR * kDCB,
+              "stage pieces must divide evenly over the workgroup");
+#ifndef MOE_DG_DEPTH
+#define MOE_DG_DEPTH 1
+#endif
+constexpr int kDDepth = MOE_DG_DEPTH;         // K stages held in registers ahead of the LDS stage
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+struct alignas(16) DGemmSmem {
+  uint8_t a[2][kDMT * kDArow];
+  uint8_t b[2][kNR * kDBrow];
+  uint32_t bs[2][kDThreads];  // entry i: the stage's 4 scale bytes of weight row i
+  int32_t pm[kDMT];           // down: the (token, rank) pair of each tile row
+};
+
+struct DStageRegs {
+  u32x4_t a[kDPiecesA];
+  u32x4_t b[kDPiecesB];
+  uint32_t bs;
+};
+
+struct DLoadOffs {
+  uint32_t a[kDPiecesA];  // piece p = tid + j*kDThreads: activation row p/kDCA (clamped), 16 bytes at 16*(p%kDCA)
+  uint32_t b[kDPiecesB];  // piece p = tid + j*kDThreads: weight row p/kDCB, 16 bytes at 16*(p%kDCB)
+  uint32_t bs;            // scale row of weight row tid
+};
+
+__device__ __forceinline__ void dstage_load(DStageRegs& r, const DLoadOffs& o, const uint8_t* abase,
+                                            const uint8_t* rec, int k0) {
+#pragma unroll
+  for (int j = 0; j < kDPiecesA; ++j) r.a[j] = *(const u32x4_t*)(abase + (o.a[j] + 2 * k0));
+#pragma unroll
+  for (int j = 0; j < kDPiecesB; ++j) r.b[j] = *(const u32x4_t*)(rec + (o.b[j] + k0 / 2));
+  r.bs = *(const uint32_t*)(rec + (o.bs + k0 / 32));
+}
+
+__device__ __forceinline__ void dstage_store(DGemmSmem& sm, int buf, const DStageRegs& r, int tid) {
+#pragma unroll
+  for (int j = 0; j < kDPiecesA; ++j) {
+    const int p = tid + j * kDThreads;
+    *(u32x4_t*)(sm.a[buf] + (p / kDCA) * kDArow + 16 * (p % kDCA)) = r.a[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kDPiecesB; ++j) {
+    const int p = tid + j * kDThreads;
+    *(u32x4_t*)(sm.b[buf] + (p / kDCB) * kDBrow + 16 * (p % kDCB)) = r.b[j];
+  }
+  sm.bs[buf][tid] = r.bs;
+}
+
+// LDS weight-tile block of the wavefront's column block j (0..3) in column
+// half nh: gate/up: gate blocks 2nh, 2nh+1 then the up blocks 4+2nh, 5+2nh;
+// down: blocks 4nh .. 4nh+3
+template <int NMAT>
+__device__ __forceinline__ int dcol_block(int nh, int j) {
+  return NMAT == 2 ? (j < 2 ? 2 * nh + j : 4 + 2 * nh + (j - 2)) : 4 * nh + j;
+}
+
+struct DItemCtx {
+  DLoadOffs O;
+  const uint8_t *abase, *rec;
+  int tid, c, h, mp, nh, nstage, rows, start, nt;
+};
+
+template <int NMAT, bool LIVE>
+__device__ __forceinline__ void dgemm_item(DGemmSmem& sm, const PrefillArgs& a, const DItemCtx& x) {
+  const int tid = x.tid, c = x.c, h = x.h, nstage = x.nstage;
+  v16f acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+
+  // R[j] holds stage j mod kDDepth; nstage is a multiple of kDDepth (checked
+  // at launch); the tail's loads are clamped to the last stage
+  DStageRegs R[kDDepth];
+#pragma unroll
+  for (int d = 0; d < kDDepth; ++d) dstage_load(R[d], x.O, x.abase, x.rec, d * kDKS);
+  __syncthreads();  // the previous item's last stage reads and epilogue are done
+  dstage_store(sm, 0, R[0], tid);
+  if (NMAT == 1 && tid < kDMT) sm.pm[tid] = a.perm[x.start + min(tid, x.rows - 1)];
+  dstage_load(R[0], x.O, x.abase, x.rec, min(kDDepth, nstage - 1) * kDKS);
+  __syncthreads();
+
+  const int arow = (32 * x.mp + c) * kDArow;
+  for (int s0 = 0; s0 < nstage; s0 += kDDepth) {
+#pragma unroll
+    for (int d = 0; d < kDDepth; ++d) {
+      const int s = s0 + d;
+      const int buf = (kDDepth % 2 == 0) ? (d & 1) : (s & 1);
+      if (LIVE) {
+#pragma unroll
+        for (int kc = 0; kc < kDKS / 64; ++kc) {
+          // the lane's FP4 piece of each column block: K [kc*64 + 32h, +32) of weight row c
+          u32x4_t q[4];
+          float sc[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = dcol_block<NMAT>(x.nh, j) * 32 + c;
+            q[j] = *(const u32x4_t*)(sm.b[buf] + r * kDBrow + kc * 32 + 16 * h);
+            sc[j] = e8m0_to_f32((sm.bs[buf][r] >> (8 * (2 * kc + h))) & 0xffu);
+          }
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            // K [kc*64 + 32h + 8m, +8): activations of row 32*mp + c, weights of each block's row c
+            const v8bf av = *(const v8bf*)(sm.a[buf] + arow + 2 * (kc * 64 + 32 * h + 8 * m));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              u32x4_t wv;
+              wv.x = fp4x2_to_bf16x2_scaled<0>(q[j][m], sc[j]);
+              wv.y = fp4x2_to_bf16x2_scaled<1>(q[j][m], sc[j]);
+              wv.z = fp4x2_to_bf16x2_scaled<2>(q[j][m], sc[j]);
+              wv.w = fp4x2_to_bf16x2_scaled<3>(q[j][m], sc[j]);
+              acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(v8bf, wv), acc[j], 0, 0, 0);
+            }
+          }
+        }
+      }
+      dstage_store(sm, buf ^ 1, R[(d + 1) % kDDepth], tid);
+      dstage_load(R[(d + 1) % kDDepth], x.O, x.abase, x.rec, min(s + 1 + kDDepth, nstage - 1) * kDKS);
+      __syncthreads();
+    }
+  }
+  if (!LIVE) return;
+
+  // lane indices made opaque so the epilogue's address arithmetic is not hoisted into the loop
+  int ce = c, he = h;
+  asm volatile("" : "+v"(ce), "+v"(he));
+  const int H = a.H, I = a.I;
+  const int rb = 32 * x.mp;
+  if (NMAT == 2) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int col = x.nt * (kNR / 2) + 32 * dcol_block<2>(x.nh, q) + ce;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = rb + 8 * (e / 4) + 4 * he + (e % 4);
+        if (r < x.rows) {
+          const float g = acc[q][e], u = acc[2 + q][e];
+          a.hb[(size_t)(x.start + r) * I + col] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = rb + 8 * (e / 4) + 4 * he + (e % 4);
+      if (r < x.rows) {
+        const size_t pair = (size_t)sm.pm[r];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a.yf[pair * H + (size_t)x.nt * kNR + dcol_block<1>(x.nh, j) * 32 + ce] = acc[j][e];
+      }
+    }
+  }
+}
+
+// NMAT = 2: gate/up (K = H) with SwiGLU into hb; NMAT = 1: down (K = I) into yf
+template <int NMAT>
+__global__ __launch_bounds__(kDThreads) void dgemm_kernel(PrefillArgs a) {
+  __shared__ DGemmSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31, h = lane >> 5;
+  const int mp = wave >> 1, nh = wave & 1;
+  const int H = a.H, I = a.I;
+  const int K = NMAT == 2 ? H : I;
+  const int ncol = NMAT == 2 ? I / (kNR / 2) : H / kNR;
+  const int nitems = a.items[0] * ncol;
+  const int nstage = K / kDKS;
+  const RecordLayout L = record_layout(H, I, 4);
+  const uint32_t wrowb = (uint32_t)K / 2, wrows = (uint32_t)K / 32;
+
+  for (int item = virtual_block(); item < nitems; item += gridDim.x) {
+    const int mi = item / ncol, nt = item - mi * ncol;
+    const int key = a.items[1 + 3 * mi], row0 = a.items[2 + 3 * mi], rows = a.items[3 + 3 * mi];
+    const int start = a.offsets[key] + row0;
+    const uint8_t* rec = key_record(a, key);
+    auto act_row = [&](int r) -> uint32_t {
+      r = min(r, rows - 1);
+      return NMAT == 2 ? (uint32_t)(a.perm[start + r] / a.K1) : (uint32_t)(start + r);
+    };
+    auto weight_row = [&](int wr, bool scales) -> uint32_t {
+      uint32_t n, off;
+      if (NMAT == 2) {
+        const int mat = wr / (kNR / 2);
+        n = (uint32_t)(nt * (kNR / 2) + wr % (kNR / 2));
+        off = (uint32_t)(scales ? (mat == 0 ? L.w1s : L.w3s) : (mat == 0 ? L.w1c : L.w3c));
+      } else {
+        n = (uint32_t)(nt * kNR + wr);
+        off = (uint32_t)(scales ? L.w2s : L.w2c);
+      }
+      return off + n * (scales ? wrows : wrowb);
+    };
+    DItemCtx x;
+#pragma unroll
+    for (int j = 0; j < kDPiecesA; ++j) {
+      const int p = tid + j * kDThreads;
+      x.O.a[j] = act_row(p / kDCA) * (uint32_t)(2 * K) + 16u * (p % kDCA);
+    }
+#pragma unroll
+    for (int j = 0; j < kDPiecesB; ++j) {
+      const int p = tid + j * kDThreads;
+      x.O.b[j] = weight_row(p / kDCB, false) + 16u * (p % kDCB);
+    }
+    x.O.bs = weight_row(tid, true);
+    x.abase = NMAT == 2 ? (const uint8_t*)a.xb : (const uint8_t*)a.hb;
+    x.rec = rec;
+    x.tid = tid, x.c = c, x.h = h, x.mp = mp, x.nh = nh, x.nstage = nstage;
+    x.rows = rows, x.start = start, x.nt = nt;
+    if (32 * mp < rows)
+      dgemm_item<NMAT, true>(sm, a, x);
+    else
+      dgemm_item<NMAT, false>(sm, a, x);
+  }
+}
+
 // out[t] = sum_{r<k} w[t][r] * y[t][r] (+ y[t][k]), y bf16, rank order, one rounding
 __global__ __launch_bounds__(256) void combine_bf16y_kernel(const uint16_t* __restrict__ y, const float* __restrict__ w,
                                                             int T, int k, int K1, int H, uint16_t* __restrict__ out) {
@@ -589,6 +836,9 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
   a.hq = (uint8_t*)(ws + lay.hq);
   a.hs = (uint8_t*)(ws + lay.hs);
   a.y = (uint16_t*)(ws + lay.y);
+  a.xb = nullptr;
+  a.hb = nullptr;
+  a.yf = nullptr;
 
   if ((H / kKS) % kDepth != 0 || (I / kKS) % kDepth != 0)
     return fail(MOE_ESHAPE, "moe_prefill_forward: H=%d and I=%d must be multiples of %d", H, I, kKS * kDepth);
@@ -601,7 +851,7 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
   st = launch_group(a.keys, P, E + 1, a.counts, a.offsets, a.perm, s);
   if (st != MOE_OK) return st;
   {
-    launch(MOE_PROF_PLAN, prefill_items_kernel, dim3(1), dim3(64), 0, s, a.counts, E + 1, a.items);
+    launch(MOE_PROF_PLAN, prefill_items_kernel<kMT>, dim3(1), dim3(64), 0, s, a.counts, E + 1, a.items);
     MOE_LAUNCH_CHECK();
   }
   // persistent grids, one workgroup per CU (each wavefront holds a SIMD's 512
@@ -625,5 +875,65 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
   }
   return MOE_OK;
 }
+
+bool decode_mfma_ok(int H, int I) {
+  return H >= 256 && I >= 128 && H % 256 == 0 && I % 128 == 0 && (H / kDKS) % kDDepth == 0 &&
+         (I / kDKS) % kDDepth == 0;
+}
+
+// Grouped decode of T >= 2 bf16 tokens on bf16 MFMA: plan (keys by slot, the
+// shared expert last; stable grouping; M tiles of up to 64 rows), gate/up
+// with SwiGLU into h (bf16, grouped order), down into y (fp32, [T][K1][H]),
+// then the rank-ordered combine.  plan: keys [P] | counts [4096] |
+// offsets [4097] | perm [P] | items.
+moe_status launch_decode_mfma(const moe_layer* Lr, const void* x, int T, int k, const int32_t* slot_ids, const float* w,
+                              void* out, uint16_t* h, float* y, int32_t* plan, hipStream_t s) {
+  const int K1 = k + (Lr->shared ? 1 : 0);
+  const int H = Lr->H, I = Lr->I, E = Lr->num_slots;
+  const int P = T * K1;
+  PrefillArgs a;
+  a.T = T, a.H = H, a.I = I, a.k = k, a.K1 = K1, a.E = E;
+  a.bank = Lr->fp4_base;
+  a.stride = Lr->fp4_stride;
+  a.shared = Lr->shared;
+  a.ids = slot_ids;
+  a.xq = nullptr;
+  a.xs = nullptr;
+  a.keys = plan;
+  a.counts = a.keys + P;
+  a.offsets = a.counts + kMaxKeys;
+  a.perm = a.offsets + kMaxKeys + 1;
+  a.items = a.perm + P;
+  a.hq = nullptr;
+  a.hs = nullptr;
+  a.y = nullptr;
+  a.xb = (const uint16_t*)x;
+  a.hb = h;
+  a.yf = y;
+  {
+    launch(MOE_PROF_PLAN, prefill_keys_kernel, dim3((P + 255) / 256), dim3(256), 0, s, a);
+    MOE_LAUNCH_CHECK();
+  }
+  moe_status st = launch_group(a.keys, P, E + 1, a.counts, a.offsets, a.perm, s);
+  if (st != MOE_OK) return st;
+  {
+    launch(MOE_PROF_PLAN, prefill_items_kernel<kDMT>, dim3(1), dim3(64), 0, s, a.counts, E + 1, a.items);
+    MOE_LAUNCH_CHECK();
+  }
+  const long max_items_m = (long)P / kDMT + std::min(P, E + 1) + 1;
+  const int grid_gu = (int)std::min<long>(max_items_m * (I / (kNR / 2)), 256L) / 8 * 8;
+  const int grid_dn = (int)std::min<long>(max_items_m * (H / kNR), 256L) / 8 * 8;
+  {
+    launch(MOE_PROF_GATEUP, dgemm_kernel<2>, dim3(std::max(grid_gu, 8)), dim3(kDThreads), 0, s, a);
+    MOE_LAUNCH_CHECK();
+  }
+  {
+    launch(MOE_PROF_DOWN, dgemm_kernel<1>, dim3(std::max(grid_dn, 8)), dim3(kDThreads), 0, s, a);
+    MOE_LAUNCH_CHECK();
+  }
+  return launch_combine(y, w, nullptr, T, k, H, Lr->shared ? 1 : 0, out, MOE_BF16, s);
+}
+
+size_t decode_mfma_plan_ints(int P) { return (size_t)P * 2 + kMaxKeys + (kMaxKeys + 1) + 1 + 3 * ((size_t)P / kDMT + kMaxKeys + 2); }
 
 }  // namespace moe

@@ -537,3 +537,85 @@ def test_layer_decode_graph_replays(gpu_lib):
         gpu_lib.moe_layer_decode(desc, lg[rep], xs[rep:rep + 1], k, ids[rep], w[rep], scratch, ws)
         torch.cuda.synchronize()
         assert torch.equal(scratch, ref[rep:rep + 1]), rep
+
+
+# ------------------------------------------------- batched decode on bf16 MFMA
+
+def _batched_bf16_case(gpu_lib, T, E, k, with_shared, seed, H=512, I=256, bad_slots=0, sample=None):
+    """bf16 tokens, all-FP4 ranks, weighted bf16 output: the grouped bf16 MFMA
+    path (weights dequantised to bf16 in registers).  Invalid slot ids count
+    as dropped ranks.  Compared per token against the oracle's expert MLPs."""
+    torch = _torch()
+    bank = W.fp4_bank(seed, 1, E, H, I)
+    shared = W.fp4_record(seed, 2, 0, H, I) if with_shared else None
+    layer = Layer(gpu_lib, bank, shared, H, I)
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    for _ in range(bad_slots):
+        ids[rng.integers(T), rng.integers(k)] = rng.choice([-1, E, E + 5])
+    w = rng.random((T, k)).astype(np.float32)
+    xb = W.bf16_normal(seed, (3,), (T, H))
+    x64 = O.bf16_bits_to_f64(xb)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    layer.forward(bf16_dev(xb), T, k, dev(ids), None, dev(w), out)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    tokens = range(T) if sample is None else sample
+    cache = {}
+
+    def ew(key):
+        if key not in cache:
+            cache[key] = O.expert_weights(shared if key == -2 else bank[key], H, I)
+        return cache[key]
+
+    for t in tokens:
+        ref = np.zeros(H)
+        for r in range(k):
+            e = int(ids[t, r])
+            if 0 <= e < E:
+                ref += w[t, r] * O.expert_mlp(x64[t], *ew(e))
+        if with_shared:
+            ref += O.expert_mlp(x64[t], *ew(-2))
+        err = max_rel(got[t], ref)
+        assert err <= TOL_BF16_MAX_REL, (t, err)
+    log(f"batched bf16 MFMA T={T} E={E} k={k} shared={with_shared}: ok over {len(list(tokens))} tokens")
+
+
+@pytest.mark.parametrize("T,E,k,with_shared,bad", [
+    (2, 16, 4, True, 0),      # groups of one or two rows
+    (37, 16, 4, True, 3),     # ragged groups, dropped ranks
+    (70, 4, 3, True, 0),      # groups past 64 rows (two M tiles each), shared 70 rows
+    (130, 2, 2, False, 0),    # no shared expert, three M tiles per group
+])
+def test_batched_bf16_mfma_path(gpu_lib, T, E, k, with_shared, bad):
+    _batched_bf16_case(gpu_lib, T, E, k, with_shared, seed=300 + T, bad_slots=bad)
+
+
+def test_layer_decode_b64_full_size(gpu_lib):
+    """The batch-64 decode shape (256 experts + shared, H 4096, I 2048, top-6,
+    Zipf-skewed routing) in the launch configuration the benchmark times;
+    outputs compared on a seeded sample of tokens."""
+    torch = _torch()
+    cfg = W.CONFIGS[2]
+    seed = W.config_seed(2)
+    E, H, I, k, T = cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"]
+    d = W.make_layer_inputs(cfg, seed, 0)
+    bank, shared = d["bank"], d["shared_rec"]
+    layer = Layer(gpu_lib, bank, shared, H, I)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    gpu_lib.moe_route(dev(d["logits"]), k, ids, w)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    layer.forward(bf16_dev(d["x"]), T, k, ids, None, w, out)
+    torch.cuda.synchronize()
+    oids, ow = O.route(d["logits"], k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    x64 = O.bf16_bits_to_f64(d["x"])
+    got = to_f64(out)
+    rng = np.random.default_rng(44)
+    for t in sorted(rng.choice(T, 3, replace=False).tolist()):
+        ys = [O.expert_mlp(x64[t], *O.expert_weights(bank[int(e)], H, I)) for e in oids[t]]
+        ref = O.combine(np.stack(ys), ow[t], O.expert_mlp(x64[t], *O.expert_weights(shared, H, I)))
+        err = max_rel(got[t], ref)
+        log(f"b64 token {t}: max-rel {err:.3e}")
+        assert err <= TOL_BF16_MAX_REL
