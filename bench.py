@@ -52,18 +52,21 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_hash() -> str:
+def kernel_hash(files=("decode_b1.hip", "route_dev.h", "common.h")) -> str:
     h = hashlib.sha256()
-    for f in ("decode_b1.hip", "route_dev.h", "common.h"):
+    for f in files:
         with open(os.path.join(ROOT, "mxfp4_routed_expert_renorm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(khash: str):
+B64_KERNEL_FILES = ("prefill.hip", "common.h")
+
+
+def traffic_from_profiles(khash: str, record: str = "traffic_gateup_decode_b1.json"):
     """HBM bytes per launch of the gate/up kernel from committed counter runs,
     or None when absent or taken on a different kernel source."""
-    p = os.path.join(ROOT, "profiles", "traffic_gateup_decode_b1.json")
+    p = os.path.join(ROOT, "profiles", record)
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -134,6 +137,17 @@ def resident_bank(W, lib, torch, cfg, seed, dev):
     return bank, shared, rec_bytes
 
 
+def calibration_copy(torch, dev):
+    """One 256 MiB device-to-device copy: the reference launch that scales the
+    FETCH_SIZE / WRITE_SIZE counters of the same profiling run to bytes."""
+    src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def bench_decode_b1(args):
 
     import torch
@@ -170,12 +184,7 @@ def bench_decode_b1(args):
         lib.moe_layer_decode(layer, lg_d[s], x_d[s:s + 1], k, ids_d[s], w_d[s], out_d[s:s + 1], ws)
 
     if args.calibrate_copy:
-        src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(torch, dev)
 
     step(0)
     torch.cuda.synchronize()
@@ -316,6 +325,9 @@ def bench_decode_b64(args):
         lib.moe_route(lg_d[s], k, ids_d[s], w_d[s])
         lib.moe_expert_forward(layer, x_d[s], T, k, ids_d[s], None, w_d[s], out_d[s], ws)
 
+    if args.calibrate_copy:
+        calibration_copy(torch, dev)
+
     step(0)
     torch.cuda.synchronize()
     elapsed = run_steps(args, torch, step, K, Wm)
@@ -338,9 +350,26 @@ def bench_decode_b64(args):
                    "expert_intermediate": I, "top_k": k, "tokens_per_step": T, "launch": args.mode,
                    "distinct_experts_per_step_mean": round(float(distinct.mean()), 2)},
         "step_hbm_GBps": round(gbps, 1), "step_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "roofline": b64_roofline(prof, distinct, T, k, H, I),
         "kernel_avg_us": {n: round(v[0] / v[1] * 1e3, 3) for n, v in prof.items()},
     }
     print(json.dumps(result), flush=True)
+
+
+def b64_roofline(prof, distinct, T, k, H, I):
+    """Gate/up kernel of the batched decode: every selected record's w1 and w3
+    (codes and scales) once, the tokens' activations once, h written once."""
+    gu_unit = 2 * (H * I // 2 + H * I // 32)
+    P = T * (k + 1)
+    alg = float((distinct + 1).mean()) * gu_unit + T * H * 2 + P * I * 2
+    us = prof["gateup"][0] / prof["gateup"][1] * 1e3
+    achieved = alg / (us * 1e-6) / 1e9
+    khash = kernel_hash(B64_KERNEL_FILES)
+    return {"bound": "hbm", "kernel": "dgemm_kernel<2> (batched gate/up on bf16 MFMA + SwiGLU)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_profiles(khash, "traffic_gateup_decode_b64.json"),
+            "algorithmic_bytes_per_launch": int(alg), "avg_launch_us": round(us, 3), "kernel_hash": khash}
 
 
 def bench_prefill(args):

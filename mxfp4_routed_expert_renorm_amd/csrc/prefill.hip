@@ -539,6 +539,9 @@ static_assert(kDPiecesA * kDThreads == kDMT * kDCA && kDPiecesB * kDThreads == k
 #define MOE_DG_DEPTH 1
 #endif
 constexpr int kDDepth = MOE_DG_DEPTH;         // K stages held in registers ahead of the LDS stage
+#ifndef MOE_DG_PER_CU
+#define MOE_DG_PER_CU 1  // workgroups per CU (two fit, but measured slower)
+#endif
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
@@ -921,8 +924,9 @@ moe_status launch_decode_mfma(const moe_layer* Lr, const void* x, int T, int k, 
     MOE_LAUNCH_CHECK();
   }
   const long max_items_m = (long)P / kDMT + std::min(P, E + 1) + 1;
-  const int grid_gu = (int)std::min<long>(max_items_m * (I / (kNR / 2)), 256L) / 8 * 8;
-  const int grid_dn = (int)std::min<long>(max_items_m * (H / kNR), 256L) / 8 * 8;
+  const long slots = 256L * MOE_DG_PER_CU;  // workgroups resident at once
+  const int grid_gu = (int)std::min<long>(max_items_m * (I / (kNR / 2)), slots) / 8 * 8;
+  const int grid_dn = (int)std::min<long>(max_items_m * (H / kNR), slots) / 8 * 8;
   {
     launch(MOE_PROF_GATEUP, dgemm_kernel<2>, dim3(std::max(grid_gu, 8)), dim3(kDThreads), 0, s, a);
     MOE_LAUNCH_CHECK();
