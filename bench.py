@@ -76,9 +76,29 @@ def traffic_from_profiles(khash: str, record: str = "traffic_gateup_decode_b1.js
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(min_seconds: float):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """Host threads this process may use, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(min_seconds: float, threads: int = 1):
     """The oracle as it stands, on whole tokens of the same workload, until at
-    least min_seconds of CPU work; BLAS pinned to one thread."""
+    least min_seconds of CPU work; BLAS limited to `threads` threads."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -89,7 +109,7 @@ def cpu_baseline(min_seconds: float):
     seed = W.config_seed(CFG_INDEX)
     H, I, k = cfg["H"], cfg["I"], cfg["k"]
     toks, t_used = 0, 0.0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         while t_used < min_seconds or toks == 0:
             d = W.make_layer_inputs(cfg, seed, step=toks, with_bank=False)
             lg = d["logits"]
@@ -103,10 +123,51 @@ def cpu_baseline(min_seconds: float):
             O.round_to_bf16(out)
             t_used += time.perf_counter() - t0
             toks += 1
-    return {"value": toks / t_used, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": toks / t_used, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{toks} token(s) of the batch-1 decode workload (route + 9 experts dequantised "
-                      f"and evaluated in float64 + combine), BLAS limited to one thread; "
+                      f"and evaluated in float64 + combine), BLAS limited to {threads} thread(s); "
                       f"input generation excluded; {t_used:.1f} s"}
+
+
+def step_latency(torch, step, steps, flush_bytes=1 << 30):
+    """Per-step latency with HIP events on the launch stream, eager: "steady"
+    back to back, and "cold" with an untimed 1 GiB write before every step,
+    which leaves none of the step's weights in the 256 MB MALL."""
+    import numpy as np
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, flush in (("steady", False), ("cold", True)):
+        evs = []
+        for s in steps:
+            if flush:
+                scratch.fill_(s & 0xff)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step(s)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+        out[name] = {"p10": round(float(np.percentile(us, 10)), 3), "median": round(float(np.median(us)), 3),
+                     "p90": round(float(np.percentile(us, 90)), 3), "n": len(us)}
+    del scratch
+    return out
+
+
+def measured_read_peak(torch, lib, gib=4, reps=5):
+    """GB/s of the library's streaming-read reference over a 4 GiB buffer."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lib.moe_debug_stream_read(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        lib.moe_debug_stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = reps * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    return round(gbps, 1)
 
 
 def main():
@@ -241,9 +302,18 @@ def bench_decode_b1(args):
                      "kernel_hash": khash},
         "kernel_avg_us": per_kernel,
     }
+    result["step_latency_us"] = step_latency(torch, step, range(Wm, nsteps))
+    peak_m = measured_read_peak(torch, lib)
+    result["hbm_read_peak_measured_GBps"] = peak_m
+    result["roofline"]["frac_vs_measured_peak"] = round(achieved / peak_m, 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        cb = cpu_baseline(args.cpu_seconds)
+        n = host_threads()
+        allc = cpu_baseline(args.cpu_seconds, n)
+        cb["all_cores"] = {"value": allc["value"], "cores": n, "sample": allc["sample"]}
+        cb["cpu_model"] = cpu_model()
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
 
@@ -430,6 +500,7 @@ def bench_prefill(args):
                      "flops_per_step": flops, "traffic": None},
         "weight_bytes_per_step": wbytes,
         "gemm_weight_GBps": round(wbytes / gemm_s / 1e9, 1),
+        "gemm_weight_hbm_frac": round(wbytes / gemm_s / 1e9 / HBM_PEAK_GBPS, 4),
         "kernel_avg_us": kus,
     }
     print(json.dumps(result), flush=True)

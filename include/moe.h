@@ -185,6 +185,14 @@ moe_status moe_combine(const float* y, const float* w, const int8_t* prec, int T
 moe_status moe_debug_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out,
                              moe_stream_t stream);
 
+/* Streaming-read reference for measurements: reads `bytes` bytes of `buf`
+ * (device, 16-byte aligned, bytes a multiple of 16) once with non-temporal
+ * 16-byte loads and writes nothing (`sink`, one device uint32, is stored only
+ * under a condition the data cannot meet).  Its duration gives the measured
+ * HBM read peak that the kernels' achieved bandwidth is compared with, beside
+ * the 8 TB/s datasheet figure. */
+moe_status moe_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, moe_stream_t stream);
+
 /* ------------------------------------------------------------ prefill */
 
 /* MXFP8 quantisation of a bf16 matrix along its rows: one E8M0 scale per 32
@@ -296,6 +304,7 @@ typedef enum {
   MOE_PROF_GEMM_GATEUP = 8, /* prefill grouped GEMM, gate/up */
   MOE_PROF_GEMM_DOWN = 9,   /* prefill grouped GEMM, down */
   MOE_PROF_DEQUANT = 10,
+  MOE_PROF_READ = 11,       /* streaming-read reference */
   MOE_PROF_KINDS = 16
 } moe_prof_kind;
 

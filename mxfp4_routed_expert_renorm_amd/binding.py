@@ -68,6 +68,7 @@ _SIGS = {
                                  c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "moe_combine": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p]),
     "moe_debug_dequant": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
+    "moe_debug_stream_read": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "moe_quant_mxfp8": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "moe_prefill_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "moe_prefill_forward": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_int, c_void_p, c_void_p,
@@ -219,6 +220,11 @@ def moe_debug_dequant(record, H, I, prec, matrix, out, stream=None):
     return out
 
 
+def moe_debug_stream_read(buf, sink, stream=None):
+    """Read every byte of the uint8 device tensor `buf` once (measurement reference)."""
+    _check("moe_debug_stream_read", load().moe_debug_stream_read(_p(buf), buf.numel(), _p(sink), _stream(stream)))
+
+
 # -------------------------------------------------------------------- prefill
 
 def moe_quant_mxfp8(x, codes, scales, stream=None):
@@ -333,7 +339,7 @@ class Cache:
 # --------------------------------------------------------------------- timing
 
 PROF_KINDS = ("route", "router_logits", "gateup", "down", "combine", "group", "plan", "quant",
-              "gemm_gateup", "gemm_down", "dequant")
+              "gemm_gateup", "gemm_down", "dequant", "read")
 MOE_PROF_KINDS = 16
 
 

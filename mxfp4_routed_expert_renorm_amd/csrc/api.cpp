@@ -40,6 +40,7 @@ moe_status launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
 moe_status launch_router_logits(const void* x, moe_dtype xt, const float* wr, int T, int E, int H, float* logits,
                                 hipStream_t s);
 moe_status launch_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out, hipStream_t s);
+moe_status launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 bool decode_shape_ok(int H, int I);
 size_t prefill_workspace_bytes(int H, int I, int T, int k, int has_shared);
 moe_status launch_quant_mxfp8(const void* x, long rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s);
@@ -260,6 +261,14 @@ moe_status moe_debug_dequant(const uint8_t* record, int H, int I, int prec, int 
   REQUIRE(record && out, MOE_EINVAL, "moe_debug_dequant: NULL pointer");
   REQUIRE(aligned(record, 4), MOE_EINVAL, "moe_debug_dequant: record must be 4-byte aligned");
   return launch_dequant(record, H, I, prec, matrix, out, (hipStream_t)stream);
+}
+
+moe_status moe_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, moe_stream_t stream) {
+  REQUIRE(buf && sink, MOE_EINVAL, "moe_debug_stream_read: NULL pointer");
+  REQUIRE(aligned(buf, 16) && bytes % 16 == 0, MOE_EINVAL,
+          "moe_debug_stream_read: buf must be 16-byte aligned and bytes a multiple of 16");
+  if (bytes == 0) return MOE_OK;
+  return launch_stream_read(buf, bytes, sink, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -2,6 +2,8 @@
 // steps the expert kernels use: the gfx950 scaled FP4 convert (scale 1.0)
 // times the E8M0 block scale, or the 2-bit level (code - 1.5) times the E4M3
 // block scale.  Lets the formats be checked bit for bit against the oracle.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -43,6 +45,28 @@ moe_status launch_dequant(const uint8_t* record, int H, int I, int prec, int mat
   const long ndw = (long)rows * cols / (32 / bits);
   launch(MOE_PROF_DEQUANT, dequant_kernel, dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0, s, record + coff[matrix],
                      record + soff[matrix], rows, cols, bits, out);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+namespace {
+
+// grid-stride read of the buffer with non-temporal 16-byte loads; the sum is
+// stored only under a condition the data cannot meet, so nothing is written
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* __restrict__ buf, long n16,
+                                                          uint32_t* __restrict__ sink) {
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n16; i += (long)gridDim.x * 256)
+    acc += __builtin_nontemporal_load((const u32x4_t*)buf + i);
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u && acc.x == 0x7f4a7c15u) sink[0] = acc.y;
+}
+
+}  // namespace
+
+moe_status launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const long n16 = (long)(bytes / 16);
+  const long grid = std::min<long>(std::max<long>((n16 + 255) / 256, 1), 2048);
+  launch(MOE_PROF_READ, stream_read_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const uint8_t*)buf, n16, sink);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

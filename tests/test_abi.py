@@ -132,3 +132,12 @@ def test_last_error_is_thread_local(lib):
     assert seen["before"] == ""
     assert "E=2000" in seen["after"]
     assert lib.moe_last_error().decode() == main_msg
+
+
+def test_stream_read_validation(lib):
+    import ctypes
+    n = ctypes.c_size_t
+    assert lib.moe_debug_stream_read(None, n(16), None, None) == 1                            # MOE_EINVAL: NULL
+    assert lib.moe_debug_stream_read(ctypes.c_void_p(8), n(16), ctypes.c_void_p(64), None) == 1   # misaligned
+    assert lib.moe_debug_stream_read(ctypes.c_void_p(64), n(17), ctypes.c_void_p(64), None) == 1  # not a multiple of 16
+    assert lib.moe_debug_stream_read(ctypes.c_void_p(64), n(0), ctypes.c_void_p(64), None) == 0   # nothing to read
