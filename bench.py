@@ -45,6 +45,9 @@ def parse():
                          "prefill: 4096 tokens, top-8, MXFP8 x MXFP4 scaled MFMA; "
                          "slotcache: 512 tokens x 8 layers through the 512-slot cache with the (2,4) ladder")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--slot-tier", action="store_true",
+                    help="slotcache workload with a 100-slot 2-bit device tier and LFU eviction "
+                         "(decay 0.95, counts seeded from a separate 64-token routing trace)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (known bytes for HBM counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -533,7 +536,19 @@ def bench_slotcache(args):
         if p % 256 == 255:
             print(f"[bench] {p + 1}/{L * E} host records", file=sys.stderr, flush=True)
     arena = torch.empty(S * rb4, dtype=torch.uint8, device=dev)
-    staging = torch.empty((b - a) * rb2, dtype=torch.uint8, device=dev)
+    tier = {}
+    if args.slot_tier:
+        # LFU counts seeded from the picks of a separate 64-token trace, routed by the library
+        warm = torch.from_numpy(W.slotcache_logits(seed + 1, L, E, 64, cfg["zipf"]).reshape(64 * L, E)).to(dev)
+        wids_d = torch.empty((64 * L, k), dtype=torch.int32, device=dev)
+        ww_d = torch.empty((64 * L, k), dtype=torch.float32, device=dev)
+        lib.moe_route(warm, k, wids_d, ww_d)
+        wids = wids_d.cpu().numpy().reshape(64, L, k)
+        counts = np.zeros(L * E, np.float32)
+        for l in range(L):
+            np.add.at(counts, l * E + wids[:, l].reshape(-1), 1.0)
+        tier = {"int2_slots": 100, "policy": "lfu", "lfu_decay": 0.95, "lfu_seed": counts}
+    staging = torch.empty(tier.get("int2_slots", b - a) * rb2, dtype=torch.uint8, device=dev)
     logits = W.slotcache_logits(seed, L, E, T, cfg["zipf"]).reshape(T * L, E)
     lg_d = torch.from_numpy(logits).to(dev)
     xs = np.stack([W.slotcache_x(seed, t, l, H)[0] for t in range(T) for l in range(L)])
@@ -557,7 +572,7 @@ def bench_slotcache(args):
     print(f"[bench] setup {time.time() - t0:.1f} s; pinned copy rate {h2d_peak:.1f} GB/s",
           file=sys.stderr, flush=True)
 
-    cache = lib.Cache(L, E, H, I, S, k, a, b, 1, fp4_host, int2_host, arena, staging)
+    cache = lib.Cache(L, E, H, I, S, k, a, b, 1, fp4_host, int2_host, arena, staging, **tier)
     layer = cache.layer()
     t_tok = []
     torch.cuda.synchronize()
@@ -581,8 +596,11 @@ def bench_slotcache(args):
         "ms_per_step": round(elapsed / T * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp4+int2-w/bf16-x/f32-acc",
         "data": "synthetic (seeded; per-layer Zipf(1.1) logits, fresh activations per token and layer)",
-        "config": {"workload": cfg["name"], "layers": L, "experts": E, "slots": S, "top_k": k, "ladder": [a, b],
-                   "tokens": T, "cold_start": True},
+        "config": {"workload": cfg["name"] + ("-int2tier100-lfu" if tier else ""), "layers": L, "experts": E,
+                   "slots": S, "top_k": k, "ladder": [a, b], "tokens": T, "cold_start": True,
+                   "int2_slots": tier.get("int2_slots", 0), "policy": tier.get("policy", "lru"),
+                   "lfu_decay": tier.get("lfu_decay"),
+                   "lfu_seed": "64-token routing trace of a separate seed" if tier else None},
         "steady_state_ms_per_token": round(steady * 1e3, 4),
         "cache": {**st, "hit_rate": round(st["hits"] / uses, 4)},
         "h2d_GBps": round(st["bytes_h2d"] / elapsed / 1e9, 2),

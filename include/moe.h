@@ -245,16 +245,31 @@ typedef struct {
   const uint8_t* fp4_host;   /* host pinned: L*E FP4 records, pair l*E+e at (l*E+e)*moe_fp4_expert_bytes */
   const uint8_t* int2_host;  /* host pinned: L*E 2-bit records (NULL if a == b) */
   uint8_t* fp4_arena;        /* device: num_slots FP4 records (NULL: host-only planning) */
-  uint8_t* int2_staging;     /* device: max_tokens*(b-a) 2-bit records (NULL if a == b) */
+  uint8_t* int2_staging;     /* device: 2-bit records (NULL if a == b): max_tokens*(b-a) staging entries when
+                                int2_slots == 0, else the int2_slots slots of the 2-bit tier */
+  /* Optional tiers and eviction rule ([P2] §Rig, model & methodology, best configuration: a
+   * small device tier of 2-bit copies beside the FP4 slots, LFU with frequency decay seeded
+   * from a routing trace).  All zero = the plain LRU cache with 2-bit copies staged per use. */
+  int int2_slots;            /* > 0: 2-bit copies cached in this many device slots (>= max_tokens*(b-a)) */
+  int policy;                /* MOE_CACHE_LRU or MOE_CACHE_LFU: eviction rule of both tiers */
+  double lfu_decay;          /* LFU: every pair's use count is multiplied by this at each call, 0 < d <= 1 */
+  const float* lfu_seed;     /* LFU: host [L*E] initial use counts (e.g. a routing trace's), NULL = zeros */
 } moe_cache_desc;
+
+enum { MOE_CACHE_LRU = 0, MOE_CACHE_LFU = 1 };
 
 typedef struct {
   int64_t calls, hits, misses, int2_uses, drops, bytes_h2d, evictions;
+  int64_t int2_hits;         /* 2-bit uses served from the 2-bit tier without a copy */
 } moe_cache_stats;
 
-/* Validates the descriptor (slot floor num_slots >= E: [P1] §Step 7, "moe_cache_size
- * ... too small: need at least num_experts"), allocates host bookkeeping only; the
- * cache starts cold.  The caller keeps every buffer alive until moe_cache_destroy. */
+/* Validates the descriptor (slot floor num_slots >= E: [P1] §Step 7 fails early when the
+ * cache has fewer slots than experts), allocates host bookkeeping only; the cache starts
+ * cold.  The caller keeps every buffer alive until moe_cache_destroy.
+ * Eviction: the lowest-index empty slot, else among the slots this call has not used, LRU:
+ * the oldest use; LFU: the pair with the lowest use count (ties: the oldest use).  LFU counts
+ * belong to (layer, expert) pairs and survive eviction; each call first multiplies every
+ * count by lfu_decay, and every use of a pair (hit or fetch, either tier) adds one. */
 moe_status moe_cache_create(const moe_cache_desc* desc, moe_cache** out);
 moe_status moe_cache_destroy(moe_cache* c);
 /* Back to the cold state (empty slots, clock 0, zero stats). */

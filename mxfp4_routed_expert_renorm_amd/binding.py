@@ -42,14 +42,18 @@ class moe_cache_desc(ctypes.Structure):
         ("max_tokens", c_int),
         ("fp4_host", c_void_p), ("int2_host", c_void_p),
         ("fp4_arena", c_void_p), ("int2_staging", c_void_p),
+        ("int2_slots", c_int), ("policy", c_int), ("lfu_decay", ctypes.c_double), ("lfu_seed", c_void_p),
     ]
+
+
+MOE_CACHE_LRU, MOE_CACHE_LFU = 0, 1
 
 
 class moe_cache_stats(ctypes.Structure):
     _fields_ = [
         ("calls", ctypes.c_int64), ("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
         ("int2_uses", ctypes.c_int64), ("drops", ctypes.c_int64),
-        ("bytes_h2d", ctypes.c_int64), ("evictions", ctypes.c_int64),
+        ("bytes_h2d", ctypes.c_int64), ("evictions", ctypes.c_int64), ("int2_hits", ctypes.c_int64),
     ]
 
 
@@ -284,9 +288,14 @@ class Cache:
     caller; the handle keeps references to them, so they outlive it."""
 
     def __init__(self, L, E, H, I, num_slots, k, a, b, max_tokens=1, fp4_host=None, int2_host=None,
-                 fp4_arena=None, int2_staging=None):
+                 fp4_arena=None, int2_staging=None, int2_slots=0, policy="lru", lfu_decay=1.0, lfu_seed=None):
+        """lfu_seed: host float32 array [L*E] of initial use counts (copied), or None."""
+        import numpy as np
+        seed = None if lfu_seed is None else np.ascontiguousarray(lfu_seed, dtype=np.float32).reshape(-1)
         d = moe_cache_desc(L, E, H, I, num_slots, k, a, b, max_tokens, _addr(fp4_host), _addr(int2_host),
-                           _addr(fp4_arena), _addr(int2_staging))
+                           _addr(fp4_arena), _addr(int2_staging), int2_slots,
+                           {"lru": MOE_CACHE_LRU, "lfu": MOE_CACHE_LFU}[policy], lfu_decay,
+                           None if seed is None else seed.ctypes.data)
         h = c_void_p()
         _check("moe_cache_create", load().moe_cache_create(ctypes.byref(d), ctypes.byref(h)))
         self.h, self.L, self.E, self.k = h, L, E, k

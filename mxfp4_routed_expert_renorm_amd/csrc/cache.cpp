@@ -11,15 +11,24 @@
 // otherwise, and the survivors' weights are renormalised; §43 graphs, 43
 // syncs: one host sync per layer reads the router's picks.
 //
+// "An elephant through a straw", §Rig, model & methodology (best
+// configuration): a small device tier for the 2-bit copies beside the FP4
+// slots, and LFU eviction with frequency decay seeded from a routing trace.
+//
 // Policy details the pages leave open (same as the oracle): residency is read
-// once per token before its fetches; slots used anywhere in the call are
-// protected from eviction for the rest of the call; fetches go in rank order;
-// a global clock stamps every hit and fetch; the victim is the lowest-index
-// empty slot, else the unprotected slot with the oldest stamp; 2-bit copies
-// are not cached but copied per use into a staging area at index
-// t*(b-a) + (rank-a-1).
+// once per token before its fetches, and only FP4 residency classifies; slots
+// used anywhere in the call are protected from eviction for the rest of the
+// call (in each tier); fetches go in rank order; a global clock stamps every
+// use; the victim is the lowest-index empty slot, else the unprotected slot
+// with the oldest stamp (LRU) or whose pair has the lowest use count, ties to
+// the oldest stamp (LFU).  LFU counts belong to pairs: each call multiplies
+// them all by the decay, each use adds one (double precision, the same
+// operations in the same order as the oracle, so victims match exactly).
+// Without a 2-bit tier, 2-bit copies are copied per use into a staging area
+// at index t*(b-a) + (rank-a-1).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 #include <vector>
 
@@ -31,13 +40,16 @@ struct moe_cache {
   std::vector<int32_t> map;      // (layer, expert) -> slot or -1
   std::vector<int32_t> owner;    // slot -> pair or -1
   std::vector<int64_t> stamp;    // 0 = empty
+  std::vector<int32_t> map2, owner2;  // the 2-bit tier, as map / owner
+  std::vector<int64_t> stamp2;
+  std::vector<double> count, seed;    // LFU use counts per pair, and their initial values
   int64_t clock = 0;
   moe_cache_stats st{};
   // per-call scratch
   std::vector<int32_t> ids_h, slots_h;
   std::vector<int8_t> prec_h;
   std::vector<float> w_h, wout_h;
-  std::vector<uint8_t> prot;
+  std::vector<uint8_t> prot, prot2;
   struct Copy {
     int kind;  // 0 FP4, 1 2-bit
     int pair, dest;
@@ -57,6 +69,33 @@ namespace {
 size_t pin_in_bytes(const moe_cache_desc& d) { return (size_t)d.max_tokens * d.k * 8; }
 size_t pin_out_bytes(const moe_cache_desc& d) { return (size_t)d.max_tokens * d.k * 9; }
 
+// the lowest-index empty slot not used by this call, else the unprotected slot
+// to evict under the cache's rule; -1 when every slot is protected
+int victim(const moe_cache* c, const std::vector<int32_t>& owner, const std::vector<int64_t>& stamp,
+           const std::vector<uint8_t>& prot) {
+  const int n = (int)owner.size();
+  for (int s = 0; s < n; ++s)
+    if (owner[s] < 0 && !prot[s]) return s;
+  int v = -1;
+  for (int s = 0; s < n; ++s) {
+    if (prot[s]) continue;
+    if (v < 0) {
+      v = s;
+    } else if (c->d.policy == MOE_CACHE_LFU) {
+      const double cs = c->count[owner[s]], cv = c->count[owner[v]];
+      if (cs < cv || (cs == cv && stamp[s] < stamp[v])) v = s;
+    } else if (stamp[s] < stamp[v]) {
+      v = s;
+    }
+  }
+  return v;
+}
+
+int64_t use(moe_cache* c, int pair) {
+  c->count[pair] += 1.0;
+  return ++c->clock;
+}
+
 // one call of the policy on host arrays; fills c->slots_h, prec_h, wout_h, copies
 moe_status plan(moe_cache* c, int layer, int T, const int32_t* ids, const float* w) {
   const moe_cache_desc& d = c->d;
@@ -66,6 +105,7 @@ moe_status plan(moe_cache* c, int layer, int T, const int32_t* ids, const float*
   c->wout_h.assign((size_t)T * k, 0.0f);
   c->copies.clear();
   c->prot.assign(S, 0);
+  c->prot2.assign(c->owner2.size(), 0);
   // validate everything before the state changes
   for (int i = 0; i < T * k; ++i)
     if (ids[i] < 0 || ids[i] >= E)
@@ -75,6 +115,8 @@ moe_status plan(moe_cache* c, int layer, int T, const int32_t* ids, const float*
       for (int q = 0; q < r; ++q)
         if (ids[(size_t)t * k + q] == ids[(size_t)t * k + r])
           return fail(MOE_EINVAL, "moe_cache: token %d lists expert %d twice", t, ids[(size_t)t * k + r]);
+  if (d.policy == MOE_CACHE_LFU)
+    for (double& f : c->count) f *= d.lfu_decay;
   for (int t = 0; t < T; ++t) {
     const int32_t* id = ids + (size_t)t * k;
     int cls[64];
@@ -96,34 +138,48 @@ moe_status plan(moe_cache* c, int layer, int T, const int32_t* ids, const float*
       const size_t o = (size_t)t * k + r;
       if (cls[r] == 0 && res[r]) {
         const int s = c->map[pair];
-        c->stamp[s] = ++c->clock;
+        c->stamp[s] = use(c, pair);
         c->slots_h[o] = s;
         c->prec_h[o] = 0;
         c->st.hits++;
       } else if (cls[r] == 0) {
-        int victim = -1;
-        for (int s = 0; s < S; ++s) {
-          if (c->prot[s]) continue;
-          if (victim < 0 || c->stamp[s] < c->stamp[victim]) victim = s;
-        }
-        if (victim < 0) return fail(MOE_ECACHE_SMALL, "moe_cache: every slot is in use by this call");
-        if (c->owner[victim] >= 0) {
-          c->map[c->owner[victim]] = -1;
+        const int v = victim(c, c->owner, c->stamp, c->prot);
+        if (v < 0) return fail(MOE_ECACHE_SMALL, "moe_cache: every slot is in use by this call");
+        if (c->owner[v] >= 0) {
+          c->map[c->owner[v]] = -1;
           c->st.evictions++;
         }
-        c->owner[victim] = pair;
-        c->map[pair] = victim;
-        c->stamp[victim] = ++c->clock;
-        c->prot[victim] = 1;
-        c->slots_h[o] = victim;
+        c->owner[v] = pair;
+        c->map[pair] = v;
+        c->stamp[v] = use(c, pair);
+        c->prot[v] = 1;
+        c->slots_h[o] = v;
         c->prec_h[o] = 0;
-        c->copies.push_back({0, pair, victim});
+        c->copies.push_back({0, pair, v});
         c->st.misses++;
-      } else if (cls[r] == 1) {
+      } else if (cls[r] == 1 && d.int2_slots == 0) {
         const int st = t * (b - a) + (r + 1 - a - 1);
+        use(c, pair);
         c->slots_h[o] = st;
         c->prec_h[o] = 1;
         c->copies.push_back({1, pair, st});
+        c->st.int2_uses++;
+      } else if (cls[r] == 1) {
+        int v = c->map2[pair];
+        if (v >= 0) {
+          c->st.int2_hits++;
+        } else {
+          v = victim(c, c->owner2, c->stamp2, c->prot2);
+          if (v < 0) return fail(MOE_ECACHE_SMALL, "moe_cache: every 2-bit slot is in use by this call");
+          if (c->owner2[v] >= 0) c->map2[c->owner2[v]] = -1;
+          c->owner2[v] = pair;
+          c->map2[pair] = v;
+          c->copies.push_back({1, pair, v});
+        }
+        c->stamp2[v] = use(c, pair);
+        c->prot2[v] = 1;
+        c->slots_h[o] = v;
+        c->prec_h[o] = 1;
         c->st.int2_uses++;
       } else {
         c->st.drops++;
@@ -193,6 +249,14 @@ moe_status moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
                 (long)d->max_tokens * d->k, d->num_slots);
   if (d->H % 32 || d->I % 32 || d->H <= 0 || d->I <= 0) return fail(MOE_ESHAPE, "moe_cache_create: H=%d I=%d", d->H, d->I);
   const bool int2 = d->ladder_b > d->ladder_a;
+  if (d->int2_slots < 0) return fail(MOE_EINVAL, "moe_cache_create: int2_slots=%d", d->int2_slots);
+  if (int2 && d->int2_slots > 0 && (long)d->max_tokens * (d->ladder_b - d->ladder_a) > d->int2_slots)
+    return fail(MOE_ECACHE_SMALL, "moe_cache_create: int2_slots=%d below max_tokens*(b-a)=%ld", d->int2_slots,
+                (long)d->max_tokens * (d->ladder_b - d->ladder_a));
+  if (d->policy != MOE_CACHE_LRU && d->policy != MOE_CACHE_LFU)
+    return fail(MOE_EINVAL, "moe_cache_create: policy=%d", d->policy);
+  if (d->policy == MOE_CACHE_LFU && !(d->lfu_decay > 0.0 && d->lfu_decay <= 1.0))
+    return fail(MOE_EINVAL, "moe_cache_create: lfu_decay=%g outside (0, 1]", d->lfu_decay);
   if (d->fp4_host == nullptr && d->fp4_arena != nullptr)
     return fail(MOE_EINVAL, "moe_cache_create: fp4_host is NULL");
   if (int2 && d->fp4_arena && (!d->int2_host || !d->int2_staging))
@@ -204,6 +268,14 @@ moe_status moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
   c->map.assign((size_t)d->L * d->E, -1);
   c->owner.assign(d->num_slots, -1);
   c->stamp.assign(d->num_slots, 0);
+  c->map2.assign((size_t)d->L * d->E, -1);
+  c->owner2.assign(d->int2_slots, -1);
+  c->stamp2.assign(d->int2_slots, 0);
+  c->seed.assign((size_t)d->L * d->E, 0.0);
+  if (d->lfu_seed)
+    for (size_t i = 0; i < c->seed.size(); ++i) c->seed[i] = (double)d->lfu_seed[i];
+  c->count = c->seed;
+  c->d.lfu_seed = nullptr;  // copied: the caller's array need not outlive the call
   *out = c;
   return MOE_OK;
 }
@@ -223,6 +295,10 @@ moe_status moe_cache_reset(moe_cache* c) {
   std::fill(c->map.begin(), c->map.end(), -1);
   std::fill(c->owner.begin(), c->owner.end(), -1);
   std::fill(c->stamp.begin(), c->stamp.end(), 0);
+  std::fill(c->map2.begin(), c->map2.end(), -1);
+  std::fill(c->owner2.begin(), c->owner2.end(), -1);
+  std::fill(c->stamp2.begin(), c->stamp2.end(), 0);
+  c->count = c->seed;
   c->clock = 0;
   c->st = moe_cache_stats{};
   c->broken = false;
@@ -321,7 +397,7 @@ moe_status moe_cache_layer(const moe_cache* c, moe_layer* out) {
   const bool int2 = c->d.ladder_b > c->d.ladder_a;
   out->int2_base = int2 ? c->d.int2_staging : nullptr;
   out->int2_stride = c->int2_bytes;
-  out->num_int2 = int2 ? c->d.max_tokens * (c->d.ladder_b - c->d.ladder_a) : 0;
+  out->num_int2 = !int2 ? 0 : c->d.int2_slots > 0 ? c->d.int2_slots : c->d.max_tokens * (c->d.ladder_b - c->d.ladder_a);
   out->shared = nullptr;
   return MOE_OK;
 }

@@ -431,7 +431,7 @@ FP4, INT2, DROPPED = 0, 1, -1
 
 
 class SlotCache:
-    """Global LRU slot cache over (layer, expert) pairs with the (a, b) ladder.
+    """Global slot cache over (layer, expert) pairs with the (a, b) ladder.
 
     P1 §What the expert cache actually does: a fixed number of expert slots
     in device memory ('not layers, not experts, slots'), shared by all layers
@@ -440,32 +440,65 @@ class SlotCache:
     P2 §Not all six experts matter equally: ranks 1..a always FP4 (fetched on
     a miss); ranks a+1..b FP4 if resident, else the 2-bit copy; ranks > b used
     if resident, dropped otherwise; survivors renormalised.
+    P2 §Rig, model & methodology (best configuration): a second, smaller tier
+    of device slots for the 2-bit copies, and LFU eviction with frequency
+    decay seeded from a routing trace.
 
     Readings where the pages are silent:
       * residency for a token's classification is read once, before any of
-        that token's fetches;
+        that token's fetches; only FP4 residency classifies;
       * slots used by any rank of the call are protected from eviction for
-        the rest of the call;
+        the rest of the call (in each tier);
       * fetches are processed in rank order; each hit or fetch stamps the
-        slot with the next value of a global clock; the victim of a fetch is
-        the lowest-index empty slot, else the unprotected slot with the
-        oldest stamp;
-      * 2-bit copies are not cached: every use is a fresh copy into a staging
-        area, index t*(b-a) + (rank-a-1) within the call;
+        slot with the next value of a global clock shared by both tiers;
+      * victim of a fetch: the lowest-index empty slot; else, under LRU, the
+        unprotected slot with the oldest stamp; under LFU, the unprotected
+        slot whose pair has the lowest use count (ties: oldest stamp);
+      * LFU counts belong to pairs (kept while evicted): at the start of every
+        call each count is multiplied by the decay, and every use of a pair
+        (hit or fetch, either tier) adds one; `seed` gives the initial counts
+        (a routing trace's frequencies), zeros otherwise;
+      * int2_slots == 0: 2-bit copies are not cached; every use is a fresh
+        copy into a staging area, index t*(b-a) + (rank-a-1) within the call;
+        int2_slots > 0: the 2-bit copy of a pair is looked up in the tier and
+        fetched on a miss;
       * if every rank of a token is dropped, all its weights are zero.
     """
 
-    def __init__(self, L: int, E: int, S: int, k: int, a: int, b: int):
-        assert 0 <= a <= b <= k and S >= 1
+    def __init__(self, L: int, E: int, S: int, k: int, a: int, b: int, int2_slots: int = 0,
+                 policy: str = "lru", decay: float = 1.0, seed=None):
+        assert 0 <= a <= b <= k and S >= 1 and int2_slots >= 0 and policy in ("lru", "lfu")
         self.L, self.E, self.S, self.k, self.a, self.b = L, E, S, k, a, b
-        self.map = np.full(L * E, -1, dtype=np.int64)      # pair -> slot
-        self.owner = np.full(S, -1, dtype=np.int64)        # slot -> pair
+        self.S2, self.policy, self.decay = int2_slots, policy, float(decay)
+        self.map = np.full(L * E, -1, dtype=np.int64)      # pair -> FP4 slot
+        self.owner = np.full(S, -1, dtype=np.int64)        # FP4 slot -> pair
         self.stamp = np.zeros(S, dtype=np.int64)           # 0 = empty
+        self.map2 = np.full(L * E, -1, dtype=np.int64)     # pair -> 2-bit slot
+        self.owner2 = np.full(max(int2_slots, 1), -1, dtype=np.int64)
+        self.stamp2 = np.zeros(max(int2_slots, 1), dtype=np.int64)
+        self.count = (np.zeros(L * E) if seed is None else np.asarray(seed, np.float64).reshape(L * E).copy())
         self.clock = 0
-        self.hits = self.misses = self.int2 = self.drops = 0
+        self.hits = self.misses = self.int2 = self.drops = self.int2_hits = 0
 
     def resident(self, layer: int, e: int) -> bool:
         return self.map[layer * self.E + e] >= 0
+
+    def _victim(self, owner, stamp, protected):
+        """Lowest-index empty slot, else the unprotected slot to evict."""
+        n = len(owner)
+        for s in range(n):
+            if owner[s] < 0 and s not in protected:
+                return s
+        cand = [s for s in range(n) if s not in protected]
+        assert cand, "every slot is in use by this call"
+        if self.policy == "lru":
+            return min(cand, key=lambda q: (stamp[q], q))
+        return min(cand, key=lambda q: (self.count[owner[q]], stamp[q], q))
+
+    def _use(self, pair: int):
+        self.clock += 1
+        self.count[pair] += 1.0
+        return self.clock
 
     def step(self, layer: int, ids: np.ndarray, w: np.ndarray):
         """One call for T tokens of one layer.  ids [T,k] expert ids and w
@@ -475,11 +508,14 @@ class SlotCache:
         w = np.asarray(w, np.float64).reshape(-1, self.k)
         T, k, a, b, E = ids.shape[0], self.k, self.a, self.b, self.E
         assert T * k <= self.S
+        assert self.S2 == 0 or T * (b - a) <= self.S2
+        if self.policy == "lfu":
+            self.count *= self.decay
         slot = np.full((T, k), -1, dtype=np.int32)
         prec = np.full((T, k), DROPPED, dtype=np.int8)
         wout = np.zeros((T, k), dtype=np.float64)
         copies = []
-        protected = set()
+        protected, protected2 = set(), set()
         for t in range(T):
             res = [self.resident(layer, int(e)) for e in ids[t]]      # snapshot
             cls = []
@@ -499,27 +535,40 @@ class SlotCache:
                 pair = layer * E + e
                 if cls[r] == FP4 and res[r]:
                     s = int(self.map[pair])
-                    self.clock += 1
-                    self.stamp[s] = self.clock
+                    self.stamp[s] = self._use(pair)
                     slot[t, r], prec[t, r] = s, FP4
                     self.hits += 1
                 elif cls[r] == FP4:
-                    cand = [s for s in range(self.S) if s not in protected]
-                    s = min(cand, key=lambda q: (self.stamp[q], q))   # empty (0) first, then oldest
+                    s = self._victim(self.owner, self.stamp, protected)
                     if self.owner[s] >= 0:
                         self.map[self.owner[s]] = -1
                     self.owner[s] = pair
                     self.map[pair] = s
-                    self.clock += 1
-                    self.stamp[s] = self.clock
+                    self.stamp[s] = self._use(pair)
                     protected.add(s)
                     slot[t, r], prec[t, r] = s, FP4
                     copies.append(("fp4", layer, e, s))
                     self.misses += 1
-                elif cls[r] == INT2:
+                elif cls[r] == INT2 and self.S2 == 0:
                     st = t * (b - a) + (r + 1 - a - 1)
+                    self._use(pair)
                     slot[t, r], prec[t, r] = st, INT2
                     copies.append(("int2", layer, e, st))
+                    self.int2 += 1
+                elif cls[r] == INT2:
+                    s = int(self.map2[pair])
+                    if s >= 0:
+                        self.int2_hits += 1
+                    else:
+                        s = self._victim(self.owner2, self.stamp2, protected2)
+                        if self.owner2[s] >= 0:
+                            self.map2[self.owner2[s]] = -1
+                        self.owner2[s] = pair
+                        self.map2[pair] = s
+                        copies.append(("int2", layer, e, s))
+                    self.stamp2[s] = self._use(pair)
+                    protected2.add(s)
+                    slot[t, r], prec[t, r] = s, INT2
                     self.int2 += 1
                 else:
                     self.drops += 1

@@ -17,9 +17,10 @@ def _route_all(logits, k):
     return ids.reshape(T, L, k), w.astype(np.float32).reshape(T, L, k)
 
 
-def _compare_trace(L, E, S, k, a, b, ids, w, T_call=1):
-    c = B.Cache(L, E, 4096, 2048, S, k, a, b, max_tokens=T_call)
-    oc = O.SlotCache(L, E, S, k, a, b)
+def _compare_trace(L, E, S, k, a, b, ids, w, T_call=1, int2_slots=0, policy="lru", decay=1.0, seed=None):
+    c = B.Cache(L, E, 4096, 2048, S, k, a, b, max_tokens=T_call, int2_slots=int2_slots, policy=policy,
+                lfu_decay=decay, lfu_seed=seed)
+    oc = O.SlotCache(L, E, S, k, a, b, int2_slots=int2_slots, policy=policy, decay=decay, seed=seed)
     T = ids.shape[0]
     try:
         for t0 in range(0, T, T_call):
@@ -34,6 +35,7 @@ def _compare_trace(L, E, S, k, a, b, ids, w, T_call=1):
                 assert np.array_equal(c.slot_map(), oc.slot_map()), (t0, l)
         st = c.stats()
         assert (st["hits"], st["misses"], st["int2_uses"], st["drops"]) == (oc.hits, oc.misses, oc.int2, oc.drops)
+        assert st["int2_hits"] == oc.int2_hits
         return st
     finally:
         c.destroy()
@@ -91,3 +93,49 @@ def test_slotcache_validation():
         assert np.all(c.slot_map() == -1) and c.stats()["calls"] == 0
     finally:
         c.destroy()
+
+
+@pytest.mark.parametrize("policy,int2_slots,decay,seeded,T_call", [
+    ("lru", 8, 1.0, False, 1),
+    ("lfu", 0, 1.0, False, 1),
+    ("lfu", 0, 0.9, True, 1),
+    ("lfu", 10, 0.95, True, 1),
+    ("lfu", 12, 0.8, False, 3),
+])
+def test_slotcache_tier_and_lfu_bit_exact(policy, int2_slots, decay, seeded, T_call):
+    """The 2-bit tier and LFU with decay (2-bit hits, evictions in both tiers)
+    against the oracle's replay, slot for slot."""
+    L, E, k, S, T = 3, 32, 6, 40, 90
+    rng = np.random.default_rng(int2_slots * 7 + int(decay * 100) + T_call)
+    logits = rng.standard_normal((T, L, E)).astype(np.float32)
+    logits += W.zipf_bias(9, (1,), E, 1.1)[None, None, :]
+    ids, w = _route_all(logits, k)
+    seed = rng.integers(0, 6, L * E).astype(np.float32) if seeded else None
+    st = _compare_trace(L, E, S, k, 2, 4, ids, w, T_call=T_call, int2_slots=int2_slots, policy=policy,
+                        decay=decay, seed=seed)
+    assert st["evictions"] > 0
+    if int2_slots:
+        assert st["int2_hits"] > 0
+
+
+def test_slotcache_full_trace_with_tier_and_lfu():
+    """The slot-cache decode trace at full shape with a 100-slot 2-bit tier and
+    LFU (decay 0.95) seeded from a separate warm-up trace."""
+    cfg = W.CONFIGS[4]
+    L, E, k, S, (a, b), T = cfg["L"], cfg["E"], cfg["k"], cfg["slots"], cfg["ladder"], cfg["T"]
+    logits = W.slotcache_logits(W.config_seed(4), L, E, T, cfg["zipf"])
+    ids, w = _route_all(logits, k)
+    warm = W.slotcache_logits(W.config_seed(4) + 1, L, E, 64, cfg["zipf"])
+    wids, _ = _route_all(warm, k)
+    seed = np.zeros(L * E, np.float32)
+    for l in range(L):
+        np.add.at(seed, l * E + wids[:, l].reshape(-1), 1.0)
+    st = _compare_trace(L, E, S, k, a, b, ids, w, int2_slots=100, policy="lfu", decay=0.95, seed=seed)
+    assert st["int2_hits"] > 0
+
+
+def test_tier_validation():
+    with pytest.raises(B.MoeError, match="int2_slots"):
+        B.Cache(2, 8, 256, 128, 8, 4, 1, 3, max_tokens=2, int2_slots=3)
+    with pytest.raises(B.MoeError, match="lfu_decay"):
+        B.Cache(2, 8, 256, 128, 8, 4, 1, 3, policy="lfu", lfu_decay=0.0)

@@ -150,3 +150,55 @@ def test_hand_worked_trace():
         slot, prec, wout, copies = c.step(layer, ids, w)
         assert slot[0].tolist() == want_slot, row
         assert prec[0].tolist() == want_prec, row
+
+
+# ------------------------------------------------ 2-bit tier and LFU, by hand
+
+def test_int2_tier_hand_worked():
+    """a = 0, b = 2: both ranks take the 2-bit copy (FP4 is never fetched);
+    two 2-bit slots under LRU.  Worked by hand from the rule: the lowest empty
+    slot first, hits protect their slot, the oldest unprotected use goes."""
+    c = O.SlotCache(1, 6, 6, 2, 0, 2, int2_slots=2)
+    w = np.array([[0.6, 0.4]])
+    slot, prec, _, cp = c.step(0, np.array([[0, 1]]), w)      # clock 1: pair 0 -> slot 0; 2: pair 1 -> slot 1
+    assert slot.tolist() == [[0, 1]] and prec.tolist() == [[1, 1]]
+    assert [(k, e, d) for k, _, e, d in cp] == [("int2", 0, 0), ("int2", 1, 1)]
+    slot, _, _, cp = c.step(0, np.array([[0, 2]]), w)         # 3: pair 0 hits slot 0; 4: pair 2 evicts pair 1
+    assert slot.tolist() == [[0, 1]] and [(e, d) for _, _, e, d in cp] == [(2, 1)] and c.int2_hits == 1
+    slot, _, _, cp = c.step(0, np.array([[1, 0]]), w)         # 5: pair 1 takes slot 0 (stamp 3 < 4); 6: pair 0 -> slot 1
+    assert slot.tolist() == [[0, 1]] and [(e, d) for _, _, e, d in cp] == [(1, 0), (0, 1)] and c.int2_hits == 1
+    assert c.int2 == 6 and c.misses == 0 and np.all(c.slot_map() == -1)
+
+
+def _lfu_vs_lru(policy, decay=1.0, seed=None):
+    """Two FP4 slots; expert 0 used three times, then expert 1 once, then
+    expert 2 needs a slot.  Returns the slot expert 2 lands in."""
+    c = O.SlotCache(1, 4, 2, 1, 1, 1, policy=policy, decay=decay, seed=seed)
+    for e in (0, 0, 0, 1):
+        c.step(0, np.array([[e]]), np.array([[1.0]]))
+    slot, _, _, _ = c.step(0, np.array([[2]]), np.array([[1.0]]))
+    return int(slot[0, 0])
+
+
+def test_lfu_eviction_hand_worked():
+    # LRU: expert 0 (last use at clock 3) is older than expert 1 (clock 4): slot 0 goes
+    assert _lfu_vs_lru("lru") == 0
+    # LFU without decay: expert 1 has the lower count (1 < 3): slot 1 goes
+    assert _lfu_vs_lru("lfu") == 1
+    # LFU, decay 0.1: counts 0.0111 (expert 0) and 0.1 (expert 1) at the fifth call: slot 0 goes
+    assert _lfu_vs_lru("lfu", decay=0.1) == 0
+    # LFU seeded with 10 uses of expert 1: 3 < 11, slot 0 goes
+    assert _lfu_vs_lru("lfu", seed=np.array([0, 10, 0, 0], np.float64)) == 0
+
+
+def test_default_tier_arguments_keep_the_plain_cache():
+    """int2_slots = 0 and LRU reproduce the hand-worked trace of the plain cache."""
+    rows = read_golden("slotcache_trace.txt")
+    hdr = dict(kv.split("=") for kv in rows[0])
+    L, E, S, k, a, b = (int(hdr[n]) for n in ("L", "E", "S", "k", "a", "b"))
+    c = O.SlotCache(L, E, S, k, a, b, int2_slots=0, policy="lru", decay=0.5)
+    for row in rows[1:]:
+        slot, prec, _, _ = c.step(int(row[0]), np.array([[int(v) for v in row[1].split(",")]]),
+                                  np.array([[0.4, 0.3, 0.2, 0.1][:k]]))
+        assert slot[0].tolist() == [int(v) for v in row[2].split(",")]
+        assert prec[0].tolist() == [int(v) for v in row[3].split(",")]

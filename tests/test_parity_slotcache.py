@@ -14,13 +14,13 @@ from tests.gpu_util import TOL_BF16_MAX_REL, bf16_dev, dev, log, max_rel
 pytestmark = pytest.mark.gpu
 
 
-def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1):
+def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1, **tier):
     import torch
     lib = gpu_lib
     rb4, rb2 = O.fp4_expert_nbytes(H, I), O.int2_expert_nbytes(H, I)
     logits = W.slotcache_logits(seed, L, E, T, zipf)                 # [T, L, E]
     # the oracle's own trace tells which host records are ever read
-    oc0 = O.SlotCache(L, E, S, k, a, b)
+    oc0 = O.SlotCache(L, E, S, k, a, b, **_oracle_tier(tier))
     need4, need2 = set(), set()
     for t in range(T):
         for l in range(L):
@@ -36,9 +36,10 @@ def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1):
     for p in need2:
         W.int2_record(seed, W.S_INT2, p, H, I, out=int2_host.array[p * rb2:(p + 1) * rb2])
     arena = torch.empty(S * rb4, dtype=torch.uint8, device="cuda")
-    staging = torch.empty(max(1, (b - a)) * rb2, dtype=torch.uint8, device="cuda") if b > a else None
-    cache = lib.Cache(L, E, H, I, S, k, a, b, 1, fp4_host, int2_host, arena, staging)
-    oc = O.SlotCache(L, E, S, k, a, b)
+    n2 = tier.get("int2_slots", 0) or max(1, b - a)
+    staging = torch.empty(n2 * rb2, dtype=torch.uint8, device="cuda") if b > a else None
+    cache = lib.Cache(L, E, H, I, S, k, a, b, 1, fp4_host, int2_host, arena, staging, **tier)
+    oc = O.SlotCache(L, E, S, k, a, b, **_oracle_tier(tier))
     copy_stream = torch.cuda.Stream()
     try:
         layer = cache.layer()
@@ -75,12 +76,18 @@ def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1):
         st = cache.stats()
         log(f"  stats {st}; outputs checked: {checked}")
         assert (st["hits"], st["misses"], st["int2_uses"], st["drops"]) == (oc.hits, oc.misses, oc.int2, oc.drops)
+        assert st["int2_hits"] == oc.int2_hits
         return st
     finally:
         cache.destroy()
         fp4_host.free()
         if int2_host is not None:
             int2_host.free()
+
+
+def _oracle_tier(tier):
+    return {"int2_slots": tier.get("int2_slots", 0), "policy": tier.get("policy", "lru"),
+            "decay": tier.get("lfu_decay", 1.0), "seed": tier.get("lfu_seed")}
 
 
 def test_slotcache_loop_small(gpu_lib):
@@ -100,3 +107,13 @@ def test_slotcache_loop_full_size(gpu_lib):
     cfg = W.CONFIGS[4]
     _run(gpu_lib, L=cfg["L"], E=cfg["E"], H=cfg["H"], I=cfg["I"], S=cfg["slots"], k=cfg["k"],
          a=cfg["ladder"][0], b=cfg["ladder"][1], T=16, seed=W.config_seed(4), check_every=4)
+
+
+def test_slotcache_loop_int2_tier_lfu(gpu_lib):
+    """The 2-bit tier (6 device slots) and LFU eviction with decay, seeded:
+    2-bit hits read records copied by earlier calls; evictions in both tiers."""
+    L, E = 3, 16
+    seed_counts = np.random.default_rng(5).integers(0, 4, L * E).astype(np.float32)
+    st = _run(gpu_lib, L=L, E=E, H=512, I=256, S=16, k=4, a=1, b=3, T=30, seed=73, check_every=3,
+              int2_slots=6, policy="lfu", lfu_decay=0.875, lfu_seed=seed_counts)
+    assert st["int2_hits"] > 0 and st["evictions"] > 0
