@@ -45,6 +45,8 @@ def parse():
                          "prefill: 4096 tokens, top-8, MXFP8 x MXFP4 scaled MFMA; "
                          "slotcache: 512 tokens x 8 layers through the 512-slot cache with the (2,4) ladder")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tp-share", type=int, default=1,
+                    help="decode-b1 on rank 0's share of G-way tensor parallelism (experts cut along I)")
     ap.add_argument("--slot-tier", action="store_true",
                     help="slotcache workload with a 100-slot 2-bit device tier and LFU eviction "
                          "(decay 0.95, counts seeded from a separate 64-token routing trace)")
@@ -231,6 +233,16 @@ def bench_decode_b1(args):
     print(f"[bench] generating {E}+1 experts ({(E + 1) * rec_bytes / 1e9:.2f} GB) and {nsteps} steps of inputs",
           file=sys.stderr, flush=True)
     bank, shared, rec_bytes = resident_bank(W, lib, torch, cfg, seed, dev)
+    G = args.tp_share
+    if G > 1:  # rank 0's slice of every expert: I/G rows of w1, w3 and columns of w2
+        rec_bytes = lib.moe_fp4_expert_bytes(H, I // G)
+        share = torch.empty((E, rec_bytes), dtype=torch.uint8, device=dev)
+        shared_share = torch.empty((1, rec_bytes), dtype=torch.uint8, device=dev)
+        lib.moe_tp_slice(bank, H, I, G, 0, share)
+        lib.moe_tp_slice(shared[None, :], H, I, G, 0, shared_share)
+        torch.cuda.synchronize()
+        del bank
+        bank, shared, I = share, shared_share[0], I // G
     xs = np.stack([W.make_layer_inputs(cfg, seed, s, with_bank=False)["x"][0] for s in range(nsteps)])
     lgs = np.stack([W.make_layer_inputs(cfg, seed, s, with_bank=False)["logits"][0] for s in range(nsteps)])
     x_d = torch.from_numpy(xs).to(dev).view(torch.bfloat16)          # [steps, H]
@@ -268,12 +280,15 @@ def bench_decode_b1(args):
     # written and read back, the ids and weights, the bf16 output row
     step_alg_bytes = k1 * rec_bytes + E * 4 + H * 2 + 2 * k1 * I * 2 + k * 8 + H * 2
     khash = kernel_hash()
-    traffic = traffic_from_profiles(khash)
+    traffic = traffic_from_profiles(khash) if G == 1 else None
     per_kernel = {n: round(v[0] / v[1] * 1e3, 3) for n, v in prof.items()}
     print(f"[bench] kernel averages (us): {per_kernel}", file=sys.stderr, flush=True)
     ms, n = prof["gateup"]      # the dominant kernel of the two launches
-    dom_kernel = "gateup_b1_kernel (routing + batch-1 gate/up GEMV + SwiGLU)"
+    dom_kernel = ("gateup_b1_kernel (routing + batch-1 gate/up GEMV + SwiGLU)" if G == 1 else
+                  f"gate/up GEMV of the generic path on a 1/{G} share (I = {I})")
     dom_bytes = k1 * 2 * (H * I // 2 + H * I // 32) + E * 4 + H * 2 + k1 * I * 2
+    if G > 1:  # the generic gate/up reads ids (not logits) and writes fp32 h
+        dom_bytes = k1 * 2 * (H * I // 2 + H * I // 32) + k * 4 + H * 2 + k1 * I * 4
     dom_avg_s = ms / n / 1e3
     achieved = dom_bytes / dom_avg_s / 1e9
 
@@ -293,9 +308,10 @@ def bench_decode_b1(args):
         "vs_baseline": None,
         "dtype": "mxfp4-w/bf16-x/f32-acc",
         "data": "synthetic (seeded; fresh logits and activations every step)",
-        "config": {"workload": cfg["name"], "experts": E, "shared_experts": 1, "hidden": H,
-                   "expert_intermediate": I, "top_k": k, "tokens_per_step": T,
-                   "expert_bytes": rec_bytes, "weight_bytes_per_step": step_bytes, "launch": args.mode},
+        "config": {"workload": cfg["name"] + (f"-tp{G}-share0" if G > 1 else ""), "experts": E,
+                   "shared_experts": 1, "hidden": H, "expert_intermediate": I, "top_k": k, "tokens_per_step": T,
+                   "expert_bytes": rec_bytes, "weight_bytes_per_step": step_bytes, "launch": args.mode,
+                   "tp_share": G},
         "step_hbm_GBps": round(step_bytes * value / 1e9, 1),
         "step_hbm_frac": round(step_bytes * value / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": dom_kernel,
@@ -309,7 +325,7 @@ def bench_decode_b1(args):
     peak_m = measured_read_peak(torch, lib)
     result["hbm_read_peak_measured_GBps"] = peak_m
     result["roofline"]["frac_vs_measured_peak"] = round(achieved / peak_m, 4)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and G == 1:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         cb = cpu_baseline(args.cpu_seconds)
         n = host_threads()

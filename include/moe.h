@@ -193,6 +193,19 @@ moe_status moe_debug_dequant(const uint8_t* record, int H, int I, int prec, int 
  * the 8 TB/s datasheet figure. */
 moe_status moe_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, moe_stream_t stream);
 
+/* ------------------------------------------------------------ tensor-parallel share */
+
+/* Rank g's share of n MXFP4 records for G-way tensor parallelism ([P1] §Step 2, Check it
+ * divides: every rank keeps its own slice of each expert, cut on the FP4 32-element scale
+ * blocks).  Record e of src (H, I) at src + e*src_stride becomes record e of dst (H, I/G)
+ * at dst + e*dst_stride: rows [g*I/G, (g+1)*I/G) of w1 and w3 with their scale rows, and
+ * the same columns of w2 with its scale blocks along I.  The expert MLP of the share gives
+ * a partial output; the G partials sum to the full output.  Device to device copies on
+ * `stream`; dst_stride >= moe_fp4_expert_bytes(H, I/G).  Errors: MOE_ESHAPE when G does
+ * not divide I into multiples of 32. */
+moe_status moe_tp_slice(const uint8_t* src, size_t src_stride, int n, int H, int I, int G, int g, uint8_t* dst,
+                        size_t dst_stride, moe_stream_t stream);
+
 /* ------------------------------------------------------------ prefill */
 
 /* MXFP8 quantisation of a bf16 matrix along its rows: one E8M0 scale per 32

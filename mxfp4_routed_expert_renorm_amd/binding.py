@@ -73,6 +73,7 @@ _SIGS = {
     "moe_combine": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p]),
     "moe_debug_dequant": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
     "moe_debug_stream_read": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
+    "moe_tp_slice": (c_int, [c_void_p, c_size_t, c_int, c_int, c_int, c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "moe_quant_mxfp8": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "moe_prefill_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "moe_prefill_forward": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_int, c_void_p, c_void_p,
@@ -222,6 +223,15 @@ def moe_combine(y, w, prec, T, k, H, has_shared, out, stream=None):
 def moe_debug_dequant(record, H, I, prec, matrix, out, stream=None):
     _check("moe_debug_dequant", load().moe_debug_dequant(_p(record), H, I, prec, matrix, _p(out), _stream(stream)))
     return out
+
+
+def moe_tp_slice(src, H, I, G, g, dst, stream=None):
+    """Rank g of G's share of a bank: src uint8 [n, stride] (H, I) -> dst uint8 [n, stride'] (H, I/G)."""
+    def row_stride(t):  # a size-1 leading dimension may carry any stride
+        return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    _check("moe_tp_slice", load().moe_tp_slice(_p(src), row_stride(src), src.shape[0], H, I, G, g, _p(dst),
+                                               row_stride(dst), _stream(stream)))
+    return dst
 
 
 def moe_debug_stream_read(buf, sink, stream=None):

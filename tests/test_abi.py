@@ -141,3 +141,15 @@ def test_stream_read_validation(lib):
     assert lib.moe_debug_stream_read(ctypes.c_void_p(8), n(16), ctypes.c_void_p(64), None) == 1   # misaligned
     assert lib.moe_debug_stream_read(ctypes.c_void_p(64), n(17), ctypes.c_void_p(64), None) == 1  # not a multiple of 16
     assert lib.moe_debug_stream_read(ctypes.c_void_p(64), n(0), ctypes.c_void_p(64), None) == 0   # nothing to read
+
+
+def test_tp_slice_validation(lib):
+    import ctypes
+    n = ctypes.c_size_t
+    P = ctypes.c_void_p(256)
+    # I = 2048 over G = 3 does not divide; G = 128 leaves 16-element slices (not whole scale blocks)
+    assert lib.moe_tp_slice(P, n(1 << 24), 1, 4096, 2048, 3, 0, P, n(1 << 24), None) == 2
+    assert lib.moe_tp_slice(P, n(1 << 24), 1, 4096, 2048, 128, 0, P, n(1 << 24), None) == 2
+    assert lib.moe_tp_slice(P, n(1 << 24), 1, 4096, 2048, 4, 4, P, n(1 << 24), None) == 1   # rank out of range
+    assert lib.moe_tp_slice(P, n(16), 1, 4096, 2048, 4, 0, P, n(1 << 24), None) == 1        # stride too small
+    assert lib.moe_tp_slice(P, n(1 << 24), 0, 4096, 2048, 4, 0, P, n(1 << 24), None) == 0   # nothing to do
