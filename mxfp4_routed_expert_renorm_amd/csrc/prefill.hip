@@ -121,7 +121,7 @@ struct PrefillArgs {
   int32_t* counts;      // [nkeys]
   int32_t* offsets;     // [nkeys+1]
   int32_t* perm;        // [P] sorted position -> pair
-  int32_t* items;       // [0] = number of M-tiles, then (key, row0) pairs
+  int32_t* items;       // [0] = number of M tiles, then (key, start, rows) per tile
   // intermediate and output
   uint8_t* hq;          // [P][I] E4M3, grouped order
   uint8_t* hs;          // [P][I/32]
@@ -151,18 +151,21 @@ __global__ __launch_bounds__(256) void prefill_keys_kernel(PrefillArgs a) {
   }
 }
 
-// items[0] = number of M tiles, then (key, row0, rows) per tile.  A key with c
+// items[0] = number of M tiles, then (key, start, rows) per tile, start being
+// the tile's first position in the grouped order.  A key with c
 // rows gets ceil(c / MT) tiles of equal size rounded up to whole 32-row
 // blocks (the last one takes the rest), so e.g. 140 rows run as one tile of
 // the prefill GEMM (MT 192).
 template <int MT>
-__global__ __launch_bounds__(64) void prefill_items_kernel(const int32_t* __restrict__ counts, int nkeys,
+__global__ __launch_bounds__(64) void prefill_items_kernel(const int32_t* __restrict__ counts,
+                                                           const int32_t* __restrict__ offsets, int nkeys,
                                                            int32_t* __restrict__ items) {
   const int lane = threadIdx.x;
   int n = 0;
   for (int base = 0; base < nkeys; base += 64) {
     const int key = base + lane;
     const int c = key < nkeys ? counts[key] : 0;
+    const int o = key < nkeys ? offsets[key] : 0;
     const int tiles = (c + MT - 1) / MT;
     int incl = tiles;
 #pragma unroll
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(64) void prefill_items_kernel(const int32_t* __rest
     const int sz = tiles ? ((c + tiles - 1) / tiles + 31) / 32 * 32 : 0;
     for (int i = 0; i < tiles; ++i) {
       items[1 + 3 * (first + i)] = key;
-      items[2 + 3 * (first + i)] = i * sz;
+      items[2 + 3 * (first + i)] = o + i * sz;
       items[3 + 3 * (first + i)] = min(sz, c - i * sz);
     }
     n += __shfl(incl, 63, 64);
@@ -460,8 +463,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(PrefillArgs a) {
 
   for (int item = virtual_block(); item < nitems; item += gridDim.x) {
     const int mi = item / ncol, nt = item - mi * ncol;
-    const int key = a.items[1 + 3 * mi], row0 = a.items[2 + 3 * mi], rows = a.items[3 + 3 * mi];
-    const int start = a.offsets[key] + row0;  // first grouped position of the tile
+    const int key = a.items[1 + 3 * mi], start = a.items[2 + 3 * mi], rows = a.items[3 + 3 * mi];  // first grouped position of the tile
     const uint8_t* rec = key_record(a, key);
     // activation rows: x (gathered by token) for gate/up, h (grouped) for down
     const uint8_t* abase = NMAT == 2 ? a.xq : a.hq;
@@ -519,9 +521,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(PrefillArgs a) {
 // block scale is a power of two) and multiplied on v_mfma_f32_32x32x16_bf16
 // against the bf16 activations, so the products are exact as on the batch-1
 // path.  Items are (M tile of up to 64 grouped rows of one record, 256 weight
-// rows) and run the prefill GEMM's stage pipeline; wavefront w takes M block
-// w / 2 and column half w % 2 (for gate/up, 64 gate and the same 64 up
-// columns).  A K step of the MFMA takes, per lane, 8 consecutive elements of
+// rows) and run the prefill GEMM's stage pipeline.  A tile of two M blocks
+// gives wavefront w M block w / 2 and column half w % 2 (for gate/up, 64 gate
+// and the same 64 up columns); a tile of one M block (most of a decode
+// batch's groups) splits the columns four ways instead, so no wavefront idles.  A K step of the MFMA takes, per lane, 8 consecutive elements of
 // the 32 its FP4 piece covers; the activation fragment is read at the same K.
 
 constexpr int kDMT = 64;                      // grouped rows per item at most
@@ -587,26 +590,33 @@ __device__ __forceinline__ void dstage_store(DGemmSmem& sm, int buf, const DStag
   sm.bs[buf][tid] = r.bs;
 }
 
-// LDS weight-tile block of the wavefront's column block j (0..3) in column
-// half nh: gate/up: gate blocks 2nh, 2nh+1 then the up blocks 4+2nh, 5+2nh;
-// down: blocks 4nh .. 4nh+3
-template <int NMAT>
-__device__ __forceinline__ int dcol_block(int nh, int j) {
-  return NMAT == 2 ? (j < 2 ? 2 * nh + j : 4 + 2 * nh + (j - 2)) : 4 * nh + j;
+// LDS weight-tile block of the wavefront's column block j (0..NBW-1) in its
+// column share cs.  NBW = 4 (a tile of two M blocks; cs = column half):
+// gate/up: gate blocks 2cs, 2cs+1 then the up blocks 4+2cs, 5+2cs; down:
+// blocks 4cs .. 4cs+3.  NBW = 2 (a tile of one M block, the columns split four
+// ways; cs = wavefront): gate/up: gate block cs and up block 4+cs; down: 2cs, 2cs+1.
+template <int NMAT, int NBW>
+__device__ __forceinline__ int dcol_block(int cs, int j) {
+  constexpr int half = NBW / 2;
+  return NMAT == 2 ? (j < half ? half * cs + j : 4 + half * cs + (j - half)) : NBW * cs + j;
 }
 
 struct DItemCtx {
   DLoadOffs O;
   const uint8_t *abase, *rec;
-  int tid, c, h, mp, nh, nstage, rows, start, nt;
+  int tid, c, h, wave, mp, nh, nstage, rows, start, nt;
 };
 
-template <int NMAT, bool LIVE>
+// NBW column blocks per wavefront (4: M block mp of two, 2: the only M block),
+// LIVE false: the wavefront's M block is past the tile's rows
+template <int NMAT, int NBW, bool LIVE>
 __device__ __forceinline__ void dgemm_item(DGemmSmem& sm, const PrefillArgs& a, const DItemCtx& x) {
   const int tid = x.tid, c = x.c, h = x.h, nstage = x.nstage;
-  v16f acc[4];
+  const int mb = NBW == 4 ? x.mp : 0;       // the wavefront's M block
+  const int cs = NBW == 4 ? x.nh : x.wave;  // its column share
+  v16f acc[NBW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < NBW; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
 
@@ -621,7 +631,7 @@ __device__ __forceinline__ void dgemm_item(DGemmSmem& sm, const PrefillArgs& a, 
   dstage_load(R[0], x.O, x.abase, x.rec, min(kDDepth, nstage - 1) * kDKS);
   __syncthreads();
 
-  const int arow = (32 * x.mp + c) * kDArow;
+  const int arow = (32 * mb + c) * kDArow;
   for (int s0 = 0; s0 < nstage; s0 += kDDepth) {
 #pragma unroll
     for (int d = 0; d < kDDepth; ++d) {
@@ -631,20 +641,20 @@ __device__ __forceinline__ void dgemm_item(DGemmSmem& sm, const PrefillArgs& a, 
 #pragma unroll
         for (int kc = 0; kc < kDKS / 64; ++kc) {
           // the lane's FP4 piece of each column block: K [kc*64 + 32h, +32) of weight row c
-          u32x4_t q[4];
-          float sc[4];
+          u32x4_t q[NBW];
+          float sc[NBW];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = dcol_block<NMAT>(x.nh, j) * 32 + c;
+          for (int j = 0; j < NBW; ++j) {
+            const int r = dcol_block<NMAT, NBW>(cs, j) * 32 + c;
             q[j] = *(const u32x4_t*)(sm.b[buf] + r * kDBrow + kc * 32 + 16 * h);
             sc[j] = e8m0_to_f32((sm.bs[buf][r] >> (8 * (2 * kc + h))) & 0xffu);
           }
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            // K [kc*64 + 32h + 8m, +8): activations of row 32*mp + c, weights of each block's row c
+            // K [kc*64 + 32h + 8m, +8): activations of row 32*mb + c, weights of each block's row c
             const v8bf av = *(const v8bf*)(sm.a[buf] + arow + 2 * (kc * 64 + 32 * h + 8 * m));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NBW; ++j) {
               u32x4_t wv;
               wv.x = fp4x2_to_bf16x2_scaled<0>(q[j][m], sc[j]);
               wv.y = fp4x2_to_bf16x2_scaled<1>(q[j][m], sc[j]);
@@ -666,16 +676,16 @@ __device__ __forceinline__ void dgemm_item(DGemmSmem& sm, const PrefillArgs& a, 
   int ce = c, he = h;
   asm volatile("" : "+v"(ce), "+v"(he));
   const int H = a.H, I = a.I;
-  const int rb = 32 * x.mp;
+  const int rb = 32 * mb;
   if (NMAT == 2) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int col = x.nt * (kNR / 2) + 32 * dcol_block<2>(x.nh, q) + ce;
+    for (int q = 0; q < NBW / 2; ++q) {
+      const int col = x.nt * (kNR / 2) + 32 * dcol_block<2, NBW>(cs, q) + ce;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = rb + 8 * (e / 4) + 4 * he + (e % 4);
         if (r < x.rows) {
-          const float g = acc[q][e], u = acc[2 + q][e];
+          const float g = acc[q][e], u = acc[NBW / 2 + q][e];
           a.hb[(size_t)(x.start + r) * I + col] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
         }
       }
@@ -687,7 +697,8 @@ __device__ __forceinline__ void dgemm_item(DGemmSmem& sm, const PrefillArgs& a, 
       if (r < x.rows) {
         const size_t pair = (size_t)sm.pm[r];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a.yf[pair * H + (size_t)x.nt * kNR + dcol_block<1>(x.nh, j) * 32 + ce] = acc[j][e];
+        for (int j = 0; j < NBW; ++j)
+          a.yf[pair * H + (size_t)x.nt * kNR + dcol_block<1, NBW>(cs, j) * 32 + ce] = acc[j][e];
       }
     }
   }
@@ -711,8 +722,7 @@ __global__ __launch_bounds__(kDThreads) void dgemm_kernel(PrefillArgs a) {
 
   for (int item = virtual_block(); item < nitems; item += gridDim.x) {
     const int mi = item / ncol, nt = item - mi * ncol;
-    const int key = a.items[1 + 3 * mi], row0 = a.items[2 + 3 * mi], rows = a.items[3 + 3 * mi];
-    const int start = a.offsets[key] + row0;
+    const int key = a.items[1 + 3 * mi], start = a.items[2 + 3 * mi], rows = a.items[3 + 3 * mi];
     const uint8_t* rec = key_record(a, key);
     auto act_row = [&](int r) -> uint32_t {
       r = min(r, rows - 1);
@@ -744,12 +754,14 @@ __global__ __launch_bounds__(kDThreads) void dgemm_kernel(PrefillArgs a) {
     x.O.bs = weight_row(tid, true);
     x.abase = NMAT == 2 ? (const uint8_t*)a.xb : (const uint8_t*)a.hb;
     x.rec = rec;
-    x.tid = tid, x.c = c, x.h = h, x.mp = mp, x.nh = nh, x.nstage = nstage;
+    x.tid = tid, x.c = c, x.h = h, x.wave = wave, x.mp = mp, x.nh = nh, x.nstage = nstage;
     x.rows = rows, x.start = start, x.nt = nt;
-    if (32 * mp < rows)
-      dgemm_item<NMAT, true>(sm, a, x);
+    if (rows <= 32)  // one M block: every wavefront takes a quarter of the columns
+      dgemm_item<NMAT, 2, true>(sm, a, x);
+    else if (32 * mp < rows)
+      dgemm_item<NMAT, 4, true>(sm, a, x);
     else
-      dgemm_item<NMAT, false>(sm, a, x);
+      dgemm_item<NMAT, 4, false>(sm, a, x);
   }
 }
 
@@ -854,7 +866,7 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
   st = launch_group(a.keys, P, E + 1, a.counts, a.offsets, a.perm, s);
   if (st != MOE_OK) return st;
   {
-    launch(MOE_PROF_PLAN, prefill_items_kernel<kMT>, dim3(1), dim3(64), 0, s, a.counts, E + 1, a.items);
+    launch(MOE_PROF_PLAN, prefill_items_kernel<kMT>, dim3(1), dim3(64), 0, s, a.counts, a.offsets, E + 1, a.items);
     MOE_LAUNCH_CHECK();
   }
   // persistent grids, one workgroup per CU (each wavefront holds a SIMD's 512
@@ -920,7 +932,7 @@ moe_status launch_decode_mfma(const moe_layer* Lr, const void* x, int T, int k, 
   moe_status st = launch_group(a.keys, P, E + 1, a.counts, a.offsets, a.perm, s);
   if (st != MOE_OK) return st;
   {
-    launch(MOE_PROF_PLAN, prefill_items_kernel<kDMT>, dim3(1), dim3(64), 0, s, a.counts, E + 1, a.items);
+    launch(MOE_PROF_PLAN, prefill_items_kernel<kDMT>, dim3(1), dim3(64), 0, s, a.counts, a.offsets, E + 1, a.items);
     MOE_LAUNCH_CHECK();
   }
   const long max_items_m = (long)P / kDMT + std::min(P, E + 1) + 1;

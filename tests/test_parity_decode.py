@@ -581,14 +581,15 @@ def _batched_bf16_case(gpu_lib, T, E, k, with_shared, seed, H=512, I=256, bad_sl
     log(f"batched bf16 MFMA T={T} E={E} k={k} shared={with_shared}: ok over {len(list(tokens))} tokens")
 
 
+@pytest.mark.parametrize("I", [256, 512])   # 256: LDS-staged kernels; 512: register-direct kernels
 @pytest.mark.parametrize("T,E,k,with_shared,bad", [
     (2, 16, 4, True, 0),      # groups of one or two rows
     (37, 16, 4, True, 3),     # ragged groups, dropped ranks
     (70, 4, 3, True, 0),      # groups past 64 rows (two M tiles each), shared 70 rows
     (130, 2, 2, False, 0),    # no shared expert, three M tiles per group
 ])
-def test_batched_bf16_mfma_path(gpu_lib, T, E, k, with_shared, bad):
-    _batched_bf16_case(gpu_lib, T, E, k, with_shared, seed=300 + T, bad_slots=bad)
+def test_batched_bf16_mfma_path(gpu_lib, T, E, k, with_shared, bad, I):
+    _batched_bf16_case(gpu_lib, T, E, k, with_shared, seed=300 + T, bad_slots=bad, I=I)
 
 
 def test_layer_decode_b64_full_size(gpu_lib):
