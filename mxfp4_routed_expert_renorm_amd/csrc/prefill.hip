@@ -528,7 +528,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(PrefillArgs a) {
 // the 32 its FP4 piece covers; the activation fragment is read at the same K.
 
 constexpr int kDMT = 64;                      // grouped rows per item at most
-constexpr int kDKS = 128;                     // K per stage
+#ifndef MOE_DG_KS
+#define MOE_DG_KS 128
+#endif
+constexpr int kDKS = MOE_DG_KS;               // K per stage (128 or 256)
 constexpr int kDThreads = 256;                // 4 wavefronts
 constexpr int kDArow = 2 * kDKS + 16;         // padded bytes of a bf16 activation row per stage
 constexpr int kDBrow = kDKS / 2 + 16;         // padded bytes of an FP4 weight row per stage
@@ -548,17 +551,20 @@ constexpr int kDDepth = MOE_DG_DEPTH;         // K stages held in registers ahea
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
+// the stage's scale bytes of one weight row: one per 32 elements of K
+typedef std::conditional<kDKS == 256, uint64_t, uint32_t>::type DStageScales;
+
 struct alignas(16) DGemmSmem {
   uint8_t a[2][kDMT * kDArow];
   uint8_t b[2][kNR * kDBrow];
-  uint32_t bs[2][kDThreads];  // entry i: the stage's 4 scale bytes of weight row i
+  DStageScales bs[2][kDThreads];  // entry i: the stage's scale bytes of weight row i
   int32_t pm[kDMT];           // down: the (token, rank) pair of each tile row
 };
 
 struct DStageRegs {
   u32x4_t a[kDPiecesA];
   u32x4_t b[kDPiecesB];
-  uint32_t bs;
+  DStageScales bs;
 };
 
 struct DLoadOffs {
@@ -573,7 +579,7 @@ __device__ __forceinline__ void dstage_load(DStageRegs& r, const DLoadOffs& o, c
   for (int j = 0; j < kDPiecesA; ++j) r.a[j] = *(const u32x4_t*)(abase + (o.a[j] + 2 * k0));
 #pragma unroll
   for (int j = 0; j < kDPiecesB; ++j) r.b[j] = *(const u32x4_t*)(rec + (o.b[j] + k0 / 2));
-  r.bs = *(const uint32_t*)(rec + (o.bs + k0 / 32));
+  r.bs = *(const DStageScales*)(rec + (o.bs + k0 / 32));
 }
 
 __device__ __forceinline__ void dstage_store(DGemmSmem& sm, int buf, const DStageRegs& r, int tid) {
@@ -647,7 +653,7 @@ __device__ __forceinline__ void dgemm_item(DGemmSmem& sm, const PrefillArgs& a, 
           for (int j = 0; j < NBW; ++j) {
             const int r = dcol_block<NMAT, NBW>(cs, j) * 32 + c;
             q[j] = *(const u32x4_t*)(sm.b[buf] + r * kDBrow + kc * 32 + 16 * h);
-            sc[j] = e8m0_to_f32((sm.bs[buf][r] >> (8 * (2 * kc + h))) & 0xffu);
+            sc[j] = e8m0_to_f32((uint32_t)(sm.bs[buf][r] >> (8 * (2 * kc + h))) & 0xffu);
           }
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
@@ -892,8 +898,8 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
 }
 
 bool decode_mfma_ok(int H, int I) {
-  return H >= 256 && I >= 128 && H % 256 == 0 && I % 128 == 0 && (H / kDKS) % kDDepth == 0 &&
-         (I / kDKS) % kDDepth == 0;
+  return H >= 256 && I >= 128 && H % 256 == 0 && I % 128 == 0 && H % kDKS == 0 && I % kDKS == 0 &&
+         (H / kDKS) % kDDepth == 0 && (I / kDKS) % kDDepth == 0;
 }
 
 // Grouped decode of T >= 2 bf16 tokens on bf16 MFMA: plan (keys by slot, the
