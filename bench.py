@@ -39,17 +39,25 @@ def parse():
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
                     help="graph: the timed steps are captured into one HIP graph and replayed; "
                          "eager: one launch sequence per step from the host")
-    ap.add_argument("--workload", choices=("decode-b1", "decode-b64", "prefill", "slotcache"), default="decode-b1",
+    ap.add_argument("--workload", choices=("decode-b1", "decode-b64", "prefill", "slotcache", "slotcache-prefill"),
+                    default="decode-b1",
                     help="decode-b1 (default, the headline line): batch-1 decode of a resident 256-expert "
                          "layer; decode-b64: 64 tokens, top-6, Zipf-skewed routing, grouped by expert; "
                          "prefill: 4096 tokens, top-8, MXFP8 x MXFP4 scaled MFMA; "
-                         "slotcache: 512 tokens x 8 layers through the 512-slot cache with the (2,4) ladder")
+                         "slotcache: 512 tokens x 8 layers through the 512-slot cache with the (2,4) ladder; "
+                         "slotcache-prefill: 4096-token prompt chunks through the same 8 layers by whole-layer "
+                         "streaming into two layer buffers of the cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tp-share", type=int, default=1,
                     help="decode-b1 on rank 0's share of G-way tensor parallelism (experts cut along I)")
     ap.add_argument("--slot-tier", action="store_true",
                     help="slotcache workload with a 100-slot 2-bit device tier and LFU eviction "
                          "(decay 0.95, counts seeded from a separate 64-token routing trace)")
+    ap.add_argument("--prefetch", type=int, default=0, metavar="R",
+                    help="slotcache workload with an R-entry staging ring fed, two layers ahead, by "
+                         "12-expert predictions of controlled recall (computed before the timed loop)")
+    ap.add_argument("--prefetch-recall", type=float, default=0.75,
+                    help="share of the true top-k each prediction holds")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (known bytes for HBM counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -181,10 +189,18 @@ def main():
         print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X "
               "(no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if (args.prefetch or args.slot_tier) and args.workload != "slotcache":
+        print("--prefetch and --slot-tier apply to --workload slotcache", file=sys.stderr)
+        sys.exit(2)
+    if args.prefetch < 0:
+        print("--prefetch takes a ring size >= 0", file=sys.stderr)
+        sys.exit(2)
     if args.workload == "decode-b64":
         return bench_decode_b64(args)
     if args.workload == "slotcache":
         return bench_slotcache(args)
+    if args.workload == "slotcache-prefill":
+        return bench_slotcache_prefill(args)
     if args.workload == "prefill":
         return bench_prefill(args)
     return bench_decode_b1(args)
@@ -551,7 +567,8 @@ def bench_slotcache(args):
         W.int2_record(seed, W.S_INT2, p, H, I, out=int2_host.array[p * rb2:(p + 1) * rb2])
         if p % 256 == 255:
             print(f"[bench] {p + 1}/{L * E} host records", file=sys.stderr, flush=True)
-    arena = torch.empty(S * rb4, dtype=torch.uint8, device=dev)
+    R = args.prefetch
+    arena = torch.empty((S + R) * rb4, dtype=torch.uint8, device=dev)
     tier = {}
     if args.slot_tier:
         # LFU counts seeded from the picks of a separate 64-token trace, routed by the library
@@ -575,6 +592,22 @@ def bench_slotcache(args):
     out_d = torch.empty((T * L, H), dtype=torch.bfloat16, device=dev)
     ws = lib.expert_workspace(H, I, 1, k, False, device=dev)
     copy_stream = torch.cuda.Stream()
+    pf_stream = torch.cuda.Stream()
+    pred = {}
+    if R:
+        # The pages' predictor is a trained network (out of scope): stand-in predictions hold a
+        # seeded share of the true top-k of the call two layers ahead plus the experts ranked
+        # next, 12 in all, from the library's top-(k+12) routing before the timed loop.
+        tids_d = torch.empty((T * L, k + 12), dtype=torch.int32, device=dev)
+        tw_d = torch.empty((T * L, k + 12), dtype=torch.float32, device=dev)
+        lib.moe_route(lg_d, k + 12, tids_d, tw_d)
+        tids = tids_d.cpu().numpy().reshape(T, L, k + 12)
+        for t in range(T):
+            for l in range(L):
+                t2, l2 = t + (l + 2) // L, (l + 2) % L
+                if t2 < T:
+                    pred[(t, l)] = (l2, W.predicted_experts(seed, (t2, l2), tids[t2, l2], k, m=12,
+                                                            recall=args.prefetch_recall))
     # host-link peak for this copy pattern: 64 records back to back from the pinned bank
     src = torch.from_numpy(fp4_host.array[:64 * rb4])
     dst = arena[:64 * rb4]
@@ -588,7 +621,7 @@ def bench_slotcache(args):
     print(f"[bench] setup {time.time() - t0:.1f} s; pinned copy rate {h2d_peak:.1f} GB/s",
           file=sys.stderr, flush=True)
 
-    cache = lib.Cache(L, E, H, I, S, k, a, b, 1, fp4_host, int2_host, arena, staging, **tier)
+    cache = lib.Cache(L, E, H, I, S, k, a, b, 1, fp4_host, int2_host, arena, staging, prefetch_slots=R, **tier)
     layer = cache.layer()
     t_tok = []
     torch.cuda.synchronize()
@@ -596,6 +629,8 @@ def bench_slotcache(args):
     for t in range(T):
         for l in range(L):
             row = t * L + l
+            if (t, l) in pred:
+                cache.prefetch(*pred[(t, l)], copy=pf_stream)
             lib.moe_route(lg_d[row:row + 1], k, ids, w)
             cache.ensure(l, 1, ids, w, prec, copy=copy_stream)
             lib.moe_expert_forward(layer, x_d[row:row + 1], 1, k, ids, prec, w, out_d[row:row + 1], ws)
@@ -612,11 +647,16 @@ def bench_slotcache(args):
         "ms_per_step": round(elapsed / T * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp4+int2-w/bf16-x/f32-acc",
         "data": "synthetic (seeded; per-layer Zipf(1.1) logits, fresh activations per token and layer)",
-        "config": {"workload": cfg["name"] + ("-int2tier100-lfu" if tier else ""), "layers": L, "experts": E,
+        "config": {"workload": cfg["name"] + ("-int2tier100-lfu" if tier else "") + (f"-ring{R}" if R else ""),
+                   "layers": L, "experts": E,
                    "slots": S, "top_k": k, "ladder": [a, b], "tokens": T, "cold_start": True,
                    "int2_slots": tier.get("int2_slots", 0), "policy": tier.get("policy", "lru"),
                    "lfu_decay": tier.get("lfu_decay"),
-                   "lfu_seed": "64-token routing trace of a separate seed" if tier else None},
+                   "lfu_seed": "64-token routing trace of a separate seed" if tier else None,
+                   "prefetch_slots": R,
+                   "prediction": (f"12 experts: {int(round(args.prefetch_recall * k))} of the true top-{k} and "
+                                  "the experts ranked next, two layers ahead, precomputed from the routing "
+                                  "(stand-in for a trained predictor)") if R else None},
         "steady_state_ms_per_token": round(steady * 1e3, 4),
         "cache": {**st, "hit_rate": round(st["hits"] / uses, 4)},
         "h2d_GBps": round(st["bytes_h2d"] / elapsed / 1e9, 2),
@@ -626,6 +666,109 @@ def bench_slotcache(args):
     }
     fp4_host.free()
     int2_host.free()
+    print(json.dumps(result), flush=True)
+
+
+def bench_slotcache_prefill(args):
+    """Prompt chunks of 4096 tokens through the 8 slot-cached layers above the
+    prefill crossover (T * k >= E): per layer, route on the GPU, stream the
+    next layer's 256 experts from the pinned bank into the other layer buffer
+    of the cache (side stream, overlapping this layer's compute), then the
+    prefill GEMM on this layer's buffer.  Bound by the host link: 3.42 GB per
+    layer against a few ms of compute."""
+    import torch
+
+    from mxfp4_routed_expert_renorm_amd import binding as lib
+    from mxfp4_routed_expert_renorm_amd import workloads as W
+
+    ci = 4
+    cfg = W.CONFIGS[ci]
+    seed = W.config_seed(ci)
+    L, E, H, I, k, S = cfg["L"], cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["slots"]
+    T = 4096
+    chunks = max(1, min(args.steps, 4))
+    assert lib.moe_prefill_streams(T, k, E)
+    dev = torch.device("cuda:0")
+    rb4 = lib.moe_fp4_expert_bytes(H, I)
+    t0 = time.time()
+    print(f"[bench] pinning {L * E * rb4 / 1e9:.1f} GB of host bank", file=sys.stderr, flush=True)
+    fp4_host = lib.PinnedBuffer(L * E * rb4)
+    for p in range(L * E):
+        W.fp4_record(seed, W.S_BANK, p, H, I, out=fp4_host.array[p * rb4:(p + 1) * rb4])
+        if p % 256 == 255:
+            print(f"[bench] {p + 1}/{L * E} host records", file=sys.stderr, flush=True)
+    arena = torch.empty(S * rb4, dtype=torch.uint8, device=dev)
+    # per (chunk, layer): Zipf-skewed logits and bf16 activations, resident before timing
+    lg = W.slotcache_logits(seed + 7, L, E, (chunks + 1) * T, cfg["zipf"]).reshape(chunks + 1, T, L, E)
+    lg_d = torch.from_numpy(lg).to(dev)
+    x_d = torch.from_numpy(np.stack([W.bf16_normal(seed, (W.S_X, c, l), (T, H))
+                                     for c in range(chunks + 1) for l in range(L)])).to(dev).view(torch.bfloat16)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lib.moe_prefill_workspace_bytes(H, I, T, k, False), dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream()
+    cache = lib.Cache(L, E, H, I, S, k, k, k, 1, fp4_host, None, arena, None)
+    print(f"[bench] setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    lg_rows = lg_d.permute(0, 2, 1, 3).contiguous()                                   # [chunks+1, L, T, E]
+
+    def run(c_first, n):
+        calls = [(c, l) for c in range(c_first, c_first + n) for l in range(L)]
+        cache.stream_layer(calls[0][1], copy=copy_stream)
+        for i, (c, l) in enumerate(calls):
+            lib.moe_route(lg_rows[c, l], k, ids, w)
+            if i + 1 < len(calls):
+                cache.stream_layer(calls[i + 1][1], copy=copy_stream)
+            lay = cache.layer_buffer(l)
+            lib.moe_prefill_forward(lay, x_d[c * L + l], k, ids, w, out, ws)
+
+    run(0, 1)                                  # warm-up chunk
+    torch.cuda.synchronize()
+    b0 = cache.stats()["bytes_h2d"]
+    ta = time.perf_counter()
+    run(1, chunks)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - ta
+    st = cache.stats()
+    moved = st["bytes_h2d"] - b0
+    # the same chunk's compute alone, with every layer's buffer already streamed: the GEMM share
+    lib.moe_profile_begin(64 * L)
+    for l in range(2):
+        cache.stream_layer(l, copy=copy_stream)
+    torch.cuda.synchronize()
+    for l in range(2):
+        lib.moe_route(lg_rows[1, l], k, ids, w)
+        lib.moe_prefill_forward(cache.layer_buffer(l), x_d[L + l], k, ids, w, out, ws)
+    torch.cuda.synchronize()
+    prof = lib.moe_profile_end()
+    compute_ms = sum(v[0] for v in prof.values()) / 2
+    # host-link peak for this copy size: one layer's records in one copy
+    src = torch.from_numpy(fp4_host.array[:E * rb4])
+    tc = time.perf_counter()
+    with torch.cuda.stream(copy_stream):
+        arena[:E * rb4].copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    h2d_peak = E * rb4 / (time.perf_counter() - tc) / 1e9
+    cache.destroy()
+    fp4_host.free()
+    rate = moved / elapsed / 1e9
+    result = {
+        "metric": "prefill tokens/s through 8 slot-cached layers by whole-layer streaming (host-link bound)",
+        "value": round(chunks * T / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": chunks, "warmup": 1,
+        "ms_per_step": round(elapsed / chunks * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp8-x/mxfp4-w/f32-acc",
+        "data": "synthetic (seeded; per-layer Zipf(1.1) logits, fresh activations per chunk and layer)",
+        "config": {"workload": cfg["name"].replace("decode", "prefill-stream"), "layers": L, "experts": E,
+                   "slots": S, "top_k": k, "chunk_tokens": T, "layer_buffers": 2,
+                   "crossover": f"T*k >= E ({T}*{k} >= {E})"},
+        "h2d_bytes_per_chunk": int(moved / chunks),
+        "h2d_GBps": round(rate, 2),
+        "pinned_copy_GBps_measured": round(h2d_peak, 1),
+        "link_frac": round(rate / h2d_peak, 4),
+        "compute_ms_per_layer": round(compute_ms, 3),
+        "copy_ms_per_layer": round(E * rb4 / rate / 1e6, 3),
+        "cache": st,
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -267,6 +267,8 @@ typedef struct {
   int policy;                /* MOE_CACHE_LRU or MOE_CACHE_LFU: eviction rule of both tiers */
   double lfu_decay;          /* LFU: every pair's use count is multiplied by this at each call, 0 < d <= 1 */
   const float* lfu_seed;     /* LFU: host [L*E] initial use counts (e.g. a routing trace's), NULL = zeros */
+  int prefetch_slots;        /* R > 0: a staging ring of R more FP4 records at fp4_arena slots num_slots ..
+                                num_slots+R-1 (the arena then holds num_slots+R records) for moe_cache_prefetch */
 } moe_cache_desc;
 
 enum { MOE_CACHE_LRU = 0, MOE_CACHE_LFU = 1 };
@@ -274,6 +276,9 @@ enum { MOE_CACHE_LRU = 0, MOE_CACHE_LFU = 1 };
 typedef struct {
   int64_t calls, hits, misses, int2_uses, drops, bytes_h2d, evictions;
   int64_t int2_hits;         /* 2-bit uses served from the 2-bit tier without a copy */
+  int64_t prefetches;        /* records copied into the staging ring */
+  int64_t ring_hits;         /* FP4 uses served from the staging ring */
+  int64_t streamed;          /* records copied by whole-layer streaming */
 } moe_cache_stats;
 
 /* Validates the descriptor (slot floor num_slots >= E: [P1] §Step 7 fails early when the
@@ -311,10 +316,53 @@ moe_status moe_cache_plan(moe_cache* c, int layer, int T, const int32_t* ids, co
 moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, float* w_inout, int8_t* prec_out,
                             moe_stream_t compute, moe_stream_t copy);
 
+/* Speculative prefetch into the staging ring ([P2] §Guessing the router two layers ahead:
+ * predicted experts land in a small round-robin ring appended to the slot buffers, so a wrong
+ * guess never evicts a resident expert and is overwritten by a later prediction).  experts:
+ * host [n] predicted expert ids of `layer`, most likely first.  Each one neither in the cache
+ * nor in the ring is copied from the pinned bank to the ring entry at the cursor (which
+ * advances), skipping the entries the last moe_cache_ensure call used (its expert kernels may
+ * still read them; those of any earlier call have finished, since that ensure waited for its
+ * router's picks) and those this call has filled; once every free entry is filled the rest of
+ * the list is ignored.  The copies go on `copy`, and the next moe_cache_ensure makes its
+ * compute stream wait for them.  A later call finds a ring entry resident and uses it in place
+ * (slot num_slots + entry): no copy, no move into the cache.  Without a device arena only the
+ * policy runs.  Needs prefetch_slots > 0. */
+moe_status moe_cache_prefetch(moe_cache* c, int layer, int n, const int32_t* experts, moe_stream_t copy);
+
+/* The prefill crossover ([P1] §What the expert cache actually does, §Step 7): 1 when a
+ * chunk of T tokens with top-k over E experts should stream whole expert layers
+ * (T*k >= E: the chunk touches most of the layer anyway), 0 when it should fetch
+ * slots on demand through moe_cache_ensure. */
+int moe_prefill_streams(int T, int k, int E);
+
+/* Whole-layer streaming for prefill ([P1] §What the expert cache actually does: above
+ * the crossover prefill streams whole expert layers; §Step 7: with prefill overlapping
+ * the copies the cache lends two full expert-layer buffers, hence at least 2E slots).
+ * The buffers are slots [0, E) and [E, 2E), filled alternately starting with the first
+ * (*buffer gets 0 or 1, may be NULL).  Expert e of `layer` goes to slot bE + e: the
+ * slot's previous pair is evicted, the layer's pairs held elsewhere (a slot or the
+ * staging ring) give that place up, pairs already in place are not copied, and every
+ * streamed slot is stamped as just used (no LFU use).  The streamed experts stay
+ * resident.  Copies go on `copy` (one per run of consecutive experts) after the work
+ * already on `compute` (which may still read the buffer) and after the other buffer's
+ * pending copies; moe_cache_layer_buffer or the next moe_cache_ensure makes `compute`
+ * wait for them.  Without a device arena only the policy runs.
+ * Errors: MOE_ECACHE_SMALL when num_slots < 2E. */
+moe_status moe_cache_stream_layer(moe_cache* c, int layer, int* buffer, moe_stream_t compute, moe_stream_t copy);
+
+/* moe_layer descriptor (expert e in slot e, E slots, no 2-bit copies, no shared expert)
+ * of the layer buffer that holds every expert of `layer`, for moe_prefill_forward or
+ * moe_expert_forward with the router's expert ids; makes `compute` wait for that
+ * buffer's pending copies.  Errors: MOE_ESTATE when no buffer holds the whole layer
+ * (never streamed, or since overwritten). */
+moe_status moe_cache_layer_buffer(moe_cache* c, int layer, moe_stream_t compute, moe_layer* out);
+
 /* Host copy of the (layer, expert) -> slot map, [L*E] int32 (-1 = not resident). */
 moe_status moe_cache_slot_map(const moe_cache* c, int32_t* map_host);
 moe_status moe_cache_get_stats(const moe_cache* c, moe_cache_stats* out);
-/* moe_layer descriptor of the cache's device arena and 2-bit staging (no shared expert). */
+/* moe_layer descriptor of the cache's device arena (num_slots + prefetch_slots records) and
+ * 2-bit staging or tier (no shared expert). */
 moe_status moe_cache_layer(const moe_cache* c, moe_layer* out);
 
 /* ------------------------------------------------------------ timing */

@@ -43,6 +43,7 @@ class moe_cache_desc(ctypes.Structure):
         ("fp4_host", c_void_p), ("int2_host", c_void_p),
         ("fp4_arena", c_void_p), ("int2_staging", c_void_p),
         ("int2_slots", c_int), ("policy", c_int), ("lfu_decay", ctypes.c_double), ("lfu_seed", c_void_p),
+        ("prefetch_slots", c_int),
     ]
 
 
@@ -54,6 +55,7 @@ class moe_cache_stats(ctypes.Structure):
         ("calls", ctypes.c_int64), ("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
         ("int2_uses", ctypes.c_int64), ("drops", ctypes.c_int64),
         ("bytes_h2d", ctypes.c_int64), ("evictions", ctypes.c_int64), ("int2_hits", ctypes.c_int64),
+        ("prefetches", ctypes.c_int64), ("ring_hits", ctypes.c_int64), ("streamed", ctypes.c_int64),
     ]
 
 
@@ -85,6 +87,10 @@ _SIGS = {
     "moe_cache_reset": (c_int, [c_void_p]),
     "moe_cache_plan": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_cache_ensure": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_cache_prefetch": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p]),
+    "moe_prefill_streams": (c_int, [c_int, c_int, c_int]),
+    "moe_cache_stream_layer": (c_int, [c_void_p, c_int, ctypes.POINTER(c_int), c_void_p, c_void_p]),
+    "moe_cache_layer_buffer": (c_int, [c_void_p, c_int, c_void_p, ctypes.POINTER(moe_layer)]),
     "moe_cache_slot_map": (c_int, [c_void_p, c_void_p]),
     "moe_cache_get_stats": (c_int, [c_void_p, ctypes.POINTER(moe_cache_stats)]),
     "moe_cache_layer": (c_int, [c_void_p, ctypes.POINTER(moe_layer)]),
@@ -168,6 +174,11 @@ def moe_router_logits(x, w_router, logits, stream=None):
     _check("moe_router_logits", load().moe_router_logits(_p(x), _dt(x), _p(w_router), T, E, H, _p(logits),
                                                          _stream(stream)))
     return logits
+
+
+def moe_prefill_streams(T, k, E) -> bool:
+    """The prefill crossover: stream whole expert layers when T * k >= E."""
+    return bool(load().moe_prefill_streams(T, k, E))
 
 
 def moe_route(logits, k, ids, w, stream=None):
@@ -298,14 +309,17 @@ class Cache:
     caller; the handle keeps references to them, so they outlive it."""
 
     def __init__(self, L, E, H, I, num_slots, k, a, b, max_tokens=1, fp4_host=None, int2_host=None,
-                 fp4_arena=None, int2_staging=None, int2_slots=0, policy="lru", lfu_decay=1.0, lfu_seed=None):
-        """lfu_seed: host float32 array [L*E] of initial use counts (copied), or None."""
+                 fp4_arena=None, int2_staging=None, int2_slots=0, policy="lru", lfu_decay=1.0, lfu_seed=None,
+                 prefetch_slots=0):
+        """lfu_seed: host float32 array [L*E] of initial use counts (copied), or None.
+        prefetch_slots: staging-ring entries after the slots (fp4_arena then holds
+        num_slots + prefetch_slots records)."""
         import numpy as np
         seed = None if lfu_seed is None else np.ascontiguousarray(lfu_seed, dtype=np.float32).reshape(-1)
         d = moe_cache_desc(L, E, H, I, num_slots, k, a, b, max_tokens, _addr(fp4_host), _addr(int2_host),
                            _addr(fp4_arena), _addr(int2_staging), int2_slots,
                            {"lru": MOE_CACHE_LRU, "lfu": MOE_CACHE_LFU}[policy], lfu_decay,
-                           None if seed is None else seed.ctypes.data)
+                           None if seed is None else seed.ctypes.data, prefetch_slots)
         h = c_void_p()
         _check("moe_cache_create", load().moe_cache_create(ctypes.byref(d), ctypes.byref(h)))
         self.h, self.L, self.E, self.k = h, L, E, k
@@ -336,6 +350,34 @@ class Cache:
         st = load().moe_cache_ensure(self.h, layer, T, _p(ids_inout), _p(w_inout), _p(prec_out),
                                      _stream(compute), None if copy is None else _stream(copy))
         _check("moe_cache_ensure", st)
+
+    def prefetch(self, layer, experts, copy=None):
+        """Stage predicted experts (host int sequence, most likely first) of
+        `layer` into the ring; copies go on `copy` (a torch stream; None is the
+        null stream, and a cache without a device arena copies nothing)."""
+        import numpy as np
+        e = np.ascontiguousarray(np.asarray(experts, np.int32).reshape(-1))
+        st = load().moe_cache_prefetch(self.h, layer, int(e.size), _np_p(e) if e.size else None,
+                                       None if copy is None else _stream(copy))
+        _check("moe_cache_prefetch", st)
+
+    def stream_layer(self, layer, compute=None, copy=None, device=True):
+        """Stream every expert of `layer` into the next layer buffer; returns
+        the buffer (0 or 1).  device=False: a cache without a device arena
+        (policy only, no streams touched)."""
+        b = c_int(-1)
+        st = load().moe_cache_stream_layer(self.h, layer, ctypes.byref(b),
+                                           _stream(compute) if device else None,
+                                           (None if copy is None else _stream(copy)) if device else None)
+        _check("moe_cache_stream_layer", st)
+        return b.value
+
+    def layer_buffer(self, layer, compute=None) -> moe_layer:
+        lay = moe_layer()
+        _check("moe_cache_layer_buffer", load().moe_cache_layer_buffer(self.h, layer, _stream(compute),
+                                                                       ctypes.byref(lay)))
+        lay._tensors = self._buffers
+        return lay
 
     def slot_map(self):
         import numpy as np

@@ -26,6 +26,24 @@
 // operations in the same order as the oracle, so victims match exactly).
 // Without a 2-bit tier, 2-bit copies are copied per use into a staging area
 // at index t*(b-a) + (rank-a-1).
+//
+// "An elephant through a straw", §Guessing the router two layers ahead:
+// speculative copies of predicted experts land in a small staging ring after
+// the slots, filled round-robin, so a wrong guess never evicts a resident
+// expert.  Readings: a
+// ring entry counts as FP4-resident for classification; a call uses it in
+// place (slot S + entry, its LFU count grows, it takes no stamp and is not
+// moved into the cache); a prefetch skips the entries the last call used and
+// those it filled itself, and stops when no entry is free.
+//
+// "Running DeepSeek-V4-Flash across four free GPUs", §What the expert cache
+// actually does and §Step 7: above the crossover T*k >= E prefill streams
+// whole expert layers into two expert-layer buffers lent by the cache (so it
+// needs 2E slots).  Readings: the buffers are slots [0, E) and [E, 2E), filled
+// alternately; expert e lands in slot bE + e, evicting that slot's pair; the
+// layer's pairs held elsewhere (a slot or the ring) give that place up; pairs
+// already in place are not copied; each streamed slot takes the next clock
+// stamp, with no LFU use; the streamed experts stay resident.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -43,6 +61,14 @@ struct moe_cache {
   std::vector<int32_t> map2, owner2;  // the 2-bit tier, as map / owner
   std::vector<int64_t> stamp2;
   std::vector<double> count, seed;    // LFU use counts per pair, and their initial values
+  std::vector<int32_t> ring_owner, map_ring;  // staging ring: entry -> pair, pair -> entry
+  std::vector<uint8_t> ring_used, ring_now;   // entries the last call used / this call uses
+  int cursor = 0;
+  bool prefetch_pending = false;
+  hipEvent_t ev_prefetch = nullptr;
+  int next_buf = 0;                    // the layer buffer the next moe_cache_stream_layer fills
+  bool stream_pending[2] = {false, false};
+  hipEvent_t ev_stream[2] = {nullptr, nullptr}, ev_compute = nullptr;
   int64_t clock = 0;
   moe_cache_stats st{};
   // per-call scratch
@@ -106,6 +132,7 @@ moe_status plan(moe_cache* c, int layer, int T, const int32_t* ids, const float*
   c->copies.clear();
   c->prot.assign(S, 0);
   c->prot2.assign(c->owner2.size(), 0);
+  c->ring_now.assign(c->ring_owner.size(), 0);
   // validate everything before the state changes
   for (int i = 0; i < T * k; ++i)
     if (ids[i] < 0 || ids[i] >= E)
@@ -123,7 +150,8 @@ moe_status plan(moe_cache* c, int layer, int T, const int32_t* ids, const float*
     bool res[64];
     for (int r = 0; r < k; ++r) {
       const int rank = r + 1;
-      res[r] = c->map[(size_t)layer * E + id[r]] >= 0;  // snapshot before this token's fetches
+      const size_t pr = (size_t)layer * E + id[r];
+      res[r] = c->map[pr] >= 0 || (!c->map_ring.empty() && c->map_ring[pr] >= 0);  // snapshot before fetches
       if (rank <= a)
         cls[r] = 0;
       else if (rank <= b)
@@ -132,11 +160,19 @@ moe_status plan(moe_cache* c, int layer, int T, const int32_t* ids, const float*
         cls[r] = res[r] ? 0 : -1;
     }
     for (int r = 0; r < k; ++r)
-      if (cls[r] == 0 && res[r]) c->prot[c->map[(size_t)layer * E + id[r]]] = 1;
+      if (cls[r] == 0 && res[r] && c->map[(size_t)layer * E + id[r]] >= 0)
+        c->prot[c->map[(size_t)layer * E + id[r]]] = 1;
     for (int r = 0; r < k; ++r) {
       const int pair = layer * E + id[r];
       const size_t o = (size_t)t * k + r;
-      if (cls[r] == 0 && res[r]) {
+      if (cls[r] == 0 && res[r] && c->map[pair] < 0) {  // in the staging ring: used in place
+        const int q = c->map_ring[pair];
+        c->count[pair] += 1.0;
+        c->ring_now[q] = 1;
+        c->slots_h[o] = S + q;
+        c->prec_h[o] = 0;
+        c->st.ring_hits++;
+      } else if (cls[r] == 0 && res[r]) {
         const int s = c->map[pair];
         c->stamp[s] = use(c, pair);
         c->slots_h[o] = s;
@@ -193,7 +229,71 @@ moe_status plan(moe_cache* c, int layer, int T, const int32_t* ids, const float*
         if (c->prec_h[(size_t)t * k + r] >= 0)
           c->wout_h[(size_t)t * k + r] = (float)((double)w[(size_t)t * k + r] / tot);
   }
+  c->ring_used.swap(c->ring_now);
   c->st.calls++;
+  return MOE_OK;
+}
+
+// the staging-ring half of a prefetch: fills c->copies (kind 0, dest = slot)
+// the policy half of a layer stream: fills c->copies (kind 0, dest = slot), returns the buffer
+int plan_stream(moe_cache* c, int layer) {
+  const int E = c->d.E;
+  const int b = c->next_buf;
+  c->next_buf ^= 1;
+  c->copies.clear();
+  for (int e = 0; e < E; ++e) {
+    const int s = b * E + e, pair = layer * E + e;
+    if (c->owner[s] != pair) {
+      if (c->owner[s] >= 0) {
+        c->map[c->owner[s]] = -1;
+        c->st.evictions++;
+      }
+      const int old = c->map[pair];
+      if (old >= 0) {
+        c->owner[old] = -1;
+        c->stamp[old] = 0;
+      }
+      if (!c->map_ring.empty() && c->map_ring[pair] >= 0) {
+        c->ring_owner[c->map_ring[pair]] = -1;
+        c->map_ring[pair] = -1;
+      }
+      c->owner[s] = pair;
+      c->map[pair] = s;
+      c->copies.push_back({0, pair, s});
+      c->st.streamed++;
+    }
+    c->stamp[s] = ++c->clock;
+  }
+  return b;
+}
+
+moe_status plan_prefetch(moe_cache* c, int layer, int n, const int32_t* experts) {
+  const int E = c->d.E, S = c->d.num_slots, R = c->d.prefetch_slots;
+  c->copies.clear();
+  for (int i = 0; i < n; ++i)
+    if (experts[i] < 0 || experts[i] >= E)
+      return fail(MOE_EINVAL, "moe_cache_prefetch: expert id %d at position %d outside [0, %d)", experts[i], i, E);
+  std::vector<uint8_t> filled(R, 0);
+  for (int i = 0; i < n; ++i) {
+    const int pair = layer * E + experts[i];
+    if (c->map[pair] >= 0 || c->map_ring[pair] >= 0) continue;
+    int q = -1;
+    for (int j = 0; j < R; ++j) {
+      const int cand = (c->cursor + j) % R;
+      if (!c->ring_used[cand] && !filled[cand]) {
+        q = cand;
+        break;
+      }
+    }
+    if (q < 0) break;
+    if (c->ring_owner[q] >= 0) c->map_ring[c->ring_owner[q]] = -1;
+    c->ring_owner[q] = pair;
+    c->map_ring[pair] = q;
+    c->cursor = (q + 1) % R;
+    filled[q] = 1;
+    c->copies.push_back({0, pair, S + q});
+    c->st.prefetches++;
+  }
   return MOE_OK;
 }
 
@@ -253,6 +353,7 @@ moe_status moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
   if (int2 && d->int2_slots > 0 && (long)d->max_tokens * (d->ladder_b - d->ladder_a) > d->int2_slots)
     return fail(MOE_ECACHE_SMALL, "moe_cache_create: int2_slots=%d below max_tokens*(b-a)=%ld", d->int2_slots,
                 (long)d->max_tokens * (d->ladder_b - d->ladder_a));
+  if (d->prefetch_slots < 0) return fail(MOE_EINVAL, "moe_cache_create: prefetch_slots=%d", d->prefetch_slots);
   if (d->policy != MOE_CACHE_LRU && d->policy != MOE_CACHE_LFU)
     return fail(MOE_EINVAL, "moe_cache_create: policy=%d", d->policy);
   if (d->policy == MOE_CACHE_LFU && !(d->lfu_decay > 0.0 && d->lfu_decay <= 1.0))
@@ -276,6 +377,9 @@ moe_status moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
     for (size_t i = 0; i < c->seed.size(); ++i) c->seed[i] = (double)d->lfu_seed[i];
   c->count = c->seed;
   c->d.lfu_seed = nullptr;  // copied: the caller's array need not outlive the call
+  c->ring_owner.assign(d->prefetch_slots, -1);
+  c->ring_used.assign(d->prefetch_slots, 0);
+  if (d->prefetch_slots > 0) c->map_ring.assign((size_t)d->L * d->E, -1);
   *out = c;
   return MOE_OK;
 }
@@ -286,6 +390,9 @@ moe_status moe_cache_destroy(moe_cache* c) {
   if (c->pin_out) (void)hipHostFree(c->pin_out);
   if (c->ev_read) (void)hipEventDestroy(c->ev_read);
   if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
+  if (c->ev_prefetch) (void)hipEventDestroy(c->ev_prefetch);
+  for (hipEvent_t e : {c->ev_stream[0], c->ev_stream[1], c->ev_compute})
+    if (e) (void)hipEventDestroy(e);
   delete c;
   return MOE_OK;
 }
@@ -299,6 +406,13 @@ moe_status moe_cache_reset(moe_cache* c) {
   std::fill(c->owner2.begin(), c->owner2.end(), -1);
   std::fill(c->stamp2.begin(), c->stamp2.end(), 0);
   c->count = c->seed;
+  std::fill(c->ring_owner.begin(), c->ring_owner.end(), -1);
+  std::fill(c->ring_used.begin(), c->ring_used.end(), 0);
+  std::fill(c->map_ring.begin(), c->map_ring.end(), -1);
+  c->cursor = 0;
+  c->prefetch_pending = false;
+  c->next_buf = 0;
+  c->stream_pending[0] = c->stream_pending[1] = false;
   c->clock = 0;
   c->st = moe_cache_stats{};
   c->broken = false;
@@ -345,6 +459,12 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
   if (s != MOE_OK) return s;
   // from here on the host state has advanced: a failure leaves the cache inconsistent
   c->broken = true;
+  for (int b = 0; b < 2; ++b)  // streamed layer buffers: their copies precede any use or overwrite
+    if (c->stream_pending[b]) {
+      MOE_HIP_CHECK(hipStreamWaitEvent(cs, c->ev_stream[b], 0));
+      if (ps != cs) MOE_HIP_CHECK(hipStreamWaitEvent(ps, c->ev_stream[b], 0));
+      c->stream_pending[b] = false;
+    }
   for (const auto& cp : c->copies) {
     if (cp.kind == 0) {
       MOE_HIP_CHECK(hipMemcpyAsync(c->d.fp4_arena + (size_t)cp.dest * c->fp4_bytes,
@@ -362,6 +482,10 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
     MOE_HIP_CHECK(hipEventRecord(c->ev_copy, ps));
     MOE_HIP_CHECK(hipStreamWaitEvent(cs, c->ev_copy, 0));
   }
+  if (c->prefetch_pending) {  // ring entries this call may use were filled on the prefetch's stream
+    MOE_HIP_CHECK(hipStreamWaitEvent(cs, c->ev_prefetch, 0));
+    c->prefetch_pending = false;
+  }
   int32_t* slots_o = (int32_t*)c->pin_out;
   float* w_o = (float*)((char*)c->pin_out + (size_t)c->d.max_tokens * c->d.k * 4);
   int8_t* prec_o = (int8_t*)((char*)c->pin_out + (size_t)c->d.max_tokens * c->d.k * 8);
@@ -372,6 +496,99 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
   MOE_HIP_CHECK(hipMemcpyAsync(w_inout, w_o, n * 4, hipMemcpyHostToDevice, cs));
   MOE_HIP_CHECK(hipMemcpyAsync(prec_out, prec_o, n, hipMemcpyHostToDevice, cs));
   c->broken = false;
+  return MOE_OK;
+}
+
+moe_status moe_cache_prefetch(moe_cache* c, int layer, int n, const int32_t* experts, moe_stream_t copy) {
+  if (!c) return fail(MOE_EINVAL, "moe_cache_prefetch: handle is NULL");
+  if (c->broken) return fail(MOE_ESTATE, "moe_cache: an earlier ensure failed midway; reset the cache");
+  if (c->d.prefetch_slots <= 0) return fail(MOE_EINVAL, "moe_cache_prefetch: the cache has no staging ring");
+  if (layer < 0 || layer >= c->d.L) return fail(MOE_EINVAL, "moe_cache_prefetch: layer %d outside [0, %d)", layer, c->d.L);
+  if (n < 0 || (n > 0 && !experts)) return fail(MOE_EINVAL, "moe_cache_prefetch: n=%d experts=%p", n, (const void*)experts);
+  moe_status s = plan_prefetch(c, layer, n, experts);
+  if (s != MOE_OK) return s;
+  if (!c->d.fp4_arena || c->copies.empty()) return MOE_OK;
+  hipStream_t ps = (hipStream_t)copy;
+  if (!c->ev_prefetch) MOE_HIP_CHECK(hipEventCreateWithFlags(&c->ev_prefetch, hipEventDisableTiming));
+  // several prefetches before one ensure may use different streams: chain them, so the one
+  // event the ensure waits on covers every copy
+  if (c->prefetch_pending) MOE_HIP_CHECK(hipStreamWaitEvent(ps, c->ev_prefetch, 0));
+  for (const auto& cp : c->copies) {
+    MOE_HIP_CHECK(hipMemcpyAsync(c->d.fp4_arena + (size_t)cp.dest * c->fp4_bytes,
+                                 c->d.fp4_host + (size_t)cp.pair * c->fp4_bytes, c->fp4_bytes,
+                                 hipMemcpyHostToDevice, ps));
+    c->st.bytes_h2d += (int64_t)c->fp4_bytes;
+  }
+  MOE_HIP_CHECK(hipEventRecord(c->ev_prefetch, ps));
+  c->prefetch_pending = true;
+  return MOE_OK;
+}
+
+int moe_prefill_streams(int T, int k, int E) { return (int64_t)T * k >= (int64_t)E ? 1 : 0; }
+
+moe_status moe_cache_stream_layer(moe_cache* c, int layer, int* buffer, moe_stream_t compute, moe_stream_t copy) {
+  if (!c) return fail(MOE_EINVAL, "moe_cache_stream_layer: handle is NULL");
+  if (c->broken) return fail(MOE_ESTATE, "moe_cache: an earlier ensure failed midway; reset the cache");
+  if (layer < 0 || layer >= c->d.L)
+    return fail(MOE_EINVAL, "moe_cache_stream_layer: layer %d outside [0, %d)", layer, c->d.L);
+  const int E = c->d.E;
+  if (c->d.num_slots < 2 * E)
+    return fail(MOE_ECACHE_SMALL, "moe_cache_stream_layer: num_slots=%d is too small: two expert-layer buffers need %d",
+                c->d.num_slots, 2 * E);
+  const int b = plan_stream(c, layer);
+  if (buffer) *buffer = b;
+  if (!c->d.fp4_arena) return MOE_OK;
+  c->broken = true;
+  hipStream_t cs = (hipStream_t)compute, ps = copy ? (hipStream_t)copy : cs;
+  for (hipEvent_t* e : {&c->ev_stream[0], &c->ev_stream[1], &c->ev_compute})
+    if (!*e) MOE_HIP_CHECK(hipEventCreateWithFlags(e, hipEventDisableTiming));
+  if (ps != cs) {  // work already on the compute stream may still read the buffer
+    MOE_HIP_CHECK(hipEventRecord(c->ev_compute, cs));
+    MOE_HIP_CHECK(hipStreamWaitEvent(ps, c->ev_compute, 0));
+  }
+  if (c->stream_pending[b ^ 1]) MOE_HIP_CHECK(hipStreamWaitEvent(ps, c->ev_stream[b ^ 1], 0));
+  // runs of consecutive experts are contiguous in both the bank and the buffer: one copy each
+  const auto& cp = c->copies;
+  for (size_t i = 0; i < cp.size();) {
+    size_t j = i + 1;
+    while (j < cp.size() && cp[j].pair == cp[j - 1].pair + 1) ++j;
+    const size_t bytes = (j - i) * c->fp4_bytes;
+    MOE_HIP_CHECK(hipMemcpyAsync(c->d.fp4_arena + (size_t)cp[i].dest * c->fp4_bytes,
+                                 c->d.fp4_host + (size_t)cp[i].pair * c->fp4_bytes, bytes, hipMemcpyHostToDevice, ps));
+    c->st.bytes_h2d += (int64_t)bytes;
+    i = j;
+  }
+  MOE_HIP_CHECK(hipEventRecord(c->ev_stream[b], ps));
+  c->stream_pending[b] = true;
+  c->broken = false;
+  return MOE_OK;
+}
+
+moe_status moe_cache_layer_buffer(moe_cache* c, int layer, moe_stream_t compute, moe_layer* out) {
+  if (!c || !out) return fail(MOE_EINVAL, "moe_cache_layer_buffer: NULL argument");
+  if (layer < 0 || layer >= c->d.L)
+    return fail(MOE_EINVAL, "moe_cache_layer_buffer: layer %d outside [0, %d)", layer, c->d.L);
+  const int E = c->d.E;
+  int found = -1;
+  for (int b = 0; b < 2 && found < 0 && c->d.num_slots >= 2 * E; ++b) {
+    bool whole = true;
+    for (int e = 0; e < E && whole; ++e) whole = c->owner[b * E + e] == layer * E + e;
+    if (whole) found = b;
+  }
+  if (found < 0) return fail(MOE_ESTATE, "moe_cache_layer_buffer: layer %d is not whole in a layer buffer", layer);
+  if (c->stream_pending[found]) {
+    MOE_HIP_CHECK(hipStreamWaitEvent((hipStream_t)compute, c->ev_stream[found], 0));
+    c->stream_pending[found] = false;
+  }
+  out->H = c->d.H;
+  out->I = c->d.I;
+  out->fp4_base = c->d.fp4_arena ? c->d.fp4_arena + (size_t)found * E * c->fp4_bytes : nullptr;
+  out->fp4_stride = c->fp4_bytes;
+  out->num_slots = E;
+  out->int2_base = nullptr;
+  out->int2_stride = 0;
+  out->num_int2 = 0;
+  out->shared = nullptr;
   return MOE_OK;
 }
 
@@ -393,7 +610,7 @@ moe_status moe_cache_layer(const moe_cache* c, moe_layer* out) {
   out->I = c->d.I;
   out->fp4_base = c->d.fp4_arena;
   out->fp4_stride = c->fp4_bytes;
-  out->num_slots = c->d.num_slots;
+  out->num_slots = c->d.num_slots + c->d.prefetch_slots;
   const bool int2 = c->d.ladder_b > c->d.ladder_a;
   out->int2_base = int2 ? c->d.int2_staging : nullptr;
   out->int2_stride = c->int2_bytes;

@@ -29,7 +29,7 @@ import numpy as np
 
 # ----------------------------------------------------------------------------
 # stream keys (second element of every SeedSequence)
-S_BANK, S_SHARED, S_X, S_LOGITS, S_ROUTER_W, S_ZIPF, S_INT2, S_STEP = range(1, 9)
+S_BANK, S_SHARED, S_X, S_LOGITS, S_ROUTER_W, S_ZIPF, S_INT2, S_STEP, S_PRED = range(1, 10)
 
 # E8M0 exponent range of the synthetic FP4 scales (2^-8 .. 2^-4)
 FP4_EXP_LO, FP4_EXP_HI = 119, 123
@@ -200,3 +200,21 @@ def slotcache_logits(seed: int, L: int, E: int, T: int, s: float) -> np.ndarray:
 def slotcache_x(seed: int, t: int, l: int, H: int) -> np.ndarray:
     """Independent bf16 N(0,1) input of token t at layer l, [1, H]."""
     return bf16_normal(seed, (S_X, t, l), (1, H))
+
+
+def predicted_experts(seed: int, keys: tuple, ranked, k: int, m: int = 12, recall: float = 0.75) -> np.ndarray:
+    """A synthetic expert prediction of controlled recall for one (token,
+    layer), standing in for the pages' trained router predictor (it needs
+    trained weights; out of scope).  ranked: that call's experts in the
+    router's rank order, at least k + m long (the caller's top-(k+m) routing).
+    The prediction holds round(recall * k) of the first k (a seeded subset),
+    filled up to m ids with the experts ranked right after the first k (a
+    predictor's false positives are near misses, not uniform draws), in
+    ranked order."""
+    ranked = np.asarray(ranked, np.int64).reshape(-1)
+    n_true = int(round(recall * k))
+    assert 0 <= n_true <= min(k, m) and len(ranked) >= k + m - n_true
+    rng = rng_for(seed, S_PRED, *keys)
+    keep = set(rng.choice(ranked[:k], n_true, replace=False).tolist())
+    pred = [e for e in ranked[:k] if e in keep] + ranked[k:k + m - n_true].tolist()
+    return np.asarray(pred, np.int32)

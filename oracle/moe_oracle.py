@@ -462,11 +462,22 @@ class SlotCache:
         copy into a staging area, index t*(b-a) + (rank-a-1) within the call;
         int2_slots > 0: the 2-bit copy of a pair is looked up in the tier and
         fetched on a miss;
-      * if every rank of a token is dropped, all its weights are zero.
+      * if every rank of a token is dropped, all its weights are zero;
+      * prefetch (P2 §Guessing the router two layers ahead: predicted
+        experts land in a small round-robin staging ring appended to the slot
+        buffers, never evicting a resident expert; a wrong guess is
+        overwritten by a later one): each
+        predicted expert of the layer that is neither FP4-resident nor in the
+        ring is copied, in list order, to the ring entry at the cursor, which
+        then advances; entries the last call used are skipped, and so are
+        entries this prefetch has filled; ring entries are slots S .. S+R-1;
+      * a pair in the ring counts as FP4-resident when a token is classified
+        and is used in place (slot S + entry): no copy, no stamp, one use for
+        LFU; it is not moved into the cache.
     """
 
     def __init__(self, L: int, E: int, S: int, k: int, a: int, b: int, int2_slots: int = 0,
-                 policy: str = "lru", decay: float = 1.0, seed=None):
+                 policy: str = "lru", decay: float = 1.0, seed=None, ring: int = 0):
         assert 0 <= a <= b <= k and S >= 1 and int2_slots >= 0 and policy in ("lru", "lfu")
         self.L, self.E, self.S, self.k, self.a, self.b = L, E, S, k, a, b
         self.S2, self.policy, self.decay = int2_slots, policy, float(decay)
@@ -477,8 +488,16 @@ class SlotCache:
         self.owner2 = np.full(max(int2_slots, 1), -1, dtype=np.int64)
         self.stamp2 = np.zeros(max(int2_slots, 1), dtype=np.int64)
         self.count = (np.zeros(L * E) if seed is None else np.asarray(seed, np.float64).reshape(L * E).copy())
+        self.R = ring
+        self.ring_owner = np.full(max(ring, 1), -1, dtype=np.int64)   # entry -> pair
+        self.map_ring = np.full(L * E, -1, dtype=np.int64)            # pair -> entry
+        self.cursor = 0
+        self.ring_used = set()   # ring entries the last call used (compute may still read them)
         self.clock = 0
         self.hits = self.misses = self.int2 = self.drops = self.int2_hits = 0
+        self.prefetches = self.ring_hits = 0
+        self.next_buf = 0        # the layer buffer the next stream_layer fills
+        self.streamed = 0        # records copied by stream_layer
 
     def resident(self, layer: int, e: int) -> bool:
         return self.map[layer * self.E + e] >= 0
@@ -515,9 +534,10 @@ class SlotCache:
         prec = np.full((T, k), DROPPED, dtype=np.int8)
         wout = np.zeros((T, k), dtype=np.float64)
         copies = []
-        protected, protected2 = set(), set()
+        protected, protected2, ring_used = set(), set(), set()
         for t in range(T):
-            res = [self.resident(layer, int(e)) for e in ids[t]]      # snapshot
+            res = [self.resident(layer, int(e)) or self.map_ring[layer * E + int(e)] >= 0
+                   for e in ids[t]]                                      # snapshot
             cls = []
             for r in range(k):
                 rank = r + 1
@@ -528,12 +548,18 @@ class SlotCache:
                 else:
                     cls.append(FP4 if res[r] else DROPPED)
             for r in range(k):
-                if cls[r] == FP4 and res[r]:
+                if cls[r] == FP4 and res[r] and self.map[layer * E + int(ids[t, r])] >= 0:
                     protected.add(int(self.map[layer * E + int(ids[t, r])]))
             for r in range(k):
                 e = int(ids[t, r])
                 pair = layer * E + e
-                if cls[r] == FP4 and res[r]:
+                if cls[r] == FP4 and res[r] and self.map[pair] < 0:     # in the staging ring
+                    q = int(self.map_ring[pair])
+                    self.count[pair] += 1.0
+                    ring_used.add(q)
+                    slot[t, r], prec[t, r] = self.S + q, FP4
+                    self.ring_hits += 1
+                elif cls[r] == FP4 and res[r]:
                     s = int(self.map[pair])
                     self.stamp[s] = self._use(pair)
                     slot[t, r], prec[t, r] = s, FP4
@@ -576,7 +602,86 @@ class SlotCache:
             tot = w[t][keep].sum()
             if tot > 0:
                 wout[t][keep] = w[t][keep] / tot
+        self.ring_used = ring_used
         return slot, prec, wout, copies
+
+    def prefetch(self, layer: int, experts):
+        """Copy the predicted experts of `layer` that are neither resident nor
+        in the ring into the ring.  Returns the copies, as step() does."""
+        copies = []
+        filled = set()
+        for e in experts:
+            e = int(e)
+            pair = layer * self.E + e
+            if self.map[pair] >= 0 or self.map_ring[pair] >= 0:
+                continue
+            q = None
+            for i in range(self.R):
+                cand = (self.cursor + i) % self.R
+                if cand not in self.ring_used and cand not in filled:
+                    q = cand
+                    break
+            if q is None:
+                break
+            old = int(self.ring_owner[q])
+            if old >= 0:
+                self.map_ring[old] = -1
+            self.ring_owner[q] = pair
+            self.map_ring[pair] = q
+            self.cursor = (q + 1) % self.R
+            filled.add(q)
+            copies.append(("fp4", layer, e, self.S + q))
+            self.prefetches += 1
+        return copies
+
+    def stream_layer(self, layer: int):
+        """Whole-layer streaming for prefill.  P1 §What the expert cache
+        actually does: above the crossover (prefill_streams) prefill streams
+        whole expert layers instead of fetching slots on demand; P1 §Step 7:
+        with prefill overlap the cache lends two full expert-layer buffers,
+        so it needs at least 2E slots.
+
+        Readings where the pages are silent: the two buffers are slots [0, E)
+        and [E, 2E), filled alternately starting with the first; expert e of
+        the layer lands in slot bE + e, whose previous pair is evicted; a pair
+        of the layer held elsewhere (another slot or the staging ring) gives
+        that place up; a pair already in its buffer slot is not copied again;
+        every streamed slot takes the next clock stamp, in expert order, and
+        no LFU use; the streamed experts stay resident afterwards.
+        Returns (buffer, copies) with copies as step() gives them."""
+        E = self.E
+        assert self.S >= 2 * E, "layer streaming needs two expert-layer buffers"
+        b = self.next_buf
+        self.next_buf ^= 1
+        copies = []
+        for e in range(E):
+            s, pair = b * E + e, layer * E + e
+            if self.owner[s] != pair:
+                if self.owner[s] >= 0:
+                    self.map[self.owner[s]] = -1
+                old = int(self.map[pair])
+                if old >= 0:
+                    self.owner[old] = -1
+                    self.stamp[old] = 0
+                q = int(self.map_ring[pair])
+                if q >= 0:
+                    self.ring_owner[q] = -1
+                    self.map_ring[pair] = -1
+                self.owner[s] = pair
+                self.map[pair] = s
+                copies.append(("fp4", layer, e, s))
+                self.streamed += 1
+            self.clock += 1
+            self.stamp[s] = self.clock
+        return b, copies
 
     def slot_map(self) -> np.ndarray:
         return self.map.astype(np.int32).copy()
+
+
+def prefill_streams(T: int, k: int, E: int) -> bool:
+    """P1 §What the expert cache actually does and §Step 7: a prefill chunk
+    of T tokens streams whole expert layers once T * top_k >= num_experts
+    (it would touch most of the layer anyway); below that it fetches slots on
+    demand."""
+    return T * k >= E

@@ -36,6 +36,29 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def _struct_fields(name):
+    """Field names of a typedef'd struct in the headers, in declaration order."""
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        m = re.search(r"typedef struct\s*\{([^}]*)\}\s*" + name + r"\s*;", src)
+        if m:
+            fields = []
+            for decl in m.group(1).split(";"):
+                decl = decl.strip()
+                if decl:
+                    head, *rest = decl.split(",")
+                    fields.append(re.findall(r"(\w+)\s*$", head)[0])
+                    fields += [r.strip().lstrip("*").strip() for r in rest]
+            return fields
+    raise AssertionError(name)
+
+
+@pytest.mark.parametrize("cname,pyname", [("moe_layer", "moe_layer"), ("moe_cache_desc", "moe_cache_desc"),
+                                          ("moe_cache_stats", "moe_cache_stats")])
+def test_binding_structs_match_header(cname, pyname):
+    assert [f for f, _ in getattr(B, pyname)._fields_] == _struct_fields(cname)
+
+
 def test_sizes_match_pages(lib):
     assert lib.moe_fp4_expert_bytes(4096, 2048) == 13369344
     assert lib.moe_int2_expert_bytes(4096, 2048) == 7077888

@@ -17,14 +17,35 @@ def _route_all(logits, k):
     return ids.reshape(T, L, k), w.astype(np.float32).reshape(T, L, k)
 
 
-def _compare_trace(L, E, S, k, a, b, ids, w, T_call=1, int2_slots=0, policy="lru", decay=1.0, seed=None):
+def _predictions(logits, k, recall, m=12, ahead=2, seed=5):
+    """pred[(t, l)]: the seeded prediction made at call (t, l) for the call
+    `ahead` layers later (the next token's layers past the last one), from
+    the oracle's top-(k+m) ranking of that call."""
+    T, L, E = logits.shape
+    ranked, _ = O.route(logits.reshape(T * L, E), k + m)
+    ranked = ranked.reshape(T, L, k + m)
+    pred = {}
+    for t in range(T):
+        for l in range(L):
+            t2, l2 = t + (l + ahead) // L, (l + ahead) % L
+            if t2 < T:
+                pred[(t, l)] = (l2, W.predicted_experts(seed, (t2, l2), ranked[t2, l2], k, m=m, recall=recall))
+    return pred
+
+
+def _compare_trace(L, E, S, k, a, b, ids, w, T_call=1, int2_slots=0, policy="lru", decay=1.0, seed=None,
+                   ring=0, pred=None):
     c = B.Cache(L, E, 4096, 2048, S, k, a, b, max_tokens=T_call, int2_slots=int2_slots, policy=policy,
-                lfu_decay=decay, lfu_seed=seed)
-    oc = O.SlotCache(L, E, S, k, a, b, int2_slots=int2_slots, policy=policy, decay=decay, seed=seed)
+                lfu_decay=decay, lfu_seed=seed, prefetch_slots=ring)
+    oc = O.SlotCache(L, E, S, k, a, b, int2_slots=int2_slots, policy=policy, decay=decay, seed=seed, ring=ring)
     T = ids.shape[0]
     try:
         for t0 in range(0, T, T_call):
             for l in range(L):
+                if pred is not None and (t0, l) in pred:
+                    l2, p = pred[(t0, l)]
+                    c.prefetch(l2, p)
+                    oc.prefetch(l2, p)
                 ii = ids[t0:t0 + T_call, l]
                 ww = w[t0:t0 + T_call, l]
                 slots, prec, wo = c.plan(l, ii, ww)
@@ -36,6 +57,7 @@ def _compare_trace(L, E, S, k, a, b, ids, w, T_call=1, int2_slots=0, policy="lru
         st = c.stats()
         assert (st["hits"], st["misses"], st["int2_uses"], st["drops"]) == (oc.hits, oc.misses, oc.int2, oc.drops)
         assert st["int2_hits"] == oc.int2_hits
+        assert (st["prefetches"], st["ring_hits"]) == (oc.prefetches, oc.ring_hits)
         return st
     finally:
         c.destroy()
@@ -139,3 +161,109 @@ def test_tier_validation():
         B.Cache(2, 8, 256, 128, 8, 4, 1, 3, max_tokens=2, int2_slots=3)
     with pytest.raises(B.MoeError, match="lfu_decay"):
         B.Cache(2, 8, 256, 128, 8, 4, 1, 3, policy="lfu", lfu_decay=0.0)
+
+
+@pytest.mark.parametrize("policy,int2_slots,ring,recall", [
+    ("lru", 0, 24, 0.75),
+    ("lru", 0, 8, 0.5),
+    ("lfu", 10, 36, 1.0),
+    ("lfu", 0, 24, 0.0),
+])
+def test_slotcache_prefetch_bit_exact(policy, int2_slots, ring, recall):
+    """Speculative prefetch two layers ahead into the staging ring, with
+    predictions of controlled recall, against the oracle's replay: the ring
+    entries (slots S..S+R-1) every use lands in, the cache map and the counts."""
+    L, E, k, S, T = 4, 48, 6, 60, 60
+    rng = np.random.default_rng(ring * 3 + int2_slots)
+    logits = rng.standard_normal((T, L, E)).astype(np.float32)
+    logits += W.zipf_bias(13, (1,), E, 1.1)[None, None, :]
+    ids, w = _route_all(logits, k)
+    st = _compare_trace(L, E, S, k, 2, 4, ids, w, int2_slots=int2_slots, policy=policy, decay=0.95, ring=ring,
+                        pred=_predictions(logits, k, recall))
+    assert st["prefetches"] > 0
+    if recall > 0:
+        assert st["ring_hits"] > 0
+
+
+def test_slotcache_full_trace_with_prefetch():
+    """The slot-cache decode trace at full shape with a 32-entry ring fed by
+    12-expert predictions holding 75% of the true top-6, two layers ahead."""
+    cfg = W.CONFIGS[4]
+    L, E, k, S, (a, b), T = cfg["L"], cfg["E"], cfg["k"], cfg["slots"], cfg["ladder"], cfg["T"]
+    logits = W.slotcache_logits(W.config_seed(4), L, E, T, cfg["zipf"])
+    ids, w = _route_all(logits, k)
+    st = _compare_trace(L, E, S, k, a, b, ids, w, ring=32, pred=_predictions(logits, k, 0.75))
+    assert st["ring_hits"] > 0
+
+
+def test_prefetch_validation():
+    c = B.Cache(2, 8, 256, 128, 8, 4, 1, 3)
+    try:
+        with pytest.raises(B.MoeError, match="staging ring"):
+            c.prefetch(0, [1])
+    finally:
+        c.destroy()
+    with pytest.raises(B.MoeError, match="prefetch_slots"):
+        B.Cache(2, 8, 256, 128, 8, 4, 1, 3, prefetch_slots=-1)
+    c = B.Cache(2, 8, 256, 128, 8, 4, 1, 3, prefetch_slots=2)
+    try:
+        with pytest.raises(B.MoeError, match="outside"):
+            c.prefetch(0, [8])
+        with pytest.raises(B.MoeError, match="layer"):
+            c.prefetch(2, [1])
+        c.prefetch(0, [])
+        assert c.stats()["prefetches"] == 0
+    finally:
+        c.destroy()
+
+
+@pytest.mark.parametrize("policy,ring", [("lru", 0), ("lfu", 6)])
+def test_stream_layer_bit_exact(policy, ring):
+    """Whole-layer streaming interleaved with decode calls and prefetches:
+    the buffer each stream fills, the slot map after every operation and the
+    counters match the oracle's replay."""
+    L, E, k, S, T = 4, 16, 4, 40, 40
+    rng = np.random.default_rng(21 + ring)
+    logits = rng.standard_normal((T, L, E)).astype(np.float32)
+    ids, w = _route_all(logits, k)
+    c = B.Cache(L, E, 512, 256, S, k, 1, 3, policy=policy, lfu_decay=0.9, prefetch_slots=ring)
+    oc = O.SlotCache(L, E, S, k, 1, 3, policy=policy, decay=0.9, ring=ring)
+    try:
+        for t in range(T):
+            for l in range(L):
+                op = rng.integers(0, 6)
+                if op == 0:
+                    ls = int(rng.integers(0, L))
+                    assert c.stream_layer(ls, device=False) == oc.stream_layer(ls)[0]
+                elif op == 1 and ring:
+                    p = rng.choice(E, 5, replace=False)
+                    c.prefetch(l, p)
+                    oc.prefetch(l, p)
+                slots, prec, wo = c.plan(l, ids[t, l][None], w[t, l][None])
+                oslots, oprec, owo, _ = oc.step(l, ids[t, l][None], w[t, l][None].astype(np.float64))
+                assert np.array_equal(slots, oslots) and np.array_equal(prec, oprec), (t, l)
+                assert np.array_equal(c.slot_map(), oc.slot_map()), (t, l)
+        st = c.stats()
+        assert (st["hits"], st["misses"], st["streamed"], st["ring_hits"]) == \
+            (oc.hits, oc.misses, oc.streamed, oc.ring_hits)
+        assert st["streamed"] > 0
+    finally:
+        c.destroy()
+
+
+def test_stream_layer_validation():
+    assert B.moe_prefill_streams(32, 8, 256) and not B.moe_prefill_streams(31, 8, 256)
+    c = B.Cache(2, 8, 256, 128, 15, 4, 1, 3)
+    try:
+        with pytest.raises(B.MoeError, match="two expert-layer buffers"):
+            c.stream_layer(0, device=False)
+    finally:
+        c.destroy()
+    c = B.Cache(2, 8, 256, 128, 16, 4, 1, 3)
+    try:
+        with pytest.raises(B.MoeError, match="layer"):
+            c.stream_layer(2, device=False)
+        assert c.stream_layer(1, device=False) == 0 and c.stream_layer(0, device=False) == 1
+        assert c.stats()["streamed"] == 16
+    finally:
+        c.destroy()

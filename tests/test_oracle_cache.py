@@ -202,3 +202,115 @@ def test_default_tier_arguments_keep_the_plain_cache():
                                   np.array([[0.4, 0.3, 0.2, 0.1][:k]]))
         assert slot[0].tolist() == [int(v) for v in row[2].split(",")]
         assert prec[0].tolist() == [int(v) for v in row[3].split(",")]
+
+
+# ------------------------------------------------ staging ring, by hand
+
+def test_staging_ring_hand_worked():
+    """Two slots, a two-entry ring, ladder (1,1): rank 1 always FP4, rank 2
+    used only when resident.  Worked by hand from the ring's rule: entries
+    from the cursor round-robin, skipping those the last call used and those
+    this prefetch filled; ring pairs count as resident and are used in place."""
+    c = O.SlotCache(1, 8, 2, 2, 1, 1, ring=2)
+    w = np.array([[0.75, 0.25]])
+    cp = c.prefetch(0, [3, 4, 5])             # 3 -> entry 0, 4 -> entry 1, 5: no free entry
+    assert cp == [("fp4", 0, 3, 2), ("fp4", 0, 4, 3)]
+    slot, prec, wout, cp = c.step(0, np.array([[3, 4]]), w)
+    assert slot.tolist() == [[2, 3]] and prec.tolist() == [[O.FP4, O.FP4]] and cp == []
+    assert np.allclose(wout, w) and c.ring_hits == 2 and c.misses == 0 and np.all(c.slot_map() == -1)
+    assert c.prefetch(0, [5]) == []           # both entries were used by the last call
+    slot, prec, wout, cp = c.step(0, np.array([[5, 6]]), w)  # 5 misses into slot 0, 6 is dropped
+    assert slot.tolist() == [[0, -1]] and prec.tolist() == [[O.FP4, O.DROPPED]]
+    assert cp == [("fp4", 0, 5, 0)] and np.allclose(wout, [[1.0, 0.0]])
+    cp = c.prefetch(0, [6, 5, 7])             # 6 replaces 3 in entry 0; 5 is cached; 7 replaces 4
+    assert cp == [("fp4", 0, 6, 2), ("fp4", 0, 7, 3)]
+    slot, prec, _, cp = c.step(0, np.array([[3, 6]]), w)     # 3 left the ring: a miss into slot 1
+    assert slot.tolist() == [[1, 2]] and prec.tolist() == [[O.FP4, O.FP4]] and cp == [("fp4", 0, 3, 1)]
+    assert c.prefetches == 4 and c.ring_hits == 3 and c.misses == 2
+    # the cursor stands at entry 0 again; entry 0 (used by the last call) is skipped
+    assert c.prefetch(0, [1, 2]) == [("fp4", 0, 1, 3)]
+
+
+def test_ring_without_prefetch_is_the_plain_cache():
+    rows = read_golden("slotcache_trace.txt")
+    hdr = dict(kv.split("=") for kv in rows[0])
+    L, E, S, k, a, b = (int(hdr[n]) for n in ("L", "E", "S", "k", "a", "b"))
+    c = O.SlotCache(L, E, S, k, a, b, ring=4)
+    for row in rows[1:]:
+        slot, prec, _, _ = c.step(int(row[0]), np.array([[int(v) for v in row[1].split(",")]]),
+                                  np.array([[0.4, 0.3, 0.2, 0.1][:k]]))
+        assert slot[0].tolist() == [int(v) for v in row[2].split(",")]
+        assert prec[0].tolist() == [int(v) for v in row[3].split(",")]
+
+
+def test_perfect_prediction_leaves_no_miss():
+    """A ring of 2k entries always has k entries the last call did not use, so
+    predicting each call's exact picks turns every non-resident pick into a
+    ring hit: no misses, no 2-bit copies, no drops, whatever the ladder."""
+    L, E, S, k, T = 4, 64, 8, 6, 60
+    rng = np.random.default_rng(7)
+    c = O.SlotCache(L, E, S, k, 2, 4, ring=2 * k)
+    for t in range(T):
+        for l in range(L):
+            ids = rng.choice(E, k, replace=False)
+            c.prefetch(l, ids[::-1])
+            slot, prec, _, cp = c.step(l, ids[None, :], np.full((1, k), 1.0 / k))
+            assert cp == [] and np.all(prec == O.FP4)
+            for e, s in zip(ids, slot[0]):             # every slot holds the pair it serves
+                owner = c.owner[s] if s < S else c.ring_owner[s - S]
+                assert owner == l * E + e
+    assert c.misses == 0 and c.int2 == 0 and c.drops == 0 and c.ring_hits > 0
+
+
+def test_ring_invariants_random():
+    """Random predictions of mixed quality: the ring and the cache never hold
+    the same pair, maps and owners agree, and every FP4 use points at a slot
+    or ring entry that holds its pair."""
+    L, E, S, k, R = 3, 32, 10, 4, 6
+    rng = np.random.default_rng(11)
+    c = O.SlotCache(L, E, S, k, 1, 3, ring=R, policy="lfu", decay=0.9)
+    for t in range(200):
+        l = t % L
+        c.prefetch(l, rng.choice(E, 7, replace=False))
+        ids = rng.choice(E, k, replace=False)
+        slot, prec, _, _ = c.step(l, ids[None, :], rng.random((1, k)))
+        for e, s, p in zip(ids, slot[0], prec[0]):
+            if p == O.FP4:
+                owner = c.owner[s] if s < S else c.ring_owner[s - S]
+                assert owner == l * E + e
+        for pair in range(L * E):
+            assert not (c.map[pair] >= 0 and c.map_ring[pair] >= 0)
+            if c.map_ring[pair] >= 0:
+                assert c.ring_owner[c.map_ring[pair]] == pair
+        assert len(c.ring_used) <= R
+    assert c.ring_hits > 0 and c.prefetches > 0
+
+
+# ------------------------------------------------ whole-layer streaming, by hand
+
+def test_stream_layer_hand_worked():
+    """Three experts per layer, six slots (two layer buffers), a two-entry
+    ring.  Worked by hand from the streaming rule: buffers alternate from the
+    first, expert e of the layer lands in slot bE + e, displaced pairs are
+    evicted, the layer's pairs held elsewhere give their place up, pairs
+    already in their buffer slot are not copied."""
+    c = O.SlotCache(2, 3, 6, 2, 2, 2, ring=2)
+    w = np.array([[0.5, 0.5]])
+    c.step(1, np.array([[0, 2]]), w)          # pairs 3, 5 -> slots 0, 1 (clock 1, 2)
+    c.prefetch(0, [1])                        # pair 1 -> ring entry 0 (slot 6)
+    b, cp = c.stream_layer(0)                 # buffer 0: pairs 0, 1, 2 -> slots 0, 1, 2
+    assert b == 0 and cp == [("fp4", 0, 0, 0), ("fp4", 0, 1, 1), ("fp4", 0, 2, 2)]
+    assert c.slot_map().tolist() == [0, 1, 2, -1, -1, -1]      # pairs 3 and 5 evicted
+    assert c.ring_owner[0] == -1 and c.map_ring[1] == -1      # pair 1 left the ring
+    assert c.stamp[:3].tolist() == [3, 4, 5] and c.count.sum() == 2.0
+    b, cp = c.stream_layer(1)                 # buffer 1: pairs 3, 4, 5 -> slots 3, 4, 5
+    assert b == 1 and [d for _, _, _, d in cp] == [3, 4, 5]
+    slot, prec, _, cp = c.step(0, np.array([[2, 0]]), w)      # the streamed layer is resident
+    assert slot.tolist() == [[2, 0]] and cp == [] and c.hits == 2
+    b, cp = c.stream_layer(0)                 # buffer 0 again: already in place, no copies
+    assert b == 0 and cp == [] and c.streamed == 6
+    c.stream_layer(0)                         # buffer 1 gets layer 0: slots 0..2 are freed
+    assert c.slot_map().tolist() == [3, 4, 5, -1, -1, -1]
+    assert c.owner[:3].tolist() == [-1, -1, -1] and c.stamp[:3].tolist() == [0, 0, 0]
+    slot, _, _, cp = c.step(1, np.array([[1, 2]]), w)        # misses take the freed slots 0, 1
+    assert slot.tolist() == [[0, 1]] and [d for _, _, _, d in cp] == [0, 1]

@@ -135,3 +135,8 @@ def test_page_constants():
     assert abs(4080 / 43 - v) <= tol
     v, tol = c["prefill_crossover_tokens"]
     assert math.ceil(E / 8) == v
+    assert min(T for T in range(1, 300) if O.prefill_streams(T, 8, E)) == v
+    v, tol = c["stream_min_slots"]
+    O.SlotCache(1, E, int(v), 8, 8, 8).stream_layer(0)
+    with pytest.raises(AssertionError):
+        O.SlotCache(1, E, int(v) - 1, 8, 8, 8).stream_layer(0)

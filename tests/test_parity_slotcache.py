@@ -14,18 +14,31 @@ from tests.gpu_util import TOL_BF16_MAX_REL, bf16_dev, dev, log, max_rel
 pytestmark = pytest.mark.gpu
 
 
-def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1, **tier):
+def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1, recall=None, m=12, **tier):
+    """recall: with tier["prefetch_slots"] > 0, every call first prefetches a
+    prediction of this recall (m experts) for the call two layers ahead."""
     import torch
     lib = gpu_lib
     rb4, rb2 = O.fp4_expert_nbytes(H, I), O.int2_expert_nbytes(H, I)
+    R = tier.get("prefetch_slots", 0)
     logits = W.slotcache_logits(seed, L, E, T, zipf)                 # [T, L, E]
+    routes = {(t, l): O.route(logits[t, l][None, :], k) for t in range(T) for l in range(L)}
+    pred = {}
+    if R:
+        for t in range(T):
+            for l in range(L):
+                t2, l2 = t + (l + 2) // L, (l + 2) % L
+                if t2 < T:
+                    ranked = O.route(logits[t2, l2][None, :], k + m)[0][0]
+                    pred[(t, l)] = (l2, W.predicted_experts(seed, (t2, l2), ranked, k, m=m, recall=recall))
     # the oracle's own trace tells which host records are ever read
     oc0 = O.SlotCache(L, E, S, k, a, b, **_oracle_tier(tier))
     need4, need2 = set(), set()
     for t in range(T):
         for l in range(L):
-            oids, ow = O.route(logits[t, l][None, :], k)
-            for kind, ll, e, _ in oc0.step(l, oids, ow)[3]:
+            cps = oc0.prefetch(*pred[(t, l)]) if (t, l) in pred else []
+            oids, ow = routes[(t, l)]
+            for kind, ll, e, _ in cps + oc0.step(l, oids, ow)[3]:
                 (need4 if kind == "fp4" else need2).add(ll * E + e)
     log(f"slot cache L={L} E={E} H={H} I={I} S={S} k={k} ladder=({a},{b}) T={T}: "
         f"{len(need4)} FP4 and {len(need2)} 2-bit records read")
@@ -35,7 +48,7 @@ def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1, **tier
         W.fp4_record(seed, W.S_BANK, p, H, I, out=fp4_host.array[p * rb4:(p + 1) * rb4])
     for p in need2:
         W.int2_record(seed, W.S_INT2, p, H, I, out=int2_host.array[p * rb2:(p + 1) * rb2])
-    arena = torch.empty(S * rb4, dtype=torch.uint8, device="cuda")
+    arena = torch.empty((S + R) * rb4, dtype=torch.uint8, device="cuda")
     n2 = tier.get("int2_slots", 0) or max(1, b - a)
     staging = torch.empty(n2 * rb2, dtype=torch.uint8, device="cuda") if b > a else None
     cache = lib.Cache(L, E, H, I, S, k, a, b, 1, fp4_host, int2_host, arena, staging, **tier)
@@ -53,11 +66,14 @@ def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1, **tier
         for t in range(T):
             for l in range(L):
                 row = t * L + l
+                if (t, l) in pred:
+                    cache.prefetch(*pred[(t, l)], copy=copy_stream)
+                    oc.prefetch(*pred[(t, l)])
                 lib.moe_route(lg_dev[row:row + 1], k, ids, w)
                 cache.ensure(l, 1, ids, w, prec, copy=copy_stream)
                 xb = W.slotcache_x(seed, t, l, H)
                 lib.moe_expert_forward(layer, bf16_dev(xb), 1, k, ids, prec, w, out, ws)
-                oids, ow = O.route(logits[t, l][None, :], k)
+                oids, ow = routes[(t, l)]
                 oslots, oprec, owo, _ = oc.step(l, oids, ow)
                 torch.cuda.synchronize()
                 assert np.array_equal(ids.cpu().numpy(), oslots), (t, l)
@@ -77,6 +93,7 @@ def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1, **tier
         log(f"  stats {st}; outputs checked: {checked}")
         assert (st["hits"], st["misses"], st["int2_uses"], st["drops"]) == (oc.hits, oc.misses, oc.int2, oc.drops)
         assert st["int2_hits"] == oc.int2_hits
+        assert (st["prefetches"], st["ring_hits"]) == (oc.prefetches, oc.ring_hits)
         return st
     finally:
         cache.destroy()
@@ -87,7 +104,7 @@ def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1, **tier
 
 def _oracle_tier(tier):
     return {"int2_slots": tier.get("int2_slots", 0), "policy": tier.get("policy", "lru"),
-            "decay": tier.get("lfu_decay", 1.0), "seed": tier.get("lfu_seed")}
+            "decay": tier.get("lfu_decay", 1.0), "seed": tier.get("lfu_seed"), "ring": tier.get("prefetch_slots", 0)}
 
 
 def test_slotcache_loop_small(gpu_lib):
@@ -117,3 +134,84 @@ def test_slotcache_loop_int2_tier_lfu(gpu_lib):
     st = _run(gpu_lib, L=L, E=E, H=512, I=256, S=16, k=4, a=1, b=3, T=30, seed=73, check_every=3,
               int2_slots=6, policy="lfu", lfu_decay=0.875, lfu_seed=seed_counts)
     assert st["int2_hits"] > 0 and st["evictions"] > 0
+
+
+def test_slotcache_loop_prefetch(gpu_lib):
+    """Speculative prefetch into an 8-entry staging ring, two layers ahead,
+    with 6-expert predictions holding 3 of the true top-4: the expert kernels
+    read ring entries (slots 16..23) that the copy stream filled."""
+    st = _run(gpu_lib, L=3, E=16, H=512, I=256, S=16, k=4, a=2, b=3, T=30, seed=74, check_every=3,
+              recall=0.75, m=6, prefetch_slots=8)
+    assert st["ring_hits"] > 0 and st["evictions"] > 0
+
+
+def test_slotcache_loop_prefetch_fused_b1_path(gpu_lib):
+    """The batch-1 fused kernels (H = I = 2048) over the arena and its ring."""
+    st = _run(gpu_lib, L=2, E=24, H=2048, I=2048, S=30, k=6, a=2, b=4, T=12, seed=75, check_every=4,
+              recall=0.75, m=12, prefetch_slots=12, policy="lfu", lfu_decay=0.95)
+    assert st["ring_hits"] > 0
+
+
+def _stream_prefill(gpu_lib, L, E, H, I, S, k, T, chunks, seed):
+    """Prompt chunks of T tokens (T*k >= E: above the crossover) through L
+    layers by whole-layer streaming: each layer's experts are copied into
+    the next layer buffer while the previous layer computes, then the
+    prefill GEMM runs on the buffer with the router's expert ids."""
+    import torch
+    lib = gpu_lib
+    assert O.prefill_streams(T, k, E) and lib.moe_prefill_streams(T, k, E)
+    rb4 = O.fp4_expert_nbytes(H, I)
+    fp4_host = lib.PinnedBuffer(L * E * rb4)
+    for p in range(L * E):
+        W.fp4_record(seed, W.S_BANK, p, H, I, out=fp4_host.array[p * rb4:(p + 1) * rb4])
+    arena = torch.empty(S * rb4, dtype=torch.uint8, device="cuda")
+    cache = lib.Cache(L, E, H, I, S, k, k, k, T, fp4_host, None, arena, None)
+    oc = O.SlotCache(L, E, S, k, k, k)
+    copy_stream = torch.cuda.Stream()
+    calls = [(c, l) for c in range(chunks) for l in range(L)]
+    try:
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(lib.moe_prefill_workspace_bytes(H, I, T, k, False), dtype=torch.uint8, device="cuda")
+        b = cache.stream_layer(calls[0][1], copy=copy_stream)
+        assert b == oc.stream_layer(calls[0][1])[0]
+        for i, (c, l) in enumerate(calls):
+            lg = W.router_logits(seed, (W.S_LOGITS, c, l), T, E)
+            xb = W.bf16_normal(seed, (W.S_X, c, l), (T, H))
+            lib.moe_route(dev(lg), k, ids, w)
+            if i + 1 < len(calls):           # the next layer streams while this one computes
+                b = cache.stream_layer(calls[i + 1][1], copy=copy_stream)
+                assert b == oc.stream_layer(calls[i + 1][1])[0]
+            lay = cache.layer_buffer(l)
+            lib.moe_prefill_forward(lay, bf16_dev(xb), k, ids, w, out, ws)
+            torch.cuda.synchronize()
+            oids, ow = O.route(lg, k)
+            assert np.array_equal(ids.cpu().numpy(), oids), (c, l)
+            assert np.array_equal(cache.slot_map(), oc.slot_map()), (c, l)
+            ref = O.prefill_forward(O.bf16_bits_to_f64(xb), oids, ow,
+                                    lambda e, l=l: fp4_host.array[(l * E + e) * rb4:(l * E + e + 1) * rb4], H, I)
+            err = max_rel(out.float().cpu().numpy(), ref)
+            assert err <= TOL_BF16_MAX_REL, (c, l, err)
+        st = cache.stats()
+        log(f"stream prefill L={L} E={E} S={S} T={T} chunks={chunks}: {st}")
+        assert st["streamed"] == oc.streamed and st["bytes_h2d"] == oc.streamed * rb4
+        return st
+    finally:
+        cache.destroy()
+        fp4_host.free()
+
+
+def test_prefill_streaming_two_layer_buffers(gpu_lib):
+    """Three layers, two chunks: every stream after the second overwrites a
+    buffer the layer before last computed on; with L odd the second chunk
+    finds no layer already in place."""
+    st = _stream_prefill(gpu_lib, L=3, E=16, H=512, I=256, S=32, k=4, T=8, chunks=2, seed=76)
+    assert st["streamed"] == 6 * 16
+
+
+def test_prefill_streaming_layer_already_in_place(gpu_lib):
+    """Two layers, two chunks, S = 3E: each layer returns to its own buffer
+    and is not copied again."""
+    st = _stream_prefill(gpu_lib, L=2, E=16, H=512, I=256, S=48, k=4, T=8, chunks=2, seed=77)
+    assert st["streamed"] == 2 * 16
