@@ -95,3 +95,25 @@ def test_prefill_full_size_sampled(gpu_lib):
     sample = sorted(rng.choice(cfg["T"], 12, replace=False).tolist())
     _prefill_case(gpu_lib, E=cfg["E"], H=cfg["H"], I=cfg["I"], k=cfg["k"], T=cfg["T"], seed=W.config_seed(3),
                   sample=sample)
+
+
+@pytest.mark.parametrize("T", [1, 5])
+def test_prefill_sparse_groups(gpu_lib, T):
+    """Few tokens over 64 experts: most groups are empty and the rest hold a
+    single row of a 32-row block."""
+    _prefill_case(gpu_lib, E=64, H=512, I=256, k=3, T=T, seed=44 + T)
+
+
+def test_prefill_T0_is_noop(gpu_lib):
+    import torch
+    H, I, E, k = 256, 128, 8, 2
+    layer = gpu_lib.make_layer(H, I, fp4_base=torch.empty(E * O.fp4_expert_nbytes(H, I), dtype=torch.uint8,
+                                                           device="cuda"),
+                               fp4_stride=O.fp4_expert_nbytes(H, I), num_slots=E)
+    x = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    gpu_lib.moe_prefill_forward(layer, x, k, ids, w, out, ws)
+    torch.cuda.synchronize()
