@@ -246,7 +246,7 @@ moe_status moe_pinned_free(void* p);
 /* Fixed-size slot cache over (layer, expert) pairs with LRU eviction and the
  * (a,b) precision ladder ([P1] §What the expert cache actually does; [P2]
  * §Not all six experts matter equally).  Opaque; created and destroyed on the
- * host. */
+ * host.  A handle is not thread-safe: calls on one handle must not overlap. */
 typedef struct moe_cache moe_cache;
 
 typedef struct {
@@ -257,7 +257,7 @@ typedef struct {
   int max_tokens;        /* most tokens per ensure call; max_tokens * k <= num_slots */
   const uint8_t* fp4_host;   /* host pinned: L*E FP4 records, pair l*E+e at (l*E+e)*moe_fp4_expert_bytes */
   const uint8_t* int2_host;  /* host pinned: L*E 2-bit records (NULL if a == b) */
-  uint8_t* fp4_arena;        /* device: num_slots FP4 records (NULL: host-only planning) */
+  uint8_t* fp4_arena;        /* device: num_slots (+ prefetch_slots) FP4 records (NULL: host-only planning) */
   uint8_t* int2_staging;     /* device: 2-bit records (NULL if a == b): max_tokens*(b-a) staging entries when
                                 int2_slots == 0, else the int2_slots slots of the 2-bit tier */
   /* Optional tiers and eviction rule ([P2] §Rig, model & methodology, best configuration: a

@@ -272,6 +272,28 @@ struct alignas(16) GemmSmem {
   int32_t pm[kMT];              // down: the (token, rank) pair of each tile row
 };
 
+// The epilogue turns a wavefront's 32 x 32 accumulator block around through
+// LDS: the MFMA leaves lane (c, h) with rows 8(e/4) + 4h + e%4 of column c;
+// afterwards lane l holds 16 consecutive columns (16 (l & 1) ..) of row l / 2,
+// so an MX block's maximum is one lane-pair exchange and a row leaves in
+// 16-byte stores.  Each wavefront uses its own kTLd-padded tile.
+constexpr int kTLd = 36;  // floats per row of the transpose tile
+static_assert((size_t)kWaves * 32 * kTLd * 4 <= sizeof(((GemmSmem*)nullptr)->a), "transpose tiles fit the A stages");
+
+__device__ __forceinline__ void acc_transpose(float* tw, const float (&v)[16], int c, int h, int lane, float (&out)[16]) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) tw[(8 * (e / 4) + 4 * h + (e % 4)) * kTLd + c] = v[e];
+  __builtin_amdgcn_wave_barrier();
+  const u32x4_t* src = (const u32x4_t*)(tw + (lane >> 1) * kTLd + 16 * (lane & 1));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const u32x4_t t = src[k];
+    out[4 * k] = __uint_as_float(t.x), out[4 * k + 1] = __uint_as_float(t.y);
+    out[4 * k + 2] = __uint_as_float(t.z), out[4 * k + 3] = __uint_as_float(t.w);
+  }
+  __builtin_amdgcn_wave_barrier();  // the reads are done before the tile is written again
+}
+
 // native vectors, not uint4: a struct copy of a register array goes through scratch
 struct StageRegs {
   u32x4_t a[kPiecesA];
@@ -401,43 +423,63 @@ __device__ __forceinline__ void gemm_item(GemmSmem& sm, const PrefillArgs& a, co
   }
 
   // the epilogue's lane indices pass through an empty asm so the compiler
-  // cannot hoist its address arithmetic into registers held across the loop
+  // cannot hoist its address arithmetic into registers held across the loop;
+  // the stage buffers are free here (the loop ended at a barrier) and hold the
+  // transpose tiles
   int ce = c, he = h;
   asm volatile("" : "+v"(ce), "+v"(he));
+  const int lane = 32 * he + ce, half = lane & 1;
+  float* tw = (float*)sm.a[0] + (tid >> 6) * (32 * kTLd);
   const int H = a.H, I = a.I;
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int rb = 32 * (x.mp + 2 * i);
+    const int r = rb + (lane >> 1);  // the row this lane holds after the transpose
     if (NMAT == 2) {
-      // SwiGLU, MXFP8 requantisation along I (a 32-column block is one half-wave row)
+      // SwiGLU, MXFP8 requantisation along I (a 32-column block is one lane pair's row)
 #pragma unroll
       for (int q = 0; q < kNB / 2; ++q) {
-        const int col = x.nt * (kNR / 2) + 32 * col_block<2>(x.nh, q) + ce;
+        const int col0 = x.nt * (kNR / 2) + 32 * col_block<2>(x.nh, q);
+        float hv[16], v[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float g = acc[i][q][e], u = acc[i][kNB / 2 + q][e];
           // silu(g) * u with the hardware exp2 and reciprocal (the result is
           // requantised to 8 bits next)
-          const float hv = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * g)) * u;
-          const float amax = half_wave_max(fabsf(hv));
-          const int sh = mx_shared_exp(amax);
-          const int r = rb + 8 * (e / 4) + 4 * he + (e % 4);
-          if (r < x.rows) {
-            const size_t pos = (size_t)(x.start + r);
-            a.hq[pos * I + col] = (uint8_t)e4m3_encode(__builtin_amdgcn_ldexpf(hv, -sh));
-            if (ce == 0) a.hs[pos * (I / 32) + col / 32] = (uint8_t)(sh + 127);
-          }
+          hv[e] = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * g)) * u;
+        }
+        acc_transpose(tw, hv, ce, he, lane, v);
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(v[k]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        const int sh = mx_shared_exp(amax);
+        if (r < x.rows) {
+          const size_t pos = (size_t)(x.start + r);
+          uint32_t w[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            w[k] = e4m3_encode4(__builtin_amdgcn_ldexpf(v[4 * k], -sh), __builtin_amdgcn_ldexpf(v[4 * k + 1], -sh),
+                                __builtin_amdgcn_ldexpf(v[4 * k + 2], -sh), __builtin_amdgcn_ldexpf(v[4 * k + 3], -sh));
+          *(u32x4_t*)(a.hq + pos * I + col0 + 16 * half) = u32x4_t{w[0], w[1], w[2], w[3]};
+          if (half == 0) a.hs[pos * (I / 32) + col0 / 32] = (uint8_t)(sh + 127);
         }
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = rb + 8 * (e / 4) + 4 * he + (e % 4);
+      for (int j = 0; j < kNB; ++j) {
+        float yv[16], v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) yv[e] = acc[i][j][e];
+        acc_transpose(tw, yv, ce, he, lane, v);
         if (r < x.rows) {
           const size_t pair = (size_t)sm.pm[r];
+          uint32_t w[8];
 #pragma unroll
-          for (int j = 0; j < kNB; ++j)
-            a.y[pair * H + (size_t)x.nt * kNR + col_block<1>(x.nh, j) * 32 + ce] = f32_to_bf16(acc[i][j][e]);
+          for (int k = 0; k < 8; ++k) w[k] = (uint32_t)f32_to_bf16(v[2 * k]) | ((uint32_t)f32_to_bf16(v[2 * k + 1]) << 16);
+          u32x4_t* dst = (u32x4_t*)(a.y + pair * H + (size_t)x.nt * kNR + col_block<1>(x.nh, j) * 32 + 16 * half);
+          dst[0] = u32x4_t{w[0], w[1], w[2], w[3]};
+          dst[1] = u32x4_t{w[4], w[5], w[6], w[7]};
         }
       }
     }
