@@ -37,7 +37,10 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 #define MOE_PF_WAVES 4
 #endif
 constexpr int kWaves = MOE_PF_WAVES;  // wavefronts per GEMM workgroup (4: one per SIMD, or 8)
-constexpr int kMB = 6;        // 32-row M blocks per item at most
+#ifndef MOE_PF_MB
+#define MOE_PF_MB 6
+#endif
+constexpr int kMB = MOE_PF_MB;  // 32-row M blocks per item at most (4 or 6)
 constexpr int kMT = 32 * kMB; // grouped rows per item at most
 constexpr int kNR = 256;      // weight rows per item (8 MFMA column blocks)
 #ifndef MOE_PF_DEPTH
@@ -544,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(PrefillArgs a) {
     x.tid = tid, x.c = c, x.h = h, x.mp = mp, x.nh = nh, x.nstage = nstage;
     x.rows = rows, x.start = start, x.nt = nt;
     // the wavefront's live M blocks: mp, mp + 2, mp + 4 while below the tile's rows
-    const int nl = max(0, min(3, (rows - 32 * mp + 63) / 64));
+    const int nl = max(0, min(kMB / 2, (rows - 32 * mp + 63) / 64));
     switch (nl) {
       case 0: gemm_item<NMAT, 0>(sm, a, x); break;
       case 1: gemm_item<NMAT, 1>(sm, a, x); break;
