@@ -381,6 +381,7 @@ typedef enum {
   MOE_PROF_GEMM_DOWN = 9,   /* prefill grouped GEMM, down */
   MOE_PROF_DEQUANT = 10,
   MOE_PROF_READ = 11,       /* streaming-read reference */
+  MOE_PROF_CACHE = 12,      /* slot cache: picks to the host, rewritten ids back */
   MOE_PROF_KINDS = 16
 } moe_prof_kind;
 

@@ -400,7 +400,7 @@ class Cache:
 # --------------------------------------------------------------------- timing
 
 PROF_KINDS = ("route", "router_logits", "gateup", "down", "combine", "group", "plan", "quant",
-              "gemm_gateup", "gemm_down", "dequant", "read")
+              "gemm_gateup", "gemm_down", "dequant", "read", "cache")
 MOE_PROF_KINDS = 16
 
 

@@ -82,8 +82,10 @@ struct moe_cache {
   };
   std::vector<Copy> copies;
   // device-side plumbing (created on first ensure)
-  void* pin_in = nullptr;   // pinned: ids [T*k] int32, w [T*k] f32
-  void* pin_out = nullptr;  // pinned: slots [T*k] int32, w' [T*k] f32, prec [T*k] int8
+  void* pin_in = nullptr;   // pinned, mapped: ids [T*k] int32, w [T*k] f32
+  void* pin_out = nullptr;  // pinned, mapped: slots [T*k] int32, w' [T*k] f32, prec [T*k] int8
+  void* pin_in_dev = nullptr;   // their device addresses
+  void* pin_out_dev = nullptr;
   hipEvent_t ev_read = nullptr, ev_copy = nullptr;
   bool broken = false;
 };
@@ -443,16 +445,23 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
   hipStream_t cs = (hipStream_t)compute, ps = copy ? (hipStream_t)copy : cs;
   const size_t n = (size_t)T * c->d.k;
   if (!c->pin_in) {
-    MOE_HIP_CHECK(hipHostMalloc(&c->pin_in, pin_in_bytes(c->d), hipHostMallocDefault));
-    MOE_HIP_CHECK(hipHostMalloc(&c->pin_out, pin_out_bytes(c->d), hipHostMallocDefault));
+    MOE_HIP_CHECK(hipHostMalloc(&c->pin_in, pin_in_bytes(c->d), hipHostMallocMapped));
+    MOE_HIP_CHECK(hipHostMalloc(&c->pin_out, pin_out_bytes(c->d), hipHostMallocMapped));
+    MOE_HIP_CHECK(hipHostGetDevicePointer(&c->pin_in_dev, c->pin_in, 0));
+    MOE_HIP_CHECK(hipHostGetDevicePointer(&c->pin_out_dev, c->pin_out, 0));
     MOE_HIP_CHECK(hipEventCreateWithFlags(&c->ev_read, hipEventDisableTiming));
     MOE_HIP_CHECK(hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming));
   }
   int32_t* ids_h = (int32_t*)c->pin_in;
   float* w_h = (float*)((char*)c->pin_in + (size_t)c->d.max_tokens * c->d.k * 4);
-  // the one host sync of the call: read the router's picks
-  MOE_HIP_CHECK(hipMemcpyAsync(ids_h, ids_inout, n * 4, hipMemcpyDeviceToHost, cs));
-  MOE_HIP_CHECK(hipMemcpyAsync(w_h, w_inout, n * 4, hipMemcpyDeviceToHost, cs));
+  // the one host sync of the call: read the router's picks (one small kernel
+  // writes them into the mapped pinned buffer)
+  {
+    int32_t* ids_d = (int32_t*)c->pin_in_dev;
+    float* w_d = (float*)((char*)c->pin_in_dev + (size_t)c->d.max_tokens * c->d.k * 4);
+    s = launch_cache_gather(ids_inout, w_inout, (int)n, ids_d, w_d, cs);
+    if (s != MOE_OK) return s;
+  }
   MOE_HIP_CHECK(hipEventRecord(c->ev_read, cs));
   MOE_HIP_CHECK(hipEventSynchronize(c->ev_read));
   s = plan(c, layer, T, ids_h, w_h);
@@ -492,9 +501,15 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
   std::memcpy(slots_o, c->slots_h.data(), n * 4);
   std::memcpy(w_o, c->wout_h.data(), n * 4);
   std::memcpy(prec_o, c->prec_h.data(), n);
-  MOE_HIP_CHECK(hipMemcpyAsync(ids_inout, slots_o, n * 4, hipMemcpyHostToDevice, cs));
-  MOE_HIP_CHECK(hipMemcpyAsync(w_inout, w_o, n * 4, hipMemcpyHostToDevice, cs));
-  MOE_HIP_CHECK(hipMemcpyAsync(prec_out, prec_o, n, hipMemcpyHostToDevice, cs));
+  // one small kernel reads them back from the mapped buffer; the next call's
+  // host writes come after its own sync, which follows this kernel
+  {
+    const char* base = (const char*)c->pin_out_dev;
+    const size_t nk = (size_t)c->d.max_tokens * c->d.k;
+    s = launch_cache_scatter((const int32_t*)base, (const float*)(base + nk * 4), (const int8_t*)(base + nk * 8),
+                             (int)n, ids_inout, w_inout, prec_out, cs);
+    if (s != MOE_OK) return s;
+  }
   c->broken = false;
   return MOE_OK;
 }
