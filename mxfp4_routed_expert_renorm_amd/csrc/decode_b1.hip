@@ -154,7 +154,7 @@ struct GURow {
   uint32_t s1[CPL], s3[CPL];
 };
 
-template <int CPL, int NB, int EPL, bool SH>
+template <int CPL, int NB, int EPL, bool SH, bool HAS2>
 __global__ __launch_bounds__(256, 2) void gateup_b1_kernel(B1Args a) {
   constexpr int XBYTES = CPL * 64 * 32 * 2;  // H bf16 activations
   static_assert(CPL == 1 || CPL == 2, "H is 2048 or 4096");
@@ -209,83 +209,77 @@ __global__ __launch_bounds__(256, 2) void gateup_b1_kernel(B1Args a) {
   }
   const bool fp4 = lane < k && my_prec == 0 && my_slot >= 0 && my_slot < a.num_slots;
   const uint64_t m = __ballot(fp4);
+  // the 2-bit ranks (slot-cache fallback copies): their rows follow the FP4 ones
+  const uint64_t m2 = HAS2 ? __ballot(lane < k && my_prec == 1 && my_slot >= 0 && my_slot < a.num_int2) : 0;
   const int nf = __popcll(m);
   constexpr int S0 = SH ? 1 : 0;
   const int nact = S0 + nf;
   ((uint4*)xs)[threadIdx.x] = xv0;
   if (CPL == 2) ((uint4*)xs)[threadIdx.x + 256] = xv1;
   __syncthreads();
-  if (nact == 0) return;
-
-  // 3. this row of every FP4 rank (batch slots past the active groups repeat
-  // the last one and are not stored)
-  int kx[NB];
-  if constexpr (SH) kx[0] = k;
+  if (nact > 0) {
+    // 3. this row of every FP4 rank (batch slots past the active groups repeat
+    // the last one and are not stored)
+    int kx[NB];
+    if constexpr (SH) kx[0] = k;
 #pragma unroll
-  for (int u = S0; u < NB; ++u) {
-    const int r = nf > 0 ? nth_set_bit(m, min(u - S0, nf - 1)) : -1;
-    kx[u] = r;
-    const uint8_t* rec = r >= 0 ? a.fp4_base + (size_t)__builtin_amdgcn_readlane(my_slot, r) * a.fp4_stride : a.shared;
-    issue(sl[u], rec);
-  }
-  __builtin_amdgcn_sched_barrier(0);  // every load above is out before the first row is consumed
-
-  // 4. rows in arrival order; the block scale rides in the convert, so each
-  // row is one accumulation chain per matrix (two for instruction overlap)
-  float gsum[NB], usum[NB];
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    float g0a = 0.0f, g1a = 0.0f, u0a = 0.0f, u1a = 0.0f;
-#pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-      XChunk xq;  // re-read per row: LDS bandwidth is cheaper than 16 registers per chunk
-      xq.load_lds(xs, (size_t)(q * 64 + lane) * 32);
-      xq.fp4_acc(sl[u].c1[q], stab[sl[u].s1[q]], g0a, g1a);
-      xq.fp4_acc(sl[u].c3[q], stab[sl[u].s3[q]], u0a, u1a);
+    for (int u = S0; u < NB; ++u) {
+      const int r = nf > 0 ? nth_set_bit(m, min(u - S0, nf - 1)) : -1;
+      kx[u] = r;
+      const uint8_t* rec = r >= 0 ? a.fp4_base + (size_t)__builtin_amdgcn_readlane(my_slot, r) * a.fp4_stride : a.shared;
+      issue(sl[u], rec);
     }
-    gsum[u] = wave_sum_to_lane63(g0a + g1a);
-    usum[u] = wave_sum_to_lane63(u0a + u1a);
-  }
-  // 5. SwiGLU of the row for every group at once: lane u takes group u
-  float gv = 0.0f, uv = 0.0f;
-  int kv = 0;
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    const float gu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gsum[u]), 63));
-    const float uu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(usum[u]), 63));
-    gv = lane == u ? gu : gv;
-    uv = lane == u ? uu : uv;
-    kv = lane == u ? kx[u] : kv;
-  }
-  if (lane < nact) a.h[(size_t)kv * I + row] = f32_to_bf16(silu_mul_b1(gv, uv));
-}
+    __builtin_amdgcn_sched_barrier(0);  // every load above is out before the first row is consumed
 
-// 2-bit groups of the batch-1 gate/up (the slot cache's fallback copies):
-// a separate kernel so the FP4 streaming kernel keeps its register budget.
-// One wavefront per row; the activations come from global memory (L2).
-template <int CPL>
-__global__ __launch_bounds__(256) void gateup_int2_b1_kernel(B1Args a) {
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nw = gridDim.x * 4;
-  const int H = a.H, I = a.I;
-  const RecordLayout L = record_layout(H, I, 2);
-  const size_t rowb2 = (size_t)H / 4, rows = (size_t)H / 32;
-  for (int g = 0; g < a.K1; ++g) {
-    int pr;
-    const uint8_t* rec = b1_group(a, g, &pr);
-    if (pr != 1) continue;
-    for (int row = gw; row < I; row += nw) {
+    // 4. rows in arrival order; the block scale rides in the convert, so each
+    // row is one accumulation chain per matrix (two for instruction overlap)
+    float gsum[NB], usum[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      float g0a = 0.0f, g1a = 0.0f, u0a = 0.0f, u1a = 0.0f;
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        XChunk xq;  // re-read per row: LDS bandwidth is cheaper than 16 registers per chunk
+        xq.load_lds(xs, (size_t)(q * 64 + lane) * 32);
+        xq.fp4_acc(sl[u].c1[q], stab[sl[u].s1[q]], g0a, g1a);
+        xq.fp4_acc(sl[u].c3[q], stab[sl[u].s3[q]], u0a, u1a);
+      }
+      gsum[u] = wave_sum_to_lane63(g0a + g1a);
+      usum[u] = wave_sum_to_lane63(u0a + u1a);
+    }
+    // 5. SwiGLU of the row for every group at once: lane u takes group u
+    float gv = 0.0f, uv = 0.0f;
+    int kv = 0;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const float gu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gsum[u]), 63));
+      const float uu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(usum[u]), 63));
+      gv = lane == u ? gu : gv;
+      uv = lane == u ? uu : uv;
+      kv = lane == u ? kx[u] : kv;
+    }
+    if (lane < nact) a.h[(size_t)kv * I + row] = f32_to_bf16(silu_mul_b1(gv, uv));
+  }
+
+  // 6. the 2-bit ranks' rows, one at a time (rarely more than two; the FP4
+  // rows' registers are free again): 32 codes per lane and chunk, the
+  // activation from LDS, the E4M3 block scale applied per chunk
+  if constexpr (HAS2) {
+    const RecordLayout L2 = record_layout(a.H, I, 2);
+    const size_t rowb2 = (size_t)a.H / 4;
+    for (uint64_t mm = m2; mm; mm &= mm - 1) {
+      const int g = __builtin_ctzll(mm);
+      const uint8_t* rec = a.int2_base + (size_t)__builtin_amdgcn_readlane(my_slot, g) * a.int2_stride;
       float gs = 0.0f, us = 0.0f;
 #pragma unroll
       for (int q = 0; q < CPL; ++q) {
         const size_t c = (size_t)(q * 64 + lane);
-        const uint2 c1 = ld_stream8(rec + L.w1c + (size_t)row * rowb2 + c * 8);
-        const uint2 c3 = ld_stream8(rec + L.w3c + (size_t)row * rowb2 + c * 8);
+        const uint2 c1 = ld_stream8(rec + L2.w1c + (size_t)row * rowb2 + c * 8);
+        const uint2 c3 = ld_stream8(rec + L2.w3c + (size_t)row * rowb2 + c * 8);
         XChunk xq;
-        xq.load_global(a.x, c * 32);
-        gs = fmaf(xq.int2(c1), e4m3_to_f32(rec[L.w1s + (size_t)row * rows + c]), gs);
-        us = fmaf(xq.int2(c3), e4m3_to_f32(rec[L.w3s + (size_t)row * rows + c]), us);
+        xq.load_lds(xs, c * 32);
+        gs = fmaf(xq.int2(c1), e4m3_to_f32(rec[L2.w1s + (size_t)row * rows4 + c]), gs);
+        us = fmaf(xq.int2(c3), e4m3_to_f32(rec[L2.w3s + (size_t)row * rows4 + c]), us);
       }
       gs = wave_sum_to_lane63(gs);
       us = wave_sum_to_lane63(us);
@@ -432,12 +426,14 @@ int down_batch(int K1) { return K1 <= 4 ? 4 : K1 <= 7 ? 7 : K1 <= 9 ? 9 : kMaxGr
 template <int CPL, int NB, bool SH>
 void launch_gateup_nb(const B1Args& a, hipStream_t s) {
   const int grid = a.I / 4;  // one wavefront per gate/up row
-  if (!a.logits)
-    launch(MOE_PROF_GATEUP, (gateup_b1_kernel<CPL, NB, 0, SH>), dim3(grid), dim3(256), 0, s, a);
+  if (!a.logits && a.prec)  // 2-bit copies can only appear when precisions are given
+    launch(MOE_PROF_GATEUP, (gateup_b1_kernel<CPL, NB, 0, SH, true>), dim3(grid), dim3(256), 0, s, a);
+  else if (!a.logits)
+    launch(MOE_PROF_GATEUP, (gateup_b1_kernel<CPL, NB, 0, SH, false>), dim3(grid), dim3(256), 0, s, a);
   else if (a.E <= 256)
-    launch(MOE_PROF_GATEUP, (gateup_b1_kernel<CPL, NB, 4, SH>), dim3(grid), dim3(256), 0, s, a);
+    launch(MOE_PROF_GATEUP, (gateup_b1_kernel<CPL, NB, 4, SH, false>), dim3(grid), dim3(256), 0, s, a);
   else
-    launch(MOE_PROF_GATEUP, (gateup_b1_kernel<CPL, NB, kMaxE / 64, SH>), dim3(grid), dim3(256), 0, s, a);
+    launch(MOE_PROF_GATEUP, (gateup_b1_kernel<CPL, NB, kMaxE / 64, SH, false>), dim3(grid), dim3(256), 0, s, a);
 }
 
 template <int CPL, bool SH>
@@ -459,10 +455,6 @@ void launch_gateup_b1(const B1Args& a, hipStream_t s) {
     launch_gateup_sh<CPL, true>(a, s);
   else
     launch_gateup_sh<CPL, false>(a, s);
-  if (a.prec) {  // 2-bit copies can only appear when precisions are given
-    const int grid2 = std::max(1, std::min(a.I / 4, 1024));
-    launch(MOE_PROF_GATEUP, (gateup_int2_b1_kernel<CPL>), dim3(grid2), dim3(256), 0, s, a);
-  }
 }
 
 template <int CPL, bool HAS2, bool SH>
