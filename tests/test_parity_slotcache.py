@@ -215,3 +215,51 @@ def test_prefill_streaming_layer_already_in_place(gpu_lib):
     and is not copied again."""
     st = _stream_prefill(gpu_lib, L=2, E=16, H=512, I=256, S=48, k=4, T=8, chunks=2, seed=77)
     assert st["streamed"] == 2 * 16
+
+
+def test_decode_after_streamed_prefill(gpu_lib):
+    """A streamed prompt chunk leaves its layers resident: decode calls that
+    follow hit the streamed slots (no copies for those experts) and read the
+    records the stream copied, in the order the events impose (the stream's
+    copies are still in flight when the first decode call is made)."""
+    import torch
+    lib = gpu_lib
+    L, E, H, I, S, k, T = 2, 16, 512, 256, 32, 4, 8
+    seed = 78
+    rb4 = O.fp4_expert_nbytes(H, I)
+    fp4_host = lib.PinnedBuffer(L * E * rb4)
+    for p in range(L * E):
+        W.fp4_record(seed, W.S_BANK, p, H, I, out=fp4_host.array[p * rb4:(p + 1) * rb4])
+    arena = torch.empty(S * rb4, dtype=torch.uint8, device="cuda")
+    cache = lib.Cache(L, E, H, I, S, k, k, k, 1, fp4_host, None, arena, None)
+    oc = O.SlotCache(L, E, S, k, k, k)
+    copy_stream = torch.cuda.Stream()
+    try:
+        for l in range(L):
+            assert cache.stream_layer(l, copy=copy_stream) == oc.stream_layer(l)[0]
+        layer = cache.layer()
+        ids = torch.empty((1, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+        prec = torch.empty((1, k), dtype=torch.int8, device="cuda")
+        out = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+        ws = lib.expert_workspace(H, I, 1, k, False)
+        logits = W.slotcache_logits(seed, L, E, T, 1.1)
+        for t in range(T):
+            for l in range(L):
+                lib.moe_route(dev(logits[t, l][None, :]), k, ids, w)
+                cache.ensure(l, 1, ids, w, prec, copy=copy_stream)
+                xb = W.slotcache_x(seed, t, l, H)
+                lib.moe_expert_forward(layer, bf16_dev(xb), 1, k, ids, prec, w, out, ws)
+                oids, ow = O.route(logits[t, l][None, :], k)
+                oslots, oprec, owo, cps = oc.step(l, oids, ow)
+                torch.cuda.synchronize()
+                assert cps == [] and np.array_equal(ids.cpu().numpy(), oslots), (t, l)
+                ref = O.layer_forward(O.bf16_bits_to_f64(xb), oids, owo,
+                                      lambda e, p, l=l: fp4_host.array[(l * E + int(e)) * rb4:(l * E + int(e) + 1) * rb4],
+                                      H, I, prec=oprec)
+                assert max_rel(out.float().cpu().numpy(), ref) <= TOL_BF16_MAX_REL, (t, l)
+        st = cache.stats()
+        assert st["misses"] == 0 and st["hits"] == T * L * k and st["streamed"] == L * E
+    finally:
+        cache.destroy()
+        fp4_host.free()
