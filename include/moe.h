@@ -290,7 +290,8 @@ typedef struct {
  * count by lfu_decay, and every use of a pair (hit or fetch, either tier) adds one. */
 moe_status moe_cache_create(const moe_cache_desc* desc, moe_cache** out);
 moe_status moe_cache_destroy(moe_cache* c);
-/* Back to the cold state (empty slots, clock 0, zero stats). */
+/* Back to the cold state (empty slots and ring, clock 0, zero stats, LFU counts at their
+ * seed).  Waits for prefetch and layer-stream copies that no call has waited for yet. */
 moe_status moe_cache_reset(moe_cache* c);
 
 /* One call of the policy on host arrays, no GPU work: for T tokens of `layer`,

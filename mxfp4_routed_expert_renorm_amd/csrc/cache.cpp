@@ -401,6 +401,11 @@ moe_status moe_cache_destroy(moe_cache* c) {
 
 moe_status moe_cache_reset(moe_cache* c) {
   if (!c) return fail(MOE_EINVAL, "moe_cache_reset: handle is NULL");
+  // speculative and streamed copies nobody has waited for yet would land in
+  // slots the emptied cache hands out again
+  if (c->prefetch_pending) MOE_HIP_CHECK(hipEventSynchronize(c->ev_prefetch));
+  for (int b = 0; b < 2; ++b)
+    if (c->stream_pending[b]) MOE_HIP_CHECK(hipEventSynchronize(c->ev_stream[b]));
   std::fill(c->map.begin(), c->map.end(), -1);
   std::fill(c->owner.begin(), c->owner.end(), -1);
   std::fill(c->stamp.begin(), c->stamp.end(), 0);
