@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-CFG_INDEX = 1
+DEFAULT_WORKLOAD = "decode-b1"
 
 
 def parse():
@@ -118,8 +118,8 @@ def cpu_baseline(min_seconds: float, threads: int = 1):
     from mxfp4_routed_expert_renorm_amd import workloads as W
     from oracle import moe_oracle as O
 
-    cfg = W.CONFIGS[CFG_INDEX]
-    seed = W.config_seed(CFG_INDEX)
+    cfg = W.WORKLOADS[DEFAULT_WORKLOAD]
+    seed = cfg["seed"]
     H, I, k = cfg["H"], cfg["I"], cfg["k"]
     toks, t_used = 0, 0.0
     with threadpool_limits(limits=threads):
@@ -237,8 +237,8 @@ def bench_decode_b1(args):
     from mxfp4_routed_expert_renorm_amd import binding as lib
     from mxfp4_routed_expert_renorm_amd import workloads as W
 
-    cfg = W.CONFIGS[CFG_INDEX]
-    seed = W.config_seed(CFG_INDEX)
+    cfg = W.WORKLOADS[DEFAULT_WORKLOAD]
+    seed = cfg["seed"]
     E, H, I, k, T = cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"]
     K, Wm = args.steps, args.warmup
     nsteps = K + Wm
@@ -408,9 +408,8 @@ def bench_decode_b64(args):
     from mxfp4_routed_expert_renorm_amd import binding as lib
     from mxfp4_routed_expert_renorm_amd import workloads as W
 
-    ci = 2
-    cfg = W.CONFIGS[ci]
-    seed = W.config_seed(ci)
+    cfg = W.WORKLOADS["decode-b64"]
+    seed = cfg["seed"]
     E, H, I, k, T = cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"]
     K, Wm = args.steps, args.warmup
     nsteps = K + Wm
@@ -486,9 +485,8 @@ def bench_prefill(args):
     from mxfp4_routed_expert_renorm_amd import binding as lib
     from mxfp4_routed_expert_renorm_amd import workloads as W
 
-    ci = 3
-    cfg = W.CONFIGS[ci]
-    seed = W.config_seed(ci)
+    cfg = W.WORKLOADS["prefill"]
+    seed = cfg["seed"]
     E, H, I, k, T = cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"]
     K, Wm = args.steps, args.warmup
     nsteps = K + Wm
@@ -551,9 +549,8 @@ def bench_slotcache(args):
     from mxfp4_routed_expert_renorm_amd import binding as lib
     from mxfp4_routed_expert_renorm_amd import workloads as W
 
-    ci = 4
-    cfg = W.CONFIGS[ci]
-    seed = W.config_seed(ci)
+    cfg = W.WORKLOADS["slotcache"]
+    seed = cfg["seed"]
     L, E, H, I, k, T, S = cfg["L"], cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"], cfg["slots"]
     a, b = cfg["ladder"]
     dev = torch.device("cuda:0")
@@ -681,9 +678,8 @@ def bench_slotcache_prefill(args):
     from mxfp4_routed_expert_renorm_amd import binding as lib
     from mxfp4_routed_expert_renorm_amd import workloads as W
 
-    ci = 4
-    cfg = W.CONFIGS[ci]
-    seed = W.config_seed(ci)
+    cfg = W.WORKLOADS["slotcache"]
+    seed = cfg["seed"]
     L, E, H, I, k, S = cfg["L"], cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["slots"]
     T = 4096
     chunks = max(1, min(args.steps, 4))

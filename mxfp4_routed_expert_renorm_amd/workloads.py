@@ -145,27 +145,23 @@ def router_logits(seed: int, keys: tuple, T: int, E: int, bias: np.ndarray | Non
 # ----------------------------------------------------------------------------
 # the five workloads
 
-CONFIGS = {
-    0: dict(name="tiny-cpu-checkable", E=8, H=256, I=128, k=2, T=4, shared=False,
-            x_dtype="f32", out_dtype="f32", router="x", router_std=0.02),
-    1: dict(name="decode-b1-E256-top8-shared", E=256, H=4096, I=2048, k=8, T=1, shared=True,
-            x_dtype="bf16", out_dtype="bf16", router="logits"),
-    2: dict(name="decode-b64-E256-top6-zipf-shared", E=256, H=4096, I=2048, k=6, T=64, shared=True,
-            x_dtype="bf16", out_dtype="bf16", router="logits", zipf=1.1),
-    3: dict(name="prefill-4096-E256-top8-shared", E=256, H=4096, I=2048, k=8, T=4096, shared=True,
-            x_dtype="bf16", out_dtype="bf16", router="logits"),
-    4: dict(name="slotcache-decode-L8-E256-S512-top6-ladder24", L=8, E=256, H=4096, I=2048, k=6,
-            T=512, shared=False, x_dtype="bf16", out_dtype="bf16", router="logits", zipf=1.1,
-            slots=512, ladder=(2, 4)),
+WORKLOADS = {
+    "tiny": dict(name="tiny-cpu-checkable", seed=1000, E=8, H=256, I=128, k=2, T=4, shared=False,
+                 x_dtype="f32", out_dtype="f32", router="x", router_std=0.02),
+    "decode-b1": dict(name="decode-b1-E256-top8-shared", seed=1001, E=256, H=4096, I=2048, k=8, T=1,
+                      shared=True, x_dtype="bf16", out_dtype="bf16", router="logits"),
+    "decode-b64": dict(name="decode-b64-E256-top6-zipf-shared", seed=1002, E=256, H=4096, I=2048, k=6,
+                       T=64, shared=True, x_dtype="bf16", out_dtype="bf16", router="logits", zipf=1.1),
+    "prefill": dict(name="prefill-4096-E256-top8-shared", seed=1003, E=256, H=4096, I=2048, k=8, T=4096,
+                    shared=True, x_dtype="bf16", out_dtype="bf16", router="logits"),
+    "slotcache": dict(name="slotcache-decode-L8-E256-S512-top6-ladder24", seed=1004, L=8, E=256, H=4096,
+                      I=2048, k=6, T=512, shared=False, x_dtype="bf16", out_dtype="bf16", router="logits",
+                      zipf=1.1, slots=512, ladder=(2, 4)),
 }
 
 
-def config_seed(index: int) -> int:
-    return 1000 + int(index)
-
-
 def make_layer_inputs(cfg: dict, seed: int, step: int = 0, with_bank: bool = True) -> dict:
-    """Inputs of one single-layer workload (configs 0-3 shape).
+    """Inputs of one single-layer workload (tiny, decode-b1, decode-b64, prefill).
 
     step selects fresh activations and logits (bank and router weights are
     fixed per seed)."""

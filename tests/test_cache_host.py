@@ -64,9 +64,9 @@ def _compare_trace(L, E, S, k, a, b, ids, w, T_call=1, int2_slots=0, policy="lru
 
 
 def test_slotcache_trace_full_size_bit_exact():
-    cfg = W.CONFIGS[4]
+    cfg = W.WORKLOADS["slotcache"]
     L, E, k, S, (a, b), T = cfg["L"], cfg["E"], cfg["k"], cfg["slots"], cfg["ladder"], cfg["T"]
-    logits = W.slotcache_logits(W.config_seed(4), L, E, T, cfg["zipf"])
+    logits = W.slotcache_logits(W.WORKLOADS["slotcache"]["seed"], L, E, T, cfg["zipf"])
     ids, w = _route_all(logits, k)
     st = _compare_trace(L, E, S, k, a, b, ids, w)
     # sanity of the workload: both fetch kinds and drops occur
@@ -143,11 +143,11 @@ def test_slotcache_tier_and_lfu_bit_exact(policy, int2_slots, decay, seeded, T_c
 def test_slotcache_full_trace_with_tier_and_lfu():
     """The slot-cache decode trace at full shape with a 100-slot 2-bit tier and
     LFU (decay 0.95) seeded from a separate warm-up trace."""
-    cfg = W.CONFIGS[4]
+    cfg = W.WORKLOADS["slotcache"]
     L, E, k, S, (a, b), T = cfg["L"], cfg["E"], cfg["k"], cfg["slots"], cfg["ladder"], cfg["T"]
-    logits = W.slotcache_logits(W.config_seed(4), L, E, T, cfg["zipf"])
+    logits = W.slotcache_logits(W.WORKLOADS["slotcache"]["seed"], L, E, T, cfg["zipf"])
     ids, w = _route_all(logits, k)
-    warm = W.slotcache_logits(W.config_seed(4) + 1, L, E, 64, cfg["zipf"])
+    warm = W.slotcache_logits(W.WORKLOADS["slotcache"]["seed"] + 1, L, E, 64, cfg["zipf"])
     wids, _ = _route_all(warm, k)
     seed = np.zeros(L * E, np.float32)
     for l in range(L):
@@ -188,9 +188,9 @@ def test_slotcache_prefetch_bit_exact(policy, int2_slots, ring, recall):
 def test_slotcache_full_trace_with_prefetch():
     """The slot-cache decode trace at full shape with a 32-entry ring fed by
     12-expert predictions holding 75% of the true top-6, two layers ahead."""
-    cfg = W.CONFIGS[4]
+    cfg = W.WORKLOADS["slotcache"]
     L, E, k, S, (a, b), T = cfg["L"], cfg["E"], cfg["k"], cfg["slots"], cfg["ladder"], cfg["T"]
-    logits = W.slotcache_logits(W.config_seed(4), L, E, T, cfg["zipf"])
+    logits = W.slotcache_logits(W.WORKLOADS["slotcache"]["seed"], L, E, T, cfg["zipf"])
     ids, w = _route_all(logits, k)
     st = _compare_trace(L, E, S, k, a, b, ids, w, ring=32, pred=_predictions(logits, k, 0.75))
     assert st["ring_hits"] > 0

@@ -10,8 +10,8 @@ from mxfp4_routed_expert_renorm_amd import workloads as W
 
 
 def test_sparse_equals_dense_brute_force_tiny():
-    cfg = W.CONFIGS[0]
-    d = W.make_layer_inputs(cfg, W.config_seed(0))
+    cfg = W.WORKLOADS["tiny"]
+    d = W.make_layer_inputs(cfg, W.WORKLOADS["tiny"]["seed"])
     E, H, I, k = cfg["E"], cfg["H"], cfg["I"], cfg["k"]
     x = d["x"].astype(np.float64)
     logits = O.router_logits(x, d["router_w"])
@@ -45,7 +45,7 @@ def test_all_ones_expert_closed_form():
 
 
 def test_one_hot_input_selects_a_column():
-    cfg = W.CONFIGS[0]
+    cfg = W.WORKLOADS["tiny"]
     H, I = cfg["H"], cfg["I"]
     rec = W.fp4_record(3, 1, 0, H, I)
     W1, W3, W2 = O.expert_weights(rec, H, I)
@@ -79,7 +79,7 @@ def test_combine_rank_order_and_shared():
 
 
 def test_layer_forward_dropped_rank_contributes_nothing():
-    cfg = W.CONFIGS[0]
+    cfg = W.WORKLOADS["tiny"]
     H, I = cfg["H"], cfg["I"]
     bank = W.fp4_bank(1, 1, 4, H, I)
     x = W.f32_normal(1, (3,), (1, H)).astype(np.float64)
@@ -170,7 +170,7 @@ def test_prefill_forward_error_bound_against_exact_layer():
     """With activations already on the MXFP8 grid, the prefill oracle differs
     from the exact layer only through the MXFP8 rounding of h, which is bounded
     elementwise by |W2| |dh| with |dh| <= 2^-4 |h| + 2^-10 * group scale."""
-    cfg = W.CONFIGS[0]
+    cfg = W.WORKLOADS["tiny"]
     H, I, E, k = cfg["H"], cfg["I"], cfg["E"], 2
     bank = W.fp4_bank(21, 1, E, H, I)
     x = W.f32_normal(21, (2,), (3, H)).astype(np.float64)

@@ -93,12 +93,12 @@ def _route_gpu(gpu_lib, logits, k):
     return ids.cpu().numpy(), w.cpu().numpy()
 
 
-@pytest.mark.parametrize("cfg_i", [1, 2, 3])
-def test_route_bit_exact_ids(gpu_lib, cfg_i):
-    cfg = W.CONFIGS[cfg_i]
-    d = W.make_layer_inputs(cfg, W.config_seed(cfg_i), step=0, with_bank=False)
+@pytest.mark.parametrize("wl", ["decode-b1", "decode-b64", "prefill"])
+def test_route_bit_exact_ids(gpu_lib, wl):
+    cfg = W.WORKLOADS[wl]
+    d = W.make_layer_inputs(cfg, cfg["seed"], step=0, with_bank=False)
     lg = d["logits"]
-    log(f"route parity config {cfg_i}: T={lg.shape[0]} E={lg.shape[1]} k={cfg['k']}")
+    log(f"route parity {wl}: T={lg.shape[0]} E={lg.shape[1]} k={cfg['k']}")
     ids, w = _route_gpu(gpu_lib, lg, cfg["k"])
     oids, ow = O.route(lg, cfg["k"])
     assert np.array_equal(ids, oids)
@@ -141,8 +141,8 @@ def test_router_logits_and_decisions_tiny(gpu_lib):
     logits, the oracle on fp64 ones; decisions must agree wherever the k-th
     and (k+1)-th logits are not within 1e-5 of each other."""
     torch = _torch()
-    cfg = W.CONFIGS[0]
-    d = W.make_layer_inputs(cfg, W.config_seed(0))
+    cfg = W.WORKLOADS["tiny"]
+    d = W.make_layer_inputs(cfg, W.WORKLOADS["tiny"]["seed"])
     T, E, H, k = cfg["T"], cfg["E"], cfg["H"], cfg["k"]
     logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
     gpu_lib.moe_router_logits(dev(d["x"]), dev(d["router_w"]), logits)
@@ -218,10 +218,10 @@ class Layer:
         return out
 
 
-def _layer_check(gpu_lib, cfg_i, steps=(0,), bank=None):
+def _layer_check(gpu_lib, wl, steps=(0,), bank=None):
     torch = _torch()
-    cfg = W.CONFIGS[cfg_i]
-    seed = W.config_seed(cfg_i)
+    cfg = W.WORKLOADS[wl]
+    seed = cfg["seed"]
     E, H, I, k, T = cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"]
     if bank is None:
         d0 = W.make_layer_inputs(cfg, seed, 0)
@@ -232,7 +232,7 @@ def _layer_check(gpu_lib, cfg_i, steps=(0,), bank=None):
     wcache = {}
     for step in steps:
         d = W.make_layer_inputs(cfg, seed, step, with_bank=False)
-        log(f"layer parity config {cfg_i} step {step}")
+        log(f"layer parity {wl} step {step}")
         if cfg["x_dtype"] == "f32":
             x_dev = dev(d["x"])
             x64 = d["x"].astype(np.float64)
@@ -285,13 +285,13 @@ def _layer_check(gpu_lib, cfg_i, steps=(0,), bank=None):
 
 
 def test_layer_tiny_fp32(gpu_lib):
-    _layer_check(gpu_lib, 0, steps=(0, 1, 2))
+    _layer_check(gpu_lib, "tiny", steps=(0, 1, 2))
 
 
 def test_layer_decode_b1_full_size(gpu_lib):
     """Batch-1 decode at the full shape (256 experts + shared, H 4096,
     I 2048, top-8), the launch configuration the benchmark times."""
-    _layer_check(gpu_lib, 1, steps=(0, 1))
+    _layer_check(gpu_lib, "decode-b1", steps=(0, 1))
 
 
 def _mixed_case(gpu_lib, T, xbf16, with_shared, seed):
@@ -597,8 +597,8 @@ def test_layer_decode_b64_full_size(gpu_lib):
     Zipf-skewed routing) in the launch configuration the benchmark times;
     outputs compared on a seeded sample of tokens."""
     torch = _torch()
-    cfg = W.CONFIGS[2]
-    seed = W.config_seed(2)
+    cfg = W.WORKLOADS["decode-b64"]
+    seed = W.WORKLOADS["decode-b64"]["seed"]
     E, H, I, k, T = cfg["E"], cfg["H"], cfg["I"], cfg["k"], cfg["T"]
     d = W.make_layer_inputs(cfg, seed, 0)
     bank, shared = d["bank"], d["shared_rec"]

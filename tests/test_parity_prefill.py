@@ -90,10 +90,10 @@ def test_prefill_no_shared_small(gpu_lib):
 def test_prefill_full_size_sampled(gpu_lib):
     """The prefill workload's shape: 4096 tokens, 256 experts + shared, H 4096,
     I 2048, top-8; outputs compared on a seeded sample of tokens."""
-    cfg = W.CONFIGS[3]
+    cfg = W.WORKLOADS["prefill"]
     rng = np.random.default_rng(43)
     sample = sorted(rng.choice(cfg["T"], 12, replace=False).tolist())
-    _prefill_case(gpu_lib, E=cfg["E"], H=cfg["H"], I=cfg["I"], k=cfg["k"], T=cfg["T"], seed=W.config_seed(3),
+    _prefill_case(gpu_lib, E=cfg["E"], H=cfg["H"], I=cfg["I"], k=cfg["k"], T=cfg["T"], seed=W.WORKLOADS["prefill"]["seed"],
                   sample=sample)
 
 

@@ -121,9 +121,9 @@ def test_slotcache_loop_fused_b1_path(gpu_lib):
 def test_slotcache_loop_full_size(gpu_lib):
     """The slot-cache decode workload's shape: 8 layers x 256 experts, H 4096,
     I 2048, 512 slots, top-6, ladder (2,4); 16 tokens, outputs on every 4th."""
-    cfg = W.CONFIGS[4]
+    cfg = W.WORKLOADS["slotcache"]
     _run(gpu_lib, L=cfg["L"], E=cfg["E"], H=cfg["H"], I=cfg["I"], S=cfg["slots"], k=cfg["k"],
-         a=cfg["ladder"][0], b=cfg["ladder"][1], T=16, seed=W.config_seed(4), check_every=4)
+         a=cfg["ladder"][0], b=cfg["ladder"][1], T=16, seed=W.WORKLOADS["slotcache"]["seed"], check_every=4)
 
 
 def test_slotcache_loop_int2_tier_lfu(gpu_lib):
