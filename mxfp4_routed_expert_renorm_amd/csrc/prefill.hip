@@ -566,80 +566,34 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(PrefillArgs a) {
 // block scale is a power of two) and multiplied on v_mfma_f32_32x32x16_bf16
 // against the bf16 activations, so the products are exact as on the batch-1
 // path.  Items are (M tile of up to 64 grouped rows of one record, 256 weight
-// rows) and run the prefill GEMM's stage pipeline.  A tile of two M blocks
+// rows); their K stages go from HBM straight into a ring of LDS stages (see
+// dgemm_item below).  A tile of two M blocks
 // gives wavefront w M block w / 2 and column half w % 2 (for gate/up, 64 gate
 // and the same 64 up columns); a tile of one M block (most of a decode
 // batch's groups) splits the columns four ways instead, so no wavefront idles.  A K step of the MFMA takes, per lane, 8 consecutive elements of
 // the 32 its FP4 piece covers; the activation fragment is read at the same K.
 
 constexpr int kDMT = 64;                      // grouped rows per item at most
-#ifndef MOE_DG_KS
-#define MOE_DG_KS 128
-#endif
-constexpr int kDKS = MOE_DG_KS;               // K per stage (128 or 256)
+constexpr int kDKS = 128;                     // K per stage
 constexpr int kDThreads = 256;                // 4 wavefronts
-constexpr int kDArow = 2 * kDKS + 16;         // padded bytes of a bf16 activation row per stage
-constexpr int kDBrow = kDKS / 2 + 16;         // padded bytes of an FP4 weight row per stage
 constexpr int kDCA = 2 * kDKS / 16;           // 16-byte pieces per activation row and stage
 constexpr int kDCB = kDKS / 32;               // 16-byte pieces per weight row and stage
 constexpr int kDPiecesA = kDMT * kDCA / kDThreads;
 constexpr int kDPiecesB = kNR * kDCB / kDThreads;
 static_assert(kDPiecesA * kDThreads == kDMT * kDCA && kDPiecesB * kDThreads == kNR * kDCB,
               "stage pieces must divide evenly over the workgroup");
-#ifndef MOE_DG_DEPTH
-#define MOE_DG_DEPTH 1
-#endif
-constexpr int kDDepth = MOE_DG_DEPTH;         // K stages held in registers ahead of the LDS stage
 #ifndef MOE_DG_PER_CU
 #define MOE_DG_PER_CU 1  // workgroups per CU (two fit, but measured slower)
 #endif
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-// the stage's scale bytes of one weight row: one per 32 elements of K
-typedef std::conditional<kDKS == 256, uint64_t, uint32_t>::type DStageScales;
-
-struct alignas(16) DGemmSmem {
-  uint8_t a[2][kDMT * kDArow];
-  uint8_t b[2][kNR * kDBrow];
-  DStageScales bs[2][kDThreads];  // entry i: the stage's scale bytes of weight row i
-  int32_t pm[kDMT];           // down: the (token, rank) pair of each tile row
-};
-
-struct DStageRegs {
-  u32x4_t a[kDPiecesA];
-  u32x4_t b[kDPiecesB];
-  DStageScales bs;
-};
-
+// global offsets of what this thread loads into stage slot p = tid + j*kDThreads
 struct DLoadOffs {
-  uint32_t a[kDPiecesA];  // piece p = tid + j*kDThreads: activation row p/kDCA (clamped), 16 bytes at 16*(p%kDCA)
-  uint32_t b[kDPiecesB];  // piece p = tid + j*kDThreads: weight row p/kDCB, 16 bytes at 16*(p%kDCB)
+  uint32_t a[kDPiecesA];  // activation row r = p/kDCA (clamped), piece (p % kDCA) ^ (r % 16)
+  uint32_t b[kDPiecesB];  // weight row r = p/kDCB, piece (p % kDCB) ^ (r / 4 % 4)
   uint32_t bs;            // scale row of weight row tid
 };
-
-__device__ __forceinline__ void dstage_load(DStageRegs& r, const DLoadOffs& o, const uint8_t* abase,
-                                            const uint8_t* rec, int k0) {
-#pragma unroll
-  for (int j = 0; j < kDPiecesA; ++j) r.a[j] = *(const u32x4_t*)(abase + (o.a[j] + 2 * k0));
-#pragma unroll
-  for (int j = 0; j < kDPiecesB; ++j) r.b[j] = *(const u32x4_t*)(rec + (o.b[j] + k0 / 2));
-  r.bs = *(const DStageScales*)(rec + (o.bs + k0 / 32));
-}
-
-__device__ __forceinline__ void dstage_store(DGemmSmem& sm, int buf, const DStageRegs& r, int tid) {
-#pragma unroll
-  for (int j = 0; j < kDPiecesA; ++j) {
-    const int p = tid + j * kDThreads;
-    *(u32x4_t*)(sm.a[buf] + (p / kDCA) * kDArow + 16 * (p % kDCA)) = r.a[j];
-  }
-#pragma unroll
-  for (int j = 0; j < kDPiecesB; ++j) {
-    const int p = tid + j * kDThreads;
-    *(u32x4_t*)(sm.b[buf] + (p / kDCB) * kDBrow + 16 * (p % kDCB)) = r.b[j];
-  }
-  sm.bs[buf][tid] = r.bs;
-}
 
 // LDS weight-tile block of the wavefront's column block j (0..NBW-1) in its
 // column share cs.  NBW = 4 (a tile of two M blocks; cs = column half):
@@ -658,72 +612,120 @@ struct DItemCtx {
   int tid, c, h, wave, mp, nh, nstage, rows, start, nt;
 };
 
+// Each stage's activation, weight and scale pieces go from HBM to LDS by
+// global_load_lds (no register staging) into a ring of kDRing stages,
+// kDRing - 1 stages ahead of the one being multiplied.  A wavefront waits for
+// its own loads of a stage by vmcnt, and one barrier per stage publishes
+// everyone's.  Lane l of a direct load writes 16-byte LDS slot base + l, so
+// the lane decides which global piece lands in which slot: the pieces are
+// XOR-swizzled (activation row r: piece q at slot 16 r + (q ^ (r % 16));
+// weight row r: piece q at slot 4 r + (q ^ (r / 4 % 4))) so that the 32 rows
+// one MFMA operand reads fall on distinct banks, two lanes per bank.
+#ifndef MOE_DG_RING
+#define MOE_DG_RING 3  // 2 and 4 measured slower
+#endif
+constexpr int kDRing = MOE_DG_RING;
+constexpr int kDStageA = kDMT * 2 * kDKS;   // bytes of a stage's activation tile
+constexpr int kDStageB = kNR * kDKS / 2;    // bytes of a stage's weight tile
+static_assert(kDRing >= 2 && kDRing <= 6, "ring of 2..6 stages");
+
+struct alignas(16) DGemmSmem {
+  uint8_t a[kDRing][kDStageA];
+  uint8_t b[kDRing][kDStageB];
+  uint32_t bs[kDRing][kDThreads];  // entry i: the stage's 4 scale bytes of weight row i
+  int32_t pm[kDMT];
+};
+
+typedef __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// this thread's loads of stage k0 into ring slot buf: pieces j < NA of the
+// activation tile (NA = 2: its first 32 rows only) and every piece of the
+// weight tile (slot tid + 256 j, offsets swizzled by the caller), and the
+// scale word of weight row tid
+template <int NA>
+__device__ __forceinline__ void dstage_issue_lds(DGemmSmem& sm, int buf, const DLoadOffs& o, const uint8_t* abase,
+                                                 const uint8_t* rec, int k0, int wave) {
+#pragma unroll
+  for (int j = 0; j < NA; ++j)
+    __builtin_amdgcn_global_load_lds((gptr_t)(abase + (o.a[j] + 2 * k0)),
+                                     (lptr_t)(sm.a[buf] + (j * kDThreads + wave * 64) * 16), 16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kDPiecesB; ++j)
+    __builtin_amdgcn_global_load_lds((gptr_t)(rec + (o.b[j] + k0 / 2)),
+                                     (lptr_t)(sm.b[buf] + (j * kDThreads + wave * 64) * 16), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gptr_t)(rec + (o.bs + k0 / 32)), (lptr_t)(&sm.bs[buf][wave * 64]), 4, 0, 0);
+}
+
 // NBW column blocks per wavefront (4: M block mp of two, 2: the only M block),
 // LIVE false: the wavefront's M block is past the tile's rows
 template <int NMAT, int NBW, bool LIVE>
 __device__ __forceinline__ void dgemm_item(DGemmSmem& sm, const PrefillArgs& a, const DItemCtx& x) {
   const int tid = x.tid, c = x.c, h = x.h, nstage = x.nstage;
-  const int mb = NBW == 4 ? x.mp : 0;       // the wavefront's M block
-  const int cs = NBW == 4 ? x.nh : x.wave;  // its column share
+  const int mb = NBW == 4 ? x.mp : 0;
+  const int cs = NBW == 4 ? x.nh : x.wave;
+  // a tile of one M block reads activation rows 0..31 only: half the pieces
+  constexpr int NA = NBW == 4 ? kDPiecesA : kDPiecesA / 2;
+  constexpr int kLoads = NA + kDPiecesB + 1;  // load instructions per stage and thread
   v16f acc[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
 
-  // R[j] holds stage j mod kDDepth; nstage is a multiple of kDDepth (checked
-  // at launch); the tail's loads are clamped to the last stage
-  DStageRegs R[kDDepth];
-#pragma unroll
-  for (int d = 0; d < kDDepth; ++d) dstage_load(R[d], x.O, x.abase, x.rec, d * kDKS);
   __syncthreads();  // the previous item's last stage reads and epilogue are done
-  dstage_store(sm, 0, R[0], tid);
   if (NMAT == 1 && tid < kDMT) sm.pm[tid] = a.perm[x.start + min(tid, x.rows - 1)];
-  dstage_load(R[0], x.O, x.abase, x.rec, min(kDDepth, nstage - 1) * kDKS);
-  __syncthreads();
+  // stages 0 .. kDRing-2 (past the last stage: the last one again, never read)
+#pragma unroll
+  for (int d = 0; d < kDRing - 1; ++d) dstage_issue_lds<NA>(sm, d, x.O, x.abase, x.rec, min(d, nstage - 1) * kDKS, x.wave);
 
-  const int arow = (32 * mb + c) * kDArow;
-  for (int s0 = 0; s0 < nstage; s0 += kDDepth) {
+  const int arow = 32 * mb + c;
+  for (int s = 0; s < nstage; ++s) {
+    const int buf = s % kDRing;
+    // this wavefront's loads of stage s are done when at most the later
+    // kDRing-2 stages' loads are outstanding
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads * (kDRing - 2)) : "memory");
+    // everyone's stage s is in LDS and everyone is done with stage s-1: a bare
+    // barrier (a fenced one would wait for every load in flight, the ring's
+    // later stages included); the empty asm statements keep the compiler from
+    // moving LDS accesses across it
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    dstage_issue_lds<NA>(sm, (s + kDRing - 1) % kDRing, x.O, x.abase, x.rec, min(s + kDRing - 1, nstage - 1) * kDKS,
+                         x.wave);
+    if (LIVE) {
 #pragma unroll
-    for (int d = 0; d < kDDepth; ++d) {
-      const int s = s0 + d;
-      const int buf = (kDDepth % 2 == 0) ? (d & 1) : (s & 1);
-      if (LIVE) {
+      for (int kc = 0; kc < kDKS / 64; ++kc) {
+        u32x4_t q[NBW];
+        float sc[NBW];
 #pragma unroll
-        for (int kc = 0; kc < kDKS / 64; ++kc) {
-          // the lane's FP4 piece of each column block: K [kc*64 + 32h, +32) of weight row c
-          u32x4_t q[NBW];
-          float sc[NBW];
+        for (int j = 0; j < NBW; ++j) {
+          const int r = dcol_block<NMAT, NBW>(cs, j) * 32 + c;
+          const int qq = (2 * kc + h) ^ ((r >> 2) & 3);
+          q[j] = *(const u32x4_t*)(sm.b[buf] + (r * 4 + qq) * 16);
+          sc[j] = e8m0_to_f32((sm.bs[buf][r] >> (8 * (2 * kc + h))) & 0xffu);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int qa = (kc * 8 + 4 * h + m) ^ (arow & 15);
+          const v8bf av = *(const v8bf*)(sm.a[buf] + (arow * 16 + qa) * 16);
 #pragma unroll
           for (int j = 0; j < NBW; ++j) {
-            const int r = dcol_block<NMAT, NBW>(cs, j) * 32 + c;
-            q[j] = *(const u32x4_t*)(sm.b[buf] + r * kDBrow + kc * 32 + 16 * h);
-            sc[j] = e8m0_to_f32((uint32_t)(sm.bs[buf][r] >> (8 * (2 * kc + h))) & 0xffu);
-          }
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            // K [kc*64 + 32h + 8m, +8): activations of row 32*mb + c, weights of each block's row c
-            const v8bf av = *(const v8bf*)(sm.a[buf] + arow + 2 * (kc * 64 + 32 * h + 8 * m));
-#pragma unroll
-            for (int j = 0; j < NBW; ++j) {
-              u32x4_t wv;
-              wv.x = fp4x2_to_bf16x2_scaled<0>(q[j][m], sc[j]);
-              wv.y = fp4x2_to_bf16x2_scaled<1>(q[j][m], sc[j]);
-              wv.z = fp4x2_to_bf16x2_scaled<2>(q[j][m], sc[j]);
-              wv.w = fp4x2_to_bf16x2_scaled<3>(q[j][m], sc[j]);
-              acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(v8bf, wv), acc[j], 0, 0, 0);
-            }
+            u32x4_t wv;
+            wv.x = fp4x2_to_bf16x2_scaled<0>(q[j][m], sc[j]);
+            wv.y = fp4x2_to_bf16x2_scaled<1>(q[j][m], sc[j]);
+            wv.z = fp4x2_to_bf16x2_scaled<2>(q[j][m], sc[j]);
+            wv.w = fp4x2_to_bf16x2_scaled<3>(q[j][m], sc[j]);
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(v8bf, wv), acc[j], 0, 0, 0);
           }
         }
       }
-      dstage_store(sm, buf ^ 1, R[(d + 1) % kDDepth], tid);
-      dstage_load(R[(d + 1) % kDDepth], x.O, x.abase, x.rec, min(s + 1 + kDDepth, nstage - 1) * kDKS);
-      __syncthreads();
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the ring's trailing loads land before the next item reuses it
   if (!LIVE) return;
 
-  // lane indices made opaque so the epilogue's address arithmetic is not hoisted into the loop
   int ce = c, he = h;
   asm volatile("" : "+v"(ce), "+v"(he));
   const int H = a.H, I = a.I;
@@ -795,12 +797,14 @@ __global__ __launch_bounds__(kDThreads) void dgemm_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < kDPiecesA; ++j) {
       const int p = tid + j * kDThreads;
-      x.O.a[j] = act_row(p / kDCA) * (uint32_t)(2 * K) + 16u * (p % kDCA);
+      const int r = p / kDCA, q = (p % kDCA) ^ (r & 15);  // slot p holds piece q
+      x.O.a[j] = act_row(r) * (uint32_t)(2 * K) + 16u * q;
     }
 #pragma unroll
     for (int j = 0; j < kDPiecesB; ++j) {
       const int p = tid + j * kDThreads;
-      x.O.b[j] = weight_row(p / kDCB, false) + 16u * (p % kDCB);
+      const int r = p / kDCB, q = (p % kDCB) ^ ((r >> 2) & 3);
+      x.O.b[j] = weight_row(r, false) + 16u * q;
     }
     x.O.bs = weight_row(tid, true);
     x.abase = NMAT == 2 ? (const uint8_t*)a.xb : (const uint8_t*)a.hb;
@@ -943,8 +947,7 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
 }
 
 bool decode_mfma_ok(int H, int I) {
-  return H >= 256 && I >= 128 && H % 256 == 0 && I % 128 == 0 && H % kDKS == 0 && I % kDKS == 0 &&
-         (H / kDKS) % kDDepth == 0 && (I / kDKS) % kDDepth == 0;
+  return H >= 256 && I >= 128 && H % 256 == 0 && I % 128 == 0 && H % kDKS == 0 && I % kDKS == 0;
 }
 
 // Grouped decode of T >= 2 bf16 tokens on bf16 MFMA: plan (keys by slot, the
