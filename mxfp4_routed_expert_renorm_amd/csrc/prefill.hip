@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "group_dev.h"
 
 namespace moe {
 
@@ -135,9 +136,10 @@ struct PrefillArgs {
   float* yf;            // [P][H] fp32, pair order (when non-null, instead of y)
 };
 
-__global__ __launch_bounds__(256) void prefill_keys_kernel(PrefillArgs a) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= a.T * a.K1) return;
+// key of pair p = (token p / K1, rank p % K1): the slot id, E for the shared
+// expert, -1 for an id out of range (its output row is zeroed: it contributes
+// nothing)
+__device__ __forceinline__ void pair_key(const PrefillArgs& a, int p) {
   const int t = p / a.K1, r = p % a.K1;
   int key;
   if (r == a.k) {
@@ -147,11 +149,16 @@ __global__ __launch_bounds__(256) void prefill_keys_kernel(PrefillArgs a) {
     key = (e >= 0 && e < a.E) ? e : -1;
   }
   a.keys[p] = key;
-  if (key < 0) {  // an out-of-range id contributes nothing: its output row is zero
+  if (key < 0) {
     uint4* yrow = a.yf ? (uint4*)(a.yf + (size_t)p * a.H) : (uint4*)(a.y + (size_t)p * a.H);
     const int n16 = a.yf ? a.H / 4 : a.H / 8;
     for (int j = 0; j < n16; ++j) yrow[j] = make_uint4(0u, 0u, 0u, 0u);
   }
+}
+
+__global__ __launch_bounds__(256) void prefill_keys_kernel(PrefillArgs a) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p < a.T * a.K1) pair_key(a, p);
 }
 
 // items[0] = number of M tiles, then (key, start, rows) per tile, start being
@@ -160,10 +167,9 @@ __global__ __launch_bounds__(256) void prefill_keys_kernel(PrefillArgs a) {
 // blocks (the last one takes the rest), so e.g. 140 rows run as one tile of
 // the prefill GEMM (MT 192).
 template <int MT>
-__global__ __launch_bounds__(64) void prefill_items_kernel(const int32_t* __restrict__ counts,
-                                                           const int32_t* __restrict__ offsets, int nkeys,
-                                                           int32_t* __restrict__ items) {
-  const int lane = threadIdx.x;
+__device__ __forceinline__ void items_body(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+                                           int nkeys, int32_t* __restrict__ items) {
+  const int lane = threadIdx.x & 63;
   int n = 0;
   for (int base = 0; base < nkeys; base += 64) {
     const int key = base + lane;
@@ -186,6 +192,31 @@ __global__ __launch_bounds__(64) void prefill_items_kernel(const int32_t* __rest
     n += __shfl(incl, 63, 64);
   }
   if (lane == 0) items[0] = n;
+}
+
+template <int MT>
+__global__ __launch_bounds__(64) void prefill_items_kernel(const int32_t* __restrict__ counts,
+                                                           const int32_t* __restrict__ offsets, int nkeys,
+                                                           int32_t* __restrict__ items) {
+  items_body<MT>(counts, offsets, nkeys, items);
+}
+
+// The whole plan of a decode batch's grouped GEMM in one launch of one
+// workgroup: the pairs' keys, their stable grouping (counts, offsets, perm),
+// then the M tiles.  The barriers order each step's global writes before the
+// next step's reads within the workgroup; wavefront 0 writes counts and
+// offsets in the grouping and reads them, lane for lane, for the tiles.  (A
+// prefill's tens of thousands of pairs group faster with the keys spread over
+// many workgroups, so prefill keeps three launches.)
+template <int MT>
+__global__ __launch_bounds__(kGroupThreads) void plan_kernel(PrefillArgs a, int W) {
+  extern __shared__ int lds[];
+  const int P = a.T * a.K1, nkeys = a.E + 1;
+  for (int p = threadIdx.x; p < P; p += kGroupThreads) pair_key(a, p);
+  __syncthreads();
+  group_body(a.keys, P, nkeys, W, a.counts, a.offsets, a.perm, lds);
+  __syncthreads();
+  if (threadIdx.x < 64) items_body<MT>(a.counts, a.offsets, nkeys, a.items);
 }
 
 __device__ __forceinline__ const uint8_t* key_record(const PrefillArgs& a, int key) {
@@ -980,13 +1011,9 @@ moe_status launch_decode_mfma(const moe_layer* Lr, const void* x, int T, int k, 
   a.hb = h;
   a.yf = y;
   {
-    launch(MOE_PROF_PLAN, prefill_keys_kernel, dim3((P + 255) / 256), dim3(256), 0, s, a);
-    MOE_LAUNCH_CHECK();
-  }
-  moe_status st = launch_group(a.keys, P, E + 1, a.counts, a.offsets, a.perm, s);
-  if (st != MOE_OK) return st;
-  {
-    launch(MOE_PROF_PLAN, prefill_items_kernel<kDMT>, dim3(1), dim3(64), 0, s, a.counts, a.offsets, E + 1, a.items);
+    const int W = group_chunks(E + 1);
+    const size_t lds = (size_t)(W + 1) * (E + 1) * sizeof(int);
+    launch(MOE_PROF_PLAN, plan_kernel<kDMT>, dim3(1), dim3(kGroupThreads), lds, s, a, W);
     MOE_LAUNCH_CHECK();
   }
   const long max_items_m = (long)P / kDMT + std::min(P, E + 1) + 1;
