@@ -47,13 +47,19 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ keys, int
   const int lo = wave * chunk, hi = min(n, lo + chunk);
   for (int i = tid; i < W * nkeys; i += kGroupThreads) hist[i] = 0;
   __syncthreads();
-  // 1. per-chunk histograms
-  if (wave < W) {
+  // 1. per-chunk histograms (16 keys per lane in flight: the loads are
+  // unconditional, at clamped positions, and the out-of-range ones unused)
+  if (wave < W && lo < hi) {
     int* hw = hist + wave * nkeys;
-#pragma unroll 4
-    for (int i = lo + lane; i < hi; i += 64) {
-      const int key = keys[i];
-      if (key >= 0 && key < nkeys) atomicAdd(&hw[key], 1);
+    for (int base = lo; base < hi; base += 16 * 64) {
+      int kk[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) kk[j] = keys[min(base + j * 64 + lane, hi - 1)];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = kk[j];
+        if (base + j * 64 + lane < hi && key >= 0 && key < nkeys) atomicAdd(&hw[key], 1);
+      }
     }
   }
   __syncthreads();
@@ -91,17 +97,24 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ keys, int
   __syncthreads();
   for (int i = tid; i < W * nkeys; i += kGroupThreads) hist[i] += tot[i % nkeys];
   __syncthreads();
-  // 3. stable placement, one chunk per wavefront
-  if (wave < W) {
+  // 3. stable placement, one chunk per wavefront (an empty chunk loads nothing)
+  if (wave < W && lo < hi) {
     int* cur = hist + wave * nkeys;
     int nbits = 1;
     while ((1 << nbits) < nkeys) ++nbits;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int next = (lo + lane < hi) ? keys[lo + lane] : -1;
+    // keys of the next kPF steps in registers, rotated one step at a time
+    // (unconditional loads at clamped positions; positions past hi are invalid)
+    constexpr int kPF = 8;
+    int kb[kPF];
+#pragma unroll
+    for (int j = 0; j < kPF; ++j) kb[j] = keys[min(lo + j * 64 + lane, hi - 1)];
     for (int base = lo; base < hi; base += 64) {
       const int i = base + lane;
-      int key = next;
-      next = (i + 64 < hi) ? keys[i + 64] : -1;
+      int key = kb[0];
+#pragma unroll
+      for (int j = 0; j + 1 < kPF; ++j) kb[j] = kb[j + 1];
+      kb[kPF - 1] = keys[min(base + kPF * 64 + lane, hi - 1)];
       const bool valid = i < hi && key >= 0 && key < nkeys;
       if (!valid) key = -1;
       // lanes with an identical key (invalid lanes match only each other)
