@@ -581,7 +581,7 @@ def _batched_bf16_case(gpu_lib, T, E, k, with_shared, seed, H=512, I=256, bad_sl
     log(f"batched bf16 MFMA T={T} E={E} k={k} shared={with_shared}: ok over {len(list(tokens))} tokens")
 
 
-@pytest.mark.parametrize("I", [256, 512])   # down K of 2 and 4 stages: shorter than the LDS ring and longer
+@pytest.mark.parametrize("I", [128, 256, 512])   # down K of 1, 2 and 4 stages: within, at and past the LDS ring
 @pytest.mark.parametrize("T,E,k,with_shared,bad", [
     (2, 16, 4, True, 0),      # groups of one or two rows
     (37, 16, 4, True, 3),     # ragged groups, dropped ranks
