@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cstring>
 #include <vector>
 
@@ -82,7 +84,8 @@ struct moe_cache {
   };
   std::vector<Copy> copies;
   // device-side plumbing (created on first ensure)
-  void* pin_in = nullptr;   // pinned, mapped: ids [T*k] int32, w [T*k] f32
+  void* pin_in = nullptr;   // pinned, mapped: ids [T*k] int32, w [T*k] f32, then the sequence word
+  uint32_t seq = 0;         // sequence number of the last call's picks
   void* pin_out = nullptr;  // pinned, mapped: slots [T*k] int32, w' [T*k] f32, prec [T*k] int8
   void* pin_in_dev = nullptr;   // their device addresses
   void* pin_out_dev = nullptr;
@@ -95,6 +98,7 @@ namespace moe {
 namespace {
 
 size_t pin_in_bytes(const moe_cache_desc& d) { return (size_t)d.max_tokens * d.k * 8; }
+constexpr size_t kFlagBytes = 256;  // after the picks in the mapped input buffer: the call's sequence number
 size_t pin_out_bytes(const moe_cache_desc& d) { return (size_t)d.max_tokens * d.k * 9; }
 
 // the lowest-index empty slot not used by this call, else the unprotected slot
@@ -450,7 +454,8 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
   hipStream_t cs = (hipStream_t)compute, ps = copy ? (hipStream_t)copy : cs;
   const size_t n = (size_t)T * c->d.k;
   if (!c->pin_in) {
-    MOE_HIP_CHECK(hipHostMalloc(&c->pin_in, pin_in_bytes(c->d), hipHostMallocMapped));
+    MOE_HIP_CHECK(hipHostMalloc(&c->pin_in, pin_in_bytes(c->d) + kFlagBytes, hipHostMallocMapped));
+    std::memset(c->pin_in, 0, pin_in_bytes(c->d) + kFlagBytes);
     MOE_HIP_CHECK(hipHostMalloc(&c->pin_out, pin_out_bytes(c->d), hipHostMallocMapped));
     MOE_HIP_CHECK(hipHostGetDevicePointer(&c->pin_in_dev, c->pin_in, 0));
     MOE_HIP_CHECK(hipHostGetDevicePointer(&c->pin_out_dev, c->pin_out, 0));
@@ -459,16 +464,37 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
   }
   int32_t* ids_h = (int32_t*)c->pin_in;
   float* w_h = (float*)((char*)c->pin_in + (size_t)c->d.max_tokens * c->d.k * 4);
-  // the one host sync of the call: read the router's picks (one small kernel
-  // writes them into the mapped pinned buffer)
+  // the one host sync of the call: read the router's picks.  One small
+  // kernel writes them into the mapped pinned buffer, then the call's
+  // sequence number; the host polls that word.  A poll that has not seen it
+  // after 2 s falls back to waiting for the kernel's completion (which also
+  // reports a failed launch).
   {
     int32_t* ids_d = (int32_t*)c->pin_in_dev;
     float* w_d = (float*)((char*)c->pin_in_dev + (size_t)c->d.max_tokens * c->d.k * 4);
-    s = launch_cache_gather(ids_inout, w_inout, (int)n, ids_d, w_d, cs);
+    uint32_t* flag_d = (uint32_t*)((char*)c->pin_in_dev + pin_in_bytes(c->d));
+    s = launch_cache_gather(ids_inout, w_inout, (int)n, ids_d, w_d, flag_d, ++c->seq, cs);
     if (s != MOE_OK) return s;
   }
-  MOE_HIP_CHECK(hipEventRecord(c->ev_read, cs));
-  MOE_HIP_CHECK(hipEventSynchronize(c->ev_read));
+  {
+    const volatile uint32_t* flag_h = (const volatile uint32_t*)((char*)c->pin_in + pin_in_bytes(c->d));
+    bool seen = false;
+    const auto t0 = std::chrono::steady_clock::now();
+    for (uint64_t it = 0;; ++it) {
+      if (*flag_h == c->seq) {
+        seen = true;
+        break;
+      }
+      __builtin_ia32_pause();
+      if ((it & 4095) == 4095 && std::chrono::steady_clock::now() - t0 > std::chrono::seconds(2)) break;
+    }
+    if (!seen) {
+      MOE_HIP_CHECK(hipEventRecord(c->ev_read, cs));
+      MOE_HIP_CHECK(hipEventSynchronize(c->ev_read));
+      if (*flag_h != c->seq) return fail(MOE_EHIP, "moe_cache_ensure: the picks did not arrive");
+    }
+    std::atomic_thread_fence(std::memory_order_acquire);
+  }
   s = plan(c, layer, T, ids_h, w_h);
   if (s != MOE_OK) return s;
   // from here on the host state has advanced: a failure leaves the cache inconsistent

@@ -12,13 +12,23 @@ namespace moe {
 
 namespace {
 
-__global__ __launch_bounds__(256) void cache_gather_kernel(const int32_t* __restrict__ ids,
-                                                           const float* __restrict__ w, int n,
-                                                           int32_t* __restrict__ ids_h, float* __restrict__ w_h) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) {
+// One workgroup: the picks go out, then (after the workgroup's stores and a
+// system-scope fence) the call's sequence number, which the host polls: it
+// learns the picks as soon as they are in its memory, without waiting for
+// the kernel's completion signal.
+__global__ __launch_bounds__(1024) void cache_gather_kernel(const int32_t* __restrict__ ids,
+                                                            const float* __restrict__ w, int n,
+                                                            int32_t* __restrict__ ids_h, float* __restrict__ w_h,
+                                                            uint32_t* __restrict__ flag_h, uint32_t seq) {
+  for (int i = threadIdx.x; i < n; i += 1024) {
     ids_h[i] = ids[i];
     w_h[i] = w[i];
+  }
+  __threadfence_system();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence_system();
+    __hip_atomic_store(flag_h, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 
@@ -37,9 +47,9 @@ __global__ __launch_bounds__(256) void cache_scatter_kernel(const int32_t* __res
 
 }  // namespace
 
-moe_status launch_cache_gather(const int32_t* ids, const float* w, int n, int32_t* ids_h, float* w_h, hipStream_t s) {
-  if (n <= 0) return MOE_OK;
-  launch(MOE_PROF_CACHE, cache_gather_kernel, dim3((n + 255) / 256), dim3(256), 0, s, ids, w, n, ids_h, w_h);
+moe_status launch_cache_gather(const int32_t* ids, const float* w, int n, int32_t* ids_h, float* w_h, uint32_t* flag_h,
+                               uint32_t seq, hipStream_t s) {
+  launch(MOE_PROF_CACHE, cache_gather_kernel, dim3(1), dim3(1024), 0, s, ids, w, n, ids_h, w_h, flag_h, seq);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -213,7 +213,9 @@ moe_status launch_combine(const float* y, const float* w, const int8_t* prec, in
 moe_status launch_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int32_t* offsets,
                         int32_t* perm, hipStream_t s);
 // slot cache exchange: device picks -> mapped pinned host memory, and back
-moe_status launch_cache_gather(const int32_t* ids, const float* w, int n, int32_t* ids_h, float* w_h, hipStream_t s);
+// (flag_h: a word of the same mapped buffer that receives seq after the picks)
+moe_status launch_cache_gather(const int32_t* ids, const float* w, int n, int32_t* ids_h, float* w_h, uint32_t* flag_h,
+                               uint32_t seq, hipStream_t s);
 moe_status launch_cache_scatter(const int32_t* slots_h, const float* w_h, const int8_t* prec_h, int n, int32_t* ids,
                                 float* w, int8_t* prec, hipStream_t s);
 
