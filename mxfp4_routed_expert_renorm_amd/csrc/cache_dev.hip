@@ -24,12 +24,12 @@ __global__ __launch_bounds__(1024) void cache_gather_kernel(const int32_t* __res
     ids_h[i] = ids[i];
     w_h[i] = w[i];
   }
-  __threadfence_system();
+  // every wavefront waits for its own stores to reach this CU's L2, then one
+  // system-scope release by thread 0 (an L2 write-back) makes them all
+  // visible to the host ahead of the sequence number
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence_system();
-    __hip_atomic_store(flag_h, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-  }
+  if (threadIdx.x == 0) __hip_atomic_store(flag_h, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 __global__ __launch_bounds__(256) void cache_scatter_kernel(const int32_t* __restrict__ slots_h,
