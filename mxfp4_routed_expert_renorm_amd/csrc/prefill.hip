@@ -171,10 +171,14 @@ __device__ __forceinline__ void items_body(const int32_t* __restrict__ counts, c
                                            int nkeys, int32_t* __restrict__ items) {
   const int lane = threadIdx.x & 63;
   int n = 0;
+  // keys in the order nkeys-1, 0, 1, ..., nkeys-2: the shared expert's key
+  // (the last, and the largest group) first, so that its tiles, the heaviest
+  // items, are not the ones left for the last round of workgroups
   for (int base = 0; base < nkeys; base += 64) {
-    const int key = base + lane;
-    const int c = key < nkeys ? counts[key] : 0;
-    const int o = key < nkeys ? offsets[key] : 0;
+    const int kk = base + lane;
+    const int key = kk == 0 ? nkeys - 1 : kk - 1;
+    const int c = kk < nkeys ? counts[key] : 0;
+    const int o = kk < nkeys ? offsets[key] : 0;
     const int tiles = (c + MT - 1) / MT;
     int incl = tiles;
 #pragma unroll
