@@ -308,7 +308,10 @@ moe_status moe_cache_plan(moe_cache* c, int layer, int T, const int32_t* ids, co
  *   w_inout   [T][k] fp32 device: router weights in, renormalised survivors out
  *   prec_out  [T][k] int8 device: 0 FP4, 1 2-bit, -1 dropped
  * Enqueues a device->host read of ids and w on `compute` and waits for it (the one
- * host sync), runs the policy, enqueues the FP4 miss copies and 2-bit copies from the
+ * host sync: the host polls a sequence word that the read's kernel writes after the
+ * picks; after MOE_CACHE_POLL_US microseconds, read from the environment when the
+ * cache is created, default 2000000, 0 = no polling, it waits for the kernel's
+ * completion instead), runs the policy, enqueues the FP4 miss copies and 2-bit copies from the
  * pinned banks on `copy` (NULL = compute), makes `compute` wait for them, and
  * enqueues the small host->device writes of the results on `compute`.  Everything the
  * caller enqueues on `compute` afterwards sees the copied experts.  Not capturable in

@@ -49,6 +49,7 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -86,6 +87,7 @@ struct moe_cache {
   // device-side plumbing (created on first ensure)
   void* pin_in = nullptr;   // pinned, mapped: ids [T*k] int32, w [T*k] f32, then the sequence word
   uint32_t seq = 0;         // sequence number of the last call's picks
+  long poll_us = 2000000;   // how long the host polls for them before waiting on the event
   void* pin_out = nullptr;  // pinned, mapped: slots [T*k] int32, w' [T*k] f32, prec [T*k] int8
   void* pin_in_dev = nullptr;   // their device addresses
   void* pin_out_dev = nullptr;
@@ -370,6 +372,7 @@ moe_status moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
     return fail(MOE_EINVAL, "moe_cache_create: ladder a < b needs int2_host and int2_staging");
   moe_cache* c = new moe_cache();
   c->d = *d;
+  if (const char* e = std::getenv("MOE_CACHE_POLL_US")) c->poll_us = std::max(0L, std::atol(e));
   c->fp4_bytes = record_layout(d->H, d->I, 4).bytes;
   c->int2_bytes = record_layout(d->H, d->I, 2).bytes;
   c->map.assign((size_t)d->L * d->E, -1);
@@ -467,8 +470,9 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
   // the one host sync of the call: read the router's picks.  One small
   // kernel writes them into the mapped pinned buffer, then the call's
   // sequence number; the host polls that word.  A poll that has not seen it
-  // after 2 s falls back to waiting for the kernel's completion (which also
-  // reports a failed launch).
+  // within poll_us (2 s unless MOE_CACHE_POLL_US says otherwise; 0: no poll)
+  // falls back to waiting for the kernel's completion (which also reports a
+  // failed launch).
   {
     int32_t* ids_d = (int32_t*)c->pin_in_dev;
     float* w_d = (float*)((char*)c->pin_in_dev + (size_t)c->d.max_tokens * c->d.k * 4);
@@ -480,13 +484,13 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
     const volatile uint32_t* flag_h = (const volatile uint32_t*)((char*)c->pin_in + pin_in_bytes(c->d));
     bool seen = false;
     const auto t0 = std::chrono::steady_clock::now();
-    for (uint64_t it = 0;; ++it) {
+    for (uint64_t it = 0; c->poll_us > 0; ++it) {
       if (*flag_h == c->seq) {
         seen = true;
         break;
       }
       __builtin_ia32_pause();
-      if ((it & 4095) == 4095 && std::chrono::steady_clock::now() - t0 > std::chrono::seconds(2)) break;
+      if ((it & 63) == 63 && std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(c->poll_us)) break;
     }
     if (!seen) {
       MOE_HIP_CHECK(hipEventRecord(c->ev_read, cs));

@@ -113,6 +113,15 @@ def test_slotcache_loop_small(gpu_lib):
     assert st["evictions"] > 0
 
 
+@pytest.mark.parametrize("poll_us", ["0", "1"])
+def test_slotcache_loop_event_wait(gpu_lib, monkeypatch, poll_us):
+    """The host's wait for each call's picks without its poll (0: the kernel's
+    completion event only) or with a 1 us poll budget (the poll mostly gives up
+    and falls back to the event): slot maps and outputs as with the poll."""
+    monkeypatch.setenv("MOE_CACHE_POLL_US", poll_us)
+    _run(gpu_lib, L=3, E=16, H=512, I=256, S=16, k=4, a=2, b=3, T=12, seed=76, check_every=3)
+
+
 def test_slotcache_loop_fused_b1_path(gpu_lib):
     """H = I = 2048: the batch-1 fused kernels read the arena and the staging."""
     _run(gpu_lib, L=2, E=24, H=2048, I=2048, S=30, k=6, a=2, b=4, T=12, seed=72, check_every=4)
