@@ -489,7 +489,9 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
         seen = true;
         break;
       }
+#if defined(__x86_64__) || defined(__i386__)
       __builtin_ia32_pause();
+#endif
       if ((it & 63) == 63 && std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(c->poll_us)) break;
     }
     if (!seen) {
