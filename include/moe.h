@@ -87,7 +87,8 @@ size_t moe_int2_expert_bytes(int H, int I);
  *                                     ([P2] §Rig, model & methodology: 256 routed experts
  *                                     plus 1 shared per layer), weight 1.0, outside the
  *                                     renormalisation; NULL = no shared expert.
- * Strides must be >= the record size and multiples of 16 bytes; records 16-byte aligned. */
+ * Strides must be >= the record size and multiples of 16 bytes; records 16-byte aligned.
+ * flags: MOE_LAYER_* bits (0 = defaults). */
 typedef struct {
   int H, I;
   const uint8_t* fp4_base;
@@ -97,7 +98,12 @@ typedef struct {
   size_t int2_stride;
   int num_int2;
   const uint8_t* shared;
+  int flags;  /* MOE_LAYER_* bits, 0 for the defaults */
 } moe_layer;
+
+/* moe_layer.flags: batch-1 decode at the single-launch shape (see
+ * moe_layer_decode) runs the whole step as one kernel instead of two. */
+#define MOE_LAYER_SINGLE_LAUNCH 1
 
 /* ---------------------------------------------------------------- routing */
 
@@ -130,8 +136,19 @@ moe_status moe_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int
 /* ------------------------------------------------------------ expert MLP */
 
 /* Workspace bytes moe_expert_forward and moe_layer_decode need for T tokens,
- * top-k, with or without the shared expert. */
+ * top-k, with or without the shared expert.
+ * The last part of the workspace, from moe_expert_workspace_sync_offset(...)
+ * on, holds words that the single-launch batch-1 step keeps from one call to
+ * the next (a completion flag per workgroup carrying a call tag, then an error
+ * word).  Zero the whole workspace once after allocating it; after that the
+ * library keeps those words consistent itself.  Calls that may run at the same
+ * time (on different streams) must use different workspaces.  The error word
+ * (the uint32 at sync offset + 1024) becomes nonzero only if a call's
+ * cross-workgroup wait gave up, which happens only when the device could not
+ * hold every workgroup of the call at once; that call's output is then
+ * invalid. */
 size_t moe_expert_workspace_bytes(int H, int I, int T, int k, int has_shared);
+size_t moe_expert_workspace_sync_offset(int H, int I, int T, int k, int has_shared);
 
 /* SwiGLU expert MLP for every selected (token, rank) and the shared expert:
  *     y = W2 (silu(W1 x) * (W3 x)), dequantised in registers, fp32 accumulation.
@@ -158,8 +175,13 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype x
  * expert GEMM over the slot buffers; [P2] §The number: at batch 1 the layer is
  * a stream of expert bytes).  For bf16 activations and output with H, I in
  * {2048, 4096} and k + has_shared <= 12, the routing runs inside the gate/up
- * kernel, so the whole layer is two launches; otherwise moe_route then
- * moe_expert_forward run.
+ * kernel and the layer is two launches; otherwise moe_route then
+ * moe_expert_forward run.  With MOE_LAYER_SINGLE_LAUNCH in layer->flags, at
+ * H = 4096, I = 2048, k + has_shared <= 9, on a device of at least 256 CUs,
+ * the whole step (routing, gate/up, down and combine) is ONE launch whose
+ * workgroups hand the SwiGLU outputs to each other through the workspace;
+ * moe_expert_forward at T = 1 with prec NULL takes the same single launch
+ * from given ids and weights.  Both give the same results within rounding.
  *   layer: expert e in slot e (num_slots >= E), shared optional, no 2-bit copies
  *   logits [E] fp32, x [1][H] in xt
  *   ids [k] int32 out, w [k] fp32 out (rank order, as moe_route)
@@ -386,6 +408,7 @@ typedef enum {
   MOE_PROF_DEQUANT = 10,
   MOE_PROF_READ = 11,       /* streaming-read reference */
   MOE_PROF_CACHE = 12,      /* slot cache: picks to the host, rewritten ids back */
+  MOE_PROF_FUSED = 13,      /* fused batch-1 step: routing, gate/up, down and combine in one launch */
   MOE_PROF_KINDS = 16
 } moe_prof_kind;
 

@@ -31,8 +31,11 @@ class moe_layer(ctypes.Structure):
         ("H", c_int), ("I", c_int),
         ("fp4_base", c_void_p), ("fp4_stride", c_size_t), ("num_slots", c_int),
         ("int2_base", c_void_p), ("int2_stride", c_size_t), ("num_int2", c_int),
-        ("shared", c_void_p),
+        ("shared", c_void_p), ("flags", c_int),
     ]
+
+
+MOE_LAYER_SINGLE_LAUNCH = 1
 
 
 class moe_cache_desc(ctypes.Structure):
@@ -68,6 +71,7 @@ _SIGS = {
     "moe_route": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "moe_group": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_expert_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+    "moe_expert_workspace_sync_offset": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "moe_expert_forward": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "moe_layer_decode": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_void_p, c_int, c_int, c_void_p,
@@ -160,10 +164,15 @@ def moe_expert_workspace_bytes(H, I, T, k, has_shared) -> int:
     return load().moe_expert_workspace_bytes(H, I, T, k, int(bool(has_shared)))
 
 
+def moe_expert_workspace_sync_offset(H, I, T, k, has_shared) -> int:
+    return load().moe_expert_workspace_sync_offset(H, I, T, k, int(bool(has_shared)))
+
+
 def expert_workspace(H, I, T, k, has_shared, device="cuda"):
-    """A device workspace for moe_expert_forward / moe_layer_decode."""
+    """A device workspace for moe_expert_forward / moe_layer_decode, zeroed
+    (the single-launch batch-1 step keeps call tags in it from call to call)."""
     import torch
-    return torch.empty(moe_expert_workspace_bytes(H, I, T, k, has_shared), dtype=torch.uint8, device=device)
+    return torch.zeros(moe_expert_workspace_bytes(H, I, T, k, has_shared), dtype=torch.uint8, device=device)
 
 
 # -------------------------------------------------------------------- routing
@@ -196,11 +205,12 @@ def moe_group(keys, nkeys, counts, offsets, perm, stream=None):
 # ----------------------------------------------------------------- expert MLP
 
 def make_layer(H, I, fp4_base=None, fp4_stride=0, num_slots=0, int2_base=None, int2_stride=0, num_int2=0,
-               shared=None) -> moe_layer:
+               shared=None, flags=0) -> moe_layer:
     """A moe_layer descriptor from device tensors (uint8 records).  The
     descriptor holds raw device pointers, so it keeps references to the tensors:
     they cannot be freed (and their memory unmapped) while it is alive."""
-    lay = moe_layer(H, I, _p(fp4_base), fp4_stride, num_slots, _p(int2_base), int2_stride, num_int2, _p(shared))
+    lay = moe_layer(H, I, _p(fp4_base), fp4_stride, num_slots, _p(int2_base), int2_stride, num_int2, _p(shared),
+                    flags)
     lay._tensors = (fp4_base, int2_base, shared)
     return lay
 
@@ -400,7 +410,7 @@ class Cache:
 # --------------------------------------------------------------------- timing
 
 PROF_KINDS = ("route", "router_logits", "gateup", "down", "combine", "group", "plan", "quant",
-              "gemm_gateup", "gemm_down", "dequant", "read", "cache")
+              "gemm_gateup", "gemm_down", "dequant", "read", "cache", "fused")
 MOE_PROF_KINDS = 16
 
 

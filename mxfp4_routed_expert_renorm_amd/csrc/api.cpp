@@ -53,6 +53,10 @@ moe_status launch_b1(const moe_layer* L, const float* logits, int E, const void*
 size_t decode_plan_ints(int P);
 bool decode_mfma_ok(int H, int I);
 size_t decode_mfma_plan_ints(int P);
+size_t fused_sync_bytes();
+bool fused_path_ok(const moe_layer* L, int K1, bool xbf16, bool obf16, bool has_prec);
+moe_status launch_fused_b1(const moe_layer* L, const float* logits, int E, const void* x, int k, int32_t* slot_ids,
+                           float* w, uint16_t* h, void* out, uint32_t* sync, hipStream_t s);
 moe_status launch_decode_mfma(const moe_layer* Lr, const void* x, int T, int k, const int32_t* slot_ids, const float* w,
                               void* out, uint16_t* h, float* y, int32_t* plan, hipStream_t s);
 
@@ -109,11 +113,16 @@ moe_status moe_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int
   return launch_group(keys, n, nkeys, counts, offsets, perm, (hipStream_t)stream);
 }
 
-size_t moe_expert_workspace_bytes(int H, int I, int T, int k, int has_shared) {
+size_t moe_expert_workspace_sync_offset(int H, int I, int T, int k, int has_shared) {
   if (H <= 0 || I <= 0 || T < 0 || k <= 0) return 0;
   const size_t P = (size_t)T * (size_t)(k + (has_shared ? 1 : 0));
   return align256(P * I * 4) + align256(P * H * 4) +
          align256(std::max(decode_plan_ints((int)P), decode_mfma_plan_ints((int)P)) * 4);
+}
+
+size_t moe_expert_workspace_bytes(int H, int I, int T, int k, int has_shared) {
+  if (H <= 0 || I <= 0 || T < 0 || k <= 0) return 0;
+  return moe_expert_workspace_sync_offset(H, I, T, k, has_shared) + align256(fused_sync_bytes());
 }
 
 static moe_status check_layer(const moe_layer* L, const char* who) {
@@ -162,6 +171,10 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype x
   int32_t* plan = (int32_t*)(ws + align256(P * layer->I * 4) + align256(P * layer->H * 4));
   float* yout = w ? y : (float*)out;
   hipStream_t s = (hipStream_t)stream;
+  uint32_t* sync = (uint32_t*)(ws + moe_expert_workspace_sync_offset(layer->H, layer->I, T, k, has_shared));
+  if (T == 1 && w && fused_path_ok(layer, K1, xt == MOE_BF16, ot == MOE_BF16, prec != nullptr))
+    return launch_fused_b1(layer, nullptr, 0, x, k, const_cast<int32_t*>(slot_ids), const_cast<float*>(w),
+                           (uint16_t*)h, out, sync, s);
   if (T == 1 && w && b1_path_ok(layer->H, layer->I, K1, xt == MOE_BF16, ot == MOE_BF16))  // reads slot_ids and w only
     return launch_b1(layer, nullptr, 0, x, k, const_cast<int32_t*>(slot_ids), prec, const_cast<float*>(w),
                      (uint16_t*)h, out, s);
@@ -196,6 +209,10 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* logits, int E, 
   REQUIRE(workspace_bytes >= need, MOE_ENOMEM, "moe_layer_decode: workspace %zu bytes < %zu needed", workspace_bytes,
           need);
   hipStream_t s = (hipStream_t)stream;
+  uint32_t* sync = (uint32_t*)((char*)workspace + moe_expert_workspace_sync_offset(layer->H, layer->I, 1, k, has_shared));
+  if (fused_path_ok(layer, k + has_shared, xt == MOE_BF16, ot == MOE_BF16, false) &&
+      b1_route_ok(E, layer->num_slots))
+    return launch_fused_b1(layer, logits, E, x, k, ids, w, (uint16_t*)workspace, out, sync, s);
   if (b1_path_ok(layer->H, layer->I, k + has_shared, xt == MOE_BF16, ot == MOE_BF16) && b1_route_ok(E, layer->num_slots))
     return launch_b1(layer, logits, E, x, k, ids, nullptr, w, (uint16_t*)workspace, out, s);
   st = launch_route(logits, 1, E, k, ids, w, s);

@@ -641,6 +641,7 @@ moe_status moe_cache_layer_buffer(moe_cache* c, int layer, moe_stream_t compute,
   out->int2_stride = 0;
   out->num_int2 = 0;
   out->shared = nullptr;
+  out->flags = 0;
   return MOE_OK;
 }
 
@@ -668,6 +669,7 @@ moe_status moe_cache_layer(const moe_cache* c, moe_layer* out) {
   out->int2_stride = c->int2_bytes;
   out->num_int2 = !int2 ? 0 : c->d.int2_slots > 0 ? c->d.int2_slots : c->d.max_tokens * (c->d.ladder_b - c->d.ladder_a);
   out->shared = nullptr;
+  out->flags = 0;
   return MOE_OK;
 }
 

@@ -29,6 +29,7 @@
 
 #include "common.h"
 #include "route_dev.h"
+#include "b1_dev.h"
 
 
 namespace moe {
@@ -56,70 +57,6 @@ struct B1Args {
   void* out;            // [1][H] bf16
 };
 
-__device__ __forceinline__ float silu_mul_b1(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
-// 32 bf16 activations (16 pairs) of one 32-element chunk
-struct XChunk {
-  uint32_t p[16];
-  __device__ __forceinline__ void load_lds(const uint8_t* lds, size_t elem) {
-    const uint4* src = (const uint4*)(lds + elem * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = src[i];
-      p[4 * i] = v.x, p[4 * i + 1] = v.y, p[4 * i + 2] = v.z, p[4 * i + 3] = v.w;
-    }
-  }
-  __device__ __forceinline__ void load_global(const void* base, size_t elem) {
-    const uint4* src = (const uint4*)((const uint16_t*)base + elem);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = src[i];
-      p[4 * i] = v.x, p[4 * i + 1] = v.y, p[4 * i + 2] = v.z, p[4 * i + 3] = v.w;
-    }
-  }
-  // 32 FP4 codes (16 bytes, element 2j in the low nibble of byte j) . chunk
-  __device__ __forceinline__ float fp4(const uint4 c) const {
-    float a0 = 0.0f, a1 = 0.0f;
-    const uint32_t d[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a0 = dot2_bf16(fp4x2_to_bf16x2<0>(d[i]), p[4 * i + 0], a0);
-      a1 = dot2_bf16(fp4x2_to_bf16x2<1>(d[i]), p[4 * i + 1], a1);
-      a0 = dot2_bf16(fp4x2_to_bf16x2<2>(d[i]), p[4 * i + 2], a0);
-      a1 = dot2_bf16(fp4x2_to_bf16x2<3>(d[i]), p[4 * i + 3], a1);
-    }
-    return a0 + a1;
-  }
-  // acc0/acc1 += 32 FP4 codes . chunk, each code times the block scale
-  // inside the convert (exact: bf16 holds every E2M1 value times any power
-  // of two in range)
-  __device__ __forceinline__ void fp4_acc(const uint4 c, float scale, float& acc0, float& acc1) const {
-    const uint32_t d[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc0 = dot2_bf16(fp4x2_to_bf16x2_scaled<0>(d[i], scale), p[4 * i + 0], acc0);
-      acc1 = dot2_bf16(fp4x2_to_bf16x2_scaled<1>(d[i], scale), p[4 * i + 1], acc1);
-      acc0 = dot2_bf16(fp4x2_to_bf16x2_scaled<2>(d[i], scale), p[4 * i + 2], acc0);
-      acc1 = dot2_bf16(fp4x2_to_bf16x2_scaled<3>(d[i], scale), p[4 * i + 3], acc1);
-    }
-  }
-  // 32 2-bit codes (8 bytes, element 4j+q in bits 2q..2q+1 of byte j) . chunk
-  __device__ __forceinline__ float int2(const uint2 c) const {
-    float a0 = 0.0f, a1 = 0.0f;
-    const uint32_t d[2] = {c.x, c.y};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int q = 0; q < 16; q += 2) {
-        const uint32_t xp = p[8 * i + q / 2];
-        a0 = fmaf((float)((d[i] >> (2 * q)) & 3u) - 1.5f, bf16_lo(xp), a0);
-        a1 = fmaf((float)((d[i] >> (2 * q + 2)) & 3u) - 1.5f, bf16_hi(xp), a1);
-      }
-    }
-    return a0 + a1;
-  }
-};
-
 // record and precision of group g (rank g, or the shared expert at g == k)
 __device__ __forceinline__ const uint8_t* b1_group(const B1Args& a, int g, int* pr) {
   if (g == a.k) {
@@ -138,12 +75,6 @@ __device__ __forceinline__ const uint8_t* b1_group(const B1Args& a, int g, int* 
   }
   *pr = -1;
   return nullptr;
-}
-
-// position of the n-th set bit of m (n < popcount(m)); wave-uniform
-__device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
-  for (int t = 0; t < n; ++t) m &= m - 1;
-  return __builtin_ctzll(m);
 }
 
 // ------------------------------------------------------------------ gate/up
@@ -239,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void gateup_b1_kernel(B1Args a) {
       float g0a = 0.0f, g1a = 0.0f, u0a = 0.0f, u1a = 0.0f;
 #pragma unroll
       for (int q = 0; q < CPL; ++q) {
-        XChunk xq;  // re-read per row: LDS bandwidth is cheaper than 16 registers per chunk
+        B1Chunk xq;  // re-read per row: LDS bandwidth is cheaper than 16 registers per chunk
         xq.load_lds(xs, (size_t)(q * 64 + lane) * 32);
         xq.fp4_acc(sl[u].c1[q], stab[sl[u].s1[q]], g0a, g1a);
         xq.fp4_acc(sl[u].c3[q], stab[sl[u].s3[q]], u0a, u1a);
@@ -276,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void gateup_b1_kernel(B1Args a) {
         const size_t c = (size_t)(q * 64 + lane);
         const uint2 c1 = ld_stream8(rec + L2.w1c + (size_t)row * rowb2 + c * 8);
         const uint2 c3 = ld_stream8(rec + L2.w3c + (size_t)row * rowb2 + c * 8);
-        XChunk xq;
+        B1Chunk xq;
         xq.load_lds(xs, c * 32);
         gs = fmaf(xq.int2(c1), e4m3_to_f32(rec[L2.w1s + (size_t)row * rows4 + c]), gs);
         us = fmaf(xq.int2(c3), e4m3_to_f32(rec[L2.w3s + (size_t)row * rows4 + c]), us);
@@ -361,7 +292,7 @@ __global__ __launch_bounds__(256) void down_combine_b1_kernel(B1Args a) {
     float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
-      XChunk hq;
+      B1Chunk hq;
       hq.load_lds(lds + (size_t)gi[u] * I * 2, (size_t)(q * 64 + lane) * 32);
       if (!HAS2 || pi[u] == 0)
         hq.fp4_acc(sl[u].c[q], stab[sl[u].s[q]], p0, p1);
