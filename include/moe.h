@@ -201,9 +201,16 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* logits, int E, 
 moe_status moe_combine(const float* y, const float* w, const int8_t* prec, int T, int k, int H,
                        int has_shared, void* out, moe_dtype ot, moe_stream_t stream);
 
-/* Dequantise one matrix of a record to fp32 [rows][cols] with the same decode
- * path the expert kernels use (bit-exact check of the formats).
- *   record: device record; prec 0 = MXFP4, 1 = 2-bit; matrix 0 = w1, 1 = w3, 2 = w2. */
+/* Dequantise one matrix of a record to fp32 [rows][cols] with a decode path
+ * of the expert kernels (bit-exact check of the formats).
+ *   record: device record; matrix 0 = w1, 1 = w3, 2 = w2;
+ *   prec (mode) 0 = MXFP4: the FP4 convert at scale 1.0 times the E8M0 scale
+ *     in fp32 (the grouped decode kernels' two factors: they apply the scale
+ *     to each 32-element partial sum);
+ *   1 = 2-bit: (code - 1.5) times the E4M3 scale;
+ *   2 = MXFP4 through the scaled FP4-to-bf16 convert with the E8M0 scale as
+ *     its scale operand, widened to fp32: exactly the decode of the batch-1,
+ *     single-launch and batched-decode (bf16 MFMA) kernels. */
 moe_status moe_debug_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out,
                              moe_stream_t stream);
 
@@ -291,6 +298,8 @@ typedef struct {
   const float* lfu_seed;     /* LFU: host [L*E] initial use counts (e.g. a routing trace's), NULL = zeros */
   int prefetch_slots;        /* R > 0: a staging ring of R more FP4 records at fp4_arena slots num_slots ..
                                 num_slots+R-1 (the arena then holds num_slots+R records) for moe_cache_prefetch */
+  long long poll_us;         /* how long moe_cache_ensure polls for the router's picks before it waits for the
+                                kernel that publishes them, in microseconds: 0 = 2 s; < 0 = never poll */
 } moe_cache_desc;
 
 enum { MOE_CACHE_LRU = 0, MOE_CACHE_LFU = 1 };
@@ -313,7 +322,8 @@ typedef struct {
 moe_status moe_cache_create(const moe_cache_desc* desc, moe_cache** out);
 moe_status moe_cache_destroy(moe_cache* c);
 /* Back to the cold state (empty slots and ring, clock 0, zero stats, LFU counts at their
- * seed).  Waits for prefetch and layer-stream copies that no call has waited for yet. */
+ * seed).  Waits for prefetch and layer-stream copies that no call has waited for yet, and
+ * for the compute stream the cache's calls have used, which a later call may then change. */
 moe_status moe_cache_reset(moe_cache* c);
 
 /* One call of the policy on host arrays, no GPU work: for T tokens of `layer`,

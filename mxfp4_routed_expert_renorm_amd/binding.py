@@ -46,7 +46,7 @@ class moe_cache_desc(ctypes.Structure):
         ("fp4_host", c_void_p), ("int2_host", c_void_p),
         ("fp4_arena", c_void_p), ("int2_staging", c_void_p),
         ("int2_slots", c_int), ("policy", c_int), ("lfu_decay", ctypes.c_double), ("lfu_seed", c_void_p),
-        ("prefetch_slots", c_int),
+        ("prefetch_slots", c_int), ("poll_us", ctypes.c_longlong),
     ]
 
 
@@ -320,16 +320,17 @@ class Cache:
 
     def __init__(self, L, E, H, I, num_slots, k, a, b, max_tokens=1, fp4_host=None, int2_host=None,
                  fp4_arena=None, int2_staging=None, int2_slots=0, policy="lru", lfu_decay=1.0, lfu_seed=None,
-                 prefetch_slots=0):
+                 prefetch_slots=0, poll_us=0):
         """lfu_seed: host float32 array [L*E] of initial use counts (copied), or None.
         prefetch_slots: staging-ring entries after the slots (fp4_arena then holds
-        num_slots + prefetch_slots records)."""
+        num_slots + prefetch_slots records).  poll_us: the host's polling budget for
+        each call's picks (0: the default, < 0: no poll)."""
         import numpy as np
         seed = None if lfu_seed is None else np.ascontiguousarray(lfu_seed, dtype=np.float32).reshape(-1)
         d = moe_cache_desc(L, E, H, I, num_slots, k, a, b, max_tokens, _addr(fp4_host), _addr(int2_host),
                            _addr(fp4_arena), _addr(int2_staging), int2_slots,
                            {"lru": MOE_CACHE_LRU, "lfu": MOE_CACHE_LFU}[policy], lfu_decay,
-                           None if seed is None else seed.ctypes.data, prefetch_slots)
+                           None if seed is None else seed.ctypes.data, prefetch_slots, poll_us)
         h = c_void_p()
         _check("moe_cache_create", load().moe_cache_create(ctypes.byref(d), ctypes.byref(h)))
         self.h, self.L, self.E, self.k = h, L, E, k

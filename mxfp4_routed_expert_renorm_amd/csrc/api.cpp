@@ -273,7 +273,8 @@ moe_status moe_prefill_forward(const moe_layer* layer, const void* x, int T, int
 moe_status moe_debug_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out,
                              moe_stream_t stream) {
   REQUIRE(H > 0 && I > 0 && H % 32 == 0 && I % 32 == 0, MOE_ESHAPE, "moe_debug_dequant: H=%d I=%d", H, I);
-  REQUIRE(prec == 0 || prec == 1, MOE_EINVAL, "moe_debug_dequant: prec=%d", prec);
+  REQUIRE(prec >= 0 && prec <= 2, MOE_EINVAL, "moe_debug_dequant: mode=%d (0 FP4, 1 2-bit, 2 FP4 scaled convert)",
+          prec);
   REQUIRE(matrix >= 0 && matrix <= 2, MOE_EINVAL, "moe_debug_dequant: matrix=%d", matrix);
   REQUIRE(record && out, MOE_EINVAL, "moe_debug_dequant: NULL pointer");
   REQUIRE(aligned(record, 4), MOE_EINVAL, "moe_debug_dequant: record must be 4-byte aligned");

@@ -87,17 +87,34 @@ struct moe_cache {
   // device-side plumbing (created on first ensure)
   void* pin_in = nullptr;   // pinned, mapped: ids [T*k] int32, w [T*k] f32, then the sequence word
   uint32_t seq = 0;         // sequence number of the last call's picks
-  long poll_us = 2000000;   // how long the host polls for them before waiting on the event
+  long long poll_us = 2000000;  // how long the host polls for them before waiting on the event (0: no poll)
   void* pin_out = nullptr;  // pinned, mapped: slots [T*k] int32, w' [T*k] f32, prec [T*k] int8
   void* pin_in_dev = nullptr;   // their device addresses
   void* pin_out_dev = nullptr;
   hipEvent_t ev_read = nullptr, ev_copy = nullptr;
   bool broken = false;
+  // the compute stream of every call since creation or the last reset: the
+  // host rewrites pin_out, victim slots and ring entries as soon as its own
+  // call's kernels are queued, which is safe only behind the previous call's
+  // readers, i.e. on the same stream
+  hipStream_t compute = nullptr;
+  bool compute_set = false;
 };
 
 namespace moe {
 
 namespace {
+
+// every call of a cache uses one compute stream (see moe_cache::compute)
+moe_status check_compute(moe_cache* c, hipStream_t cs, const char* who) {
+  if (c->compute_set && cs != c->compute)
+    return fail(MOE_EINVAL,
+                "%s: the cache's calls use one compute stream (the first call's) until moe_cache_reset; got another",
+                who);
+  c->compute = cs;
+  c->compute_set = true;
+  return MOE_OK;
+}
 
 size_t pin_in_bytes(const moe_cache_desc& d) { return (size_t)d.max_tokens * d.k * 8; }
 constexpr size_t kFlagBytes = 256;  // after the picks in the mapped input buffer: the call's sequence number
@@ -372,7 +389,7 @@ moe_status moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
     return fail(MOE_EINVAL, "moe_cache_create: ladder a < b needs int2_host and int2_staging");
   moe_cache* c = new moe_cache();
   c->d = *d;
-  if (const char* e = std::getenv("MOE_CACHE_POLL_US")) c->poll_us = std::max(0L, std::atol(e));
+  c->poll_us = d->poll_us == 0 ? 2000000 : std::max(0LL, d->poll_us);
   c->fp4_bytes = record_layout(d->H, d->I, 4).bytes;
   c->int2_bytes = record_layout(d->H, d->I, 2).bytes;
   c->map.assign((size_t)d->L * d->E, -1);
@@ -413,6 +430,9 @@ moe_status moe_cache_reset(moe_cache* c) {
   if (c->prefetch_pending) MOE_HIP_CHECK(hipEventSynchronize(c->ev_prefetch));
   for (int b = 0; b < 2; ++b)
     if (c->stream_pending[b]) MOE_HIP_CHECK(hipEventSynchronize(c->ev_stream[b]));
+  // the last call's kernels still read pin_out and the slots: after them, any stream may follow
+  if (c->compute_set && c->d.fp4_arena) MOE_HIP_CHECK(hipStreamSynchronize(c->compute));
+  c->compute_set = false;
   std::fill(c->map.begin(), c->map.end(), -1);
   std::fill(c->owner.begin(), c->owner.end(), -1);
   std::fill(c->stamp.begin(), c->stamp.end(), 0);
@@ -455,6 +475,8 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
   if (!ids_inout || !w_inout || !prec_out) return fail(MOE_EINVAL, "moe_cache_ensure: NULL pointer");
   if (!c->d.fp4_arena) return fail(MOE_EINVAL, "moe_cache_ensure: the cache has no device arena");
   hipStream_t cs = (hipStream_t)compute, ps = copy ? (hipStream_t)copy : cs;
+  s = check_compute(c, cs, "moe_cache_ensure");
+  if (s != MOE_OK) return s;
   const size_t n = (size_t)T * c->d.k;
   if (!c->pin_in) {
     MOE_HIP_CHECK(hipHostMalloc(&c->pin_in, pin_in_bytes(c->d) + kFlagBytes, hipHostMallocMapped));
@@ -470,7 +492,7 @@ moe_status moe_cache_ensure(moe_cache* c, int layer, int T, int32_t* ids_inout, 
   // the one host sync of the call: read the router's picks.  One small
   // kernel writes them into the mapped pinned buffer, then the call's
   // sequence number; the host polls that word.  A poll that has not seen it
-  // within poll_us (2 s unless MOE_CACHE_POLL_US says otherwise; 0: no poll)
+  // within poll_us (2 s unless the descriptor says otherwise; 0: no poll)
   // falls back to waiting for the kernel's completion (which also reports a
   // failed launch).
   {
@@ -587,11 +609,15 @@ moe_status moe_cache_stream_layer(moe_cache* c, int layer, int* buffer, moe_stre
   if (c->d.num_slots < 2 * E)
     return fail(MOE_ECACHE_SMALL, "moe_cache_stream_layer: num_slots=%d is too small: two expert-layer buffers need %d",
                 c->d.num_slots, 2 * E);
+  hipStream_t cs = (hipStream_t)compute, ps = copy ? (hipStream_t)copy : cs;
+  if (c->d.fp4_arena) {
+    const moe_status s = check_compute(c, cs, "moe_cache_stream_layer");
+    if (s != MOE_OK) return s;
+  }
   const int b = plan_stream(c, layer);
   if (buffer) *buffer = b;
   if (!c->d.fp4_arena) return MOE_OK;
   c->broken = true;
-  hipStream_t cs = (hipStream_t)compute, ps = copy ? (hipStream_t)copy : cs;
   for (hipEvent_t* e : {&c->ev_stream[0], &c->ev_stream[1], &c->ev_compute})
     if (!*e) MOE_HIP_CHECK(hipEventCreateWithFlags(e, hipEventDisableTiming));
   if (ps != cs) {  // work already on the compute stream may still read the buffer
@@ -628,6 +654,10 @@ moe_status moe_cache_layer_buffer(moe_cache* c, int layer, moe_stream_t compute,
     if (whole) found = b;
   }
   if (found < 0) return fail(MOE_ESTATE, "moe_cache_layer_buffer: layer %d is not whole in a layer buffer", layer);
+  if (c->d.fp4_arena) {
+    const moe_status s = check_compute(c, (hipStream_t)compute, "moe_cache_layer_buffer");
+    if (s != MOE_OK) return s;
+  }
   if (c->stream_pending[found]) {
     MOE_HIP_CHECK(hipStreamWaitEvent((hipStream_t)compute, c->ev_stream[found], 0));
     c->stream_pending[found] = false;

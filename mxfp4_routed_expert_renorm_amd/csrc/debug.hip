@@ -1,7 +1,13 @@
-// Dequantise one matrix of an expert record to fp32 with the same decode
-// steps the expert kernels use: the gfx950 scaled FP4 convert (scale 1.0)
-// times the E8M0 block scale, or the 2-bit level (code - 1.5) times the E4M3
-// block scale.  Lets the formats be checked bit for bit against the oracle.
+// Dequantise one matrix of an expert record to fp32 with the decode steps the
+// expert kernels use, so the formats can be checked bit for bit against the
+// oracle:
+//   mode 0: the gfx950 FP4 convert at scale 1.0, times the E8M0 block scale in
+//           fp32 (the grouped kernels apply the scale to each 32-element
+//           partial sum, so their factors are these two);
+//   mode 1: the 2-bit level (code - 1.5) times the E4M3 block scale;
+//   mode 2: the scaled FP4 convert to bf16 with the E8M0 block scale as the
+//           convert's own scale operand, widened to fp32: the decode of the
+//           batch-1, single-launch and batched-decode kernels.
 #include <algorithm>
 
 #include "common.h"
@@ -13,7 +19,7 @@ namespace {
 // one thread per 4 code bytes (8 FP4 or 16 two-bit elements)
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales, int rows, int cols,
-                                                      int bits, float* __restrict__ out) {
+                                                      int bits, int scaled, float* __restrict__ out) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   const int per_dw = 32 / bits;  // elements per dword
   const long ndw = (long)rows * cols / per_dw;
@@ -23,7 +29,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const uint32_t dw = ((const uint32_t*)codes)[idx];
   const uint32_t sb = scales[(size_t)r * (cols / 32) + c0 / 32];
   float* o = out + e0;
-  if (bits == 4) {
+  if (bits == 4 && scaled) {
+    const float s = e8m0_to_f32(sb);
+    const uint32_t p0 = fp4x2_to_bf16x2_scaled<0>(dw, s), p1 = fp4x2_to_bf16x2_scaled<1>(dw, s),
+                   p2 = fp4x2_to_bf16x2_scaled<2>(dw, s), p3 = fp4x2_to_bf16x2_scaled<3>(dw, s);
+    o[0] = bf16_lo(p0); o[1] = bf16_hi(p0); o[2] = bf16_lo(p1); o[3] = bf16_hi(p1);
+    o[4] = bf16_lo(p2); o[5] = bf16_hi(p2); o[6] = bf16_lo(p3); o[7] = bf16_hi(p3);
+  } else if (bits == 4) {
     const float s = e8m0_to_f32(sb);
     const v2f a0 = fp4x2_to_f32<0>(dw), a1 = fp4x2_to_f32<1>(dw), a2 = fp4x2_to_f32<2>(dw),
               a3 = fp4x2_to_f32<3>(dw);
@@ -38,13 +50,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 }  // namespace
 
 moe_status launch_dequant(const uint8_t* record, int H, int I, int prec, int matrix, float* out, hipStream_t s) {
-  const int bits = prec == 0 ? 4 : 2;
+  const int bits = prec == 1 ? 2 : 4;
   const RecordLayout L = record_layout(H, I, bits);
   const size_t coff[3] = {L.w1c, L.w3c, L.w2c}, soff[3] = {L.w1s, L.w3s, L.w2s};
   const int rows = matrix == 2 ? H : I, cols = matrix == 2 ? I : H;
   const long ndw = (long)rows * cols / (32 / bits);
   launch(MOE_PROF_DEQUANT, dequant_kernel, dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0, s, record + coff[matrix],
-                     record + soff[matrix], rows, cols, bits, out);
+                     record + soff[matrix], rows, cols, bits, prec == 2 ? 1 : 0, out);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

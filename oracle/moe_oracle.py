@@ -194,10 +194,14 @@ def route(logits: np.ndarray, k: int):
     actually does: the router picks its top_k experts; P2 §Not all six experts
     matter equally: the router emits six weights per token).  Reading: the
     score is a softmax over all E logits; ties in the logit go to the lower
-    expert id; experts are emitted in rank order (weight descending).
+    expert id; experts are emitted in rank order (weight descending).  A NaN
+    logit counts as -inf: it ranks with the -inf logits (ties to the lower
+    id), never above a real one, and its weight is 0 (when every selected
+    logit is -inf the weights are undefined: NaN).
 
     Returns ids int32 [T, k] and weights float64 [T, k]."""
     lg = np.asarray(logits, dtype=np.float64)
+    lg = np.where(np.isnan(lg), -np.inf, lg)
     T, E = lg.shape
     ids = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float64)

@@ -267,3 +267,16 @@ def test_stream_layer_validation():
         assert c.stats()["streamed"] == 16
     finally:
         c.destroy()
+
+
+def test_two_token_call_staging_indices_match_the_hand_worked_trace():
+    """The library's policy on the oracle's hand-worked two-token call (k 4,
+    ladder (1, 3)): staging entries t*(b-a) + (rank-a-1)."""
+    c = B.Cache(1, 8, 4096, 2048, 8, 4, 1, 3, max_tokens=2)
+    try:
+        slots, prec, wo = c.plan(0, np.array([[5, 2, 7, 1], [3, 5, 6, 0]], np.int32),
+                                 np.array([[0.4, 0.3, 0.2, 0.1], [0.5, 0.2, 0.2, 0.1]], np.float32))
+        assert slots.tolist() == [[0, 0, 1, -1], [1, 0, 3, -1]]
+        assert prec.tolist() == [[0, 1, 1, -1], [0, 0, 1, -1]]
+    finally:
+        c.destroy()

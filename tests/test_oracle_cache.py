@@ -314,3 +314,27 @@ def test_stream_layer_hand_worked():
     assert c.owner[:3].tolist() == [-1, -1, -1] and c.stamp[:3].tolist() == [0, 0, 0]
     slot, _, _, cp = c.step(1, np.array([[1, 2]]), w)        # misses take the freed slots 0, 1
     assert slot.tolist() == [[0, 1]] and [d for _, _, _, d in cp] == [0, 1]
+
+
+def test_two_tokens_staging_indices_by_hand():
+    """One call of two tokens with 2-bit ranks, worked by hand: k 4, ladder
+    (a, b) = (1, 3), so each token owns b - a = 2 staging entries and rank r
+    of token t (a < r <= b, not resident) goes to entry t*(b-a) + (r-a-1).
+
+    token 0, ids 5 2 7 1, cold cache: rank 1 (5) misses into slot 0; ranks 2
+    and 3 are not resident, so 2-bit copies into entries 0 and 1; rank 4 (1)
+    is dropped.  token 1, ids 3 5 6 0: the snapshot sees 5 in slot 0; rank 1
+    (3) misses into the lowest empty slot 1; rank 2 (5) hits slot 0; rank 3
+    (6) is a 2-bit copy into entry 1*2 + (3-1-1) = 3; rank 4 (0) is dropped."""
+    c = O.SlotCache(1, 8, 8, 4, 1, 3)
+    ids = np.array([[5, 2, 7, 1], [3, 5, 6, 0]])
+    w = np.array([[0.4, 0.3, 0.2, 0.1], [0.5, 0.2, 0.2, 0.1]])
+    slot, prec, wout, copies = c.step(0, ids, w)
+    assert slot.tolist() == [[0, 0, 1, -1], [1, 0, 3, -1]]
+    assert prec.tolist() == [[0, 1, 1, -1], [0, 0, 1, -1]]
+    assert copies == [("fp4", 0, 5, 0), ("int2", 0, 2, 0), ("int2", 0, 7, 1), ("fp4", 0, 3, 1),
+                      ("int2", 0, 6, 3)]
+    assert np.allclose(wout, [[4 / 9, 3 / 9, 2 / 9, 0.0], [5 / 9, 2 / 9, 2 / 9, 0.0]], rtol=0, atol=1e-15)
+    # stamps: token 0's fetch 1, its two 2-bit uses 2 and 3 (no stamp), token
+    # 1's fetch 4, the hit on slot 0 5
+    assert c.stamp[:2].tolist() == [5, 4] and c.clock == 6

@@ -195,3 +195,28 @@ def test_prefill_forward_error_bound_against_exact_layer():
     err = np.abs(pre - exact)
     assert np.all(err <= bound * (1 + 1e-9))
     assert err.max() > 0                            # h rounding does act
+
+
+def test_prefill_forward_quantises_activations():
+    """The prefill layer sees x only through its MXFP8 image: evaluating it on
+    bf16 activations off the MXFP8 grid gives exactly what it gives on their
+    quantised values, and not what the same products give on x itself."""
+    cfg = W.WORKLOADS["tiny"]
+    H, I, E, k = cfg["H"], cfg["I"], cfg["E"], 2
+    bank = W.fp4_bank(23, 1, E, H, I)
+    x = O.bf16_bits_to_f64(W.bf16_normal(23, (2,), (3, H)))
+    xc, xs = O.quant_mxfp8(x)
+    xq = O.dequant_mxfp8(xc, xs)
+    assert not np.array_equal(xq, x)                # bf16 values off the E4M3 grid
+    ids, w = O.route(W.router_logits(23, (3,), 3, E), k)
+    pre = O.prefill_forward(x, ids, w, lambda e: bank[e], H, I)
+    assert np.array_equal(pre, O.prefill_forward(xq, ids, w, lambda e: bank[e], H, I))
+    # the same products and h rounding on the unquantised x
+    raw = np.zeros_like(pre)
+    for t in range(3):
+        for r in range(k):
+            W1, W3, W2 = O.expert_weights(bank[ids[t, r]], H, I)
+            h = O.silu(W1 @ x[t]) * (W3 @ x[t])
+            hc, hs = O.quant_mxfp8(h[None, :])
+            raw[t] += w[t, r] * (W2 @ O.dequant_mxfp8(hc, hs)[0])
+    assert np.linalg.norm(pre - raw) > 1e-3 * np.linalg.norm(raw)

@@ -94,3 +94,20 @@ def test_group_pairs_bucket_sort():
         assert counts.tolist() == [len(buckets[e]) for e in range(E)]
         assert offsets[0] == 0 and offsets[-1] == T * k
         assert np.all(np.diff(offsets) == counts)
+
+
+def test_route_nan_counts_as_minus_inf():
+    """A NaN logit ranks with the -inf ones (ties by id), below every real
+    logit, and gets weight 0; the weights of the real picks are the softmax
+    over them alone."""
+    nan, ninf = float("nan"), float("-inf")
+    lg = np.array([[1.0, nan, ninf, 0.5, nan, ninf]])
+    ids, w = O.route(lg, 4)
+    assert ids[0].tolist() == [0, 3, 1, 2]
+    z = np.exp(np.array([1.0, 0.5]) - 1.0)
+    assert np.allclose(w[0], [z[0] / z.sum(), z[1] / z.sum(), 0.0, 0.0], rtol=0, atol=1e-15)
+    # the k-th pick at the NaN / -inf boundary: -inf at id 0 beats NaN at id 1
+    ids, w = O.route(np.array([[ninf, nan, ninf, 2.0]]), 2)
+    assert ids[0].tolist() == [3, 0] and w[0].tolist() == [1.0, 0.0]
+    ids, _ = O.route(np.array([[2.0, ninf, nan, ninf]]), 3)
+    assert ids[0].tolist() == [0, 1, 2]

@@ -121,6 +121,13 @@ def test_route_ties_ragged_and_edges(gpu_lib):
     lg = np.full((1, 256), -0.0, np.float32)
     lg[0, ::2] = 0.0                                               # +0 and -0 tie
     cases.append((lg, 5))
+    lg = np.full((3, 256), -np.inf, np.float32)                    # NaN counts as -inf
+    lg[:, 1::3] = np.nan
+    lg[0, [7, 100, 200]] = [1.5, 0.25, 3.0]                        # k-th pick among NaN / -inf
+    lg[1, 5] = 0.0
+    lg[2, :] = rng.standard_normal(256)
+    lg[2, ::5] = np.nan
+    cases.append((lg, 6))
     for lg, k in cases:
         ids, w = _route_gpu(gpu_lib, lg, k)
         oids, ow = O.route(lg, k)
@@ -193,6 +200,30 @@ def test_group_skips_out_of_range_keys(gpu_lib):
     assert np.array_equal(counts.cpu().numpy(), oc)
     assert np.array_equal(offsets.cpu().numpy(), oo)
     assert np.array_equal(perm.cpu().numpy(), pos[op])
+
+
+def test_dequant_fp4_scaled_convert_bit_exact_all_codes_all_scales(gpu_lib):
+    """The decode of the batch-1, single-launch and batched-decode kernels:
+    the scaled FP4-to-bf16 convert with the E8M0 scale as its operand, for
+    every FP4 code times every E8M0 byte, equals the oracle's
+    E2M1 value x 2^(e-127) bit for bit (rounded to float32: past the float
+    range the product is infinite, as in bf16)."""
+    torch = _torch()
+    H, I = 256, 128
+    rec = _exhaustive_fp4_record(H, I)
+    want = O.expert_weights(rec, H, I, 0)
+    d_rec = dev(rec)
+    for m in range(3):
+        rows, cols = (I, H) if m < 2 else (H, I)
+        out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+        gpu_lib.moe_debug_dequant(d_rec, H, I, 2, m, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        ok = _same_bits(got, want[m])
+        if not ok:
+            bad = np.nonzero(got.view(np.uint32) != np.asarray(want[m], np.float64).astype(np.float32).view(np.uint32))
+            log(f"matrix {m}: {len(bad[0])} mismatches, first {[(got[i, j], want[m][i, j]) for i, j in zip(*bad)][:6]}")
+        assert ok, f"matrix {m}"
 
 
 # ------------------------------------------------------------- layer outputs

@@ -14,9 +14,14 @@ from tests.gpu_util import TOL_BF16_MAX_REL, bf16_dev, dev, log, max_rel
 pytestmark = pytest.mark.gpu
 
 
-def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1, recall=None, m=12, **tier):
+def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1, recall=None, m=12, nosync=False,
+         **tier):
     """recall: with tier["prefetch_slots"] > 0, every call first prefetches a
-    prediction of this recall (m experts) for the call two layers ahead."""
+    prediction of this recall (m experts) for the call two layers ahead.
+    nosync: queue the whole loop without synchronising between calls (each
+    call's ids, weights, precisions and output in their own rows of device
+    buffers; prefetches on a third stream), then check every row at the end;
+    the host-side slot map is still compared after every call."""
     import torch
     lib = gpu_lib
     rb4, rb2 = O.fp4_expert_nbytes(H, I), O.int2_expert_nbytes(H, I)
@@ -54,41 +59,62 @@ def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1, recall
     cache = lib.Cache(L, E, H, I, S, k, a, b, 1, fp4_host, int2_host, arena, staging, **tier)
     oc = O.SlotCache(L, E, S, k, a, b, **_oracle_tier(tier))
     copy_stream = torch.cuda.Stream()
+    pf_stream = torch.cuda.Stream() if nosync else copy_stream
     try:
         layer = cache.layer()
         lg_dev = dev(logits.reshape(T * L, E))
-        ids = torch.empty((1, k), dtype=torch.int32, device="cuda")
-        w = torch.empty((1, k), dtype=torch.float32, device="cuda")
-        prec = torch.empty((1, k), dtype=torch.int8, device="cuda")
-        out = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+        nrow = T * L if nosync else 1
+        ids = torch.empty((nrow, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((nrow, k), dtype=torch.float32, device="cuda")
+        prec = torch.empty((nrow, k), dtype=torch.int8, device="cuda")
+        out = torch.empty((nrow, H), dtype=torch.bfloat16, device="cuda")
         ws = lib.expert_workspace(H, I, 1, k, False)
         checked = 0
+        pending = []
+
+        def check(t, l, r, oslots, oprec, owo, oids, xb, got_ids, got_prec, got_w, got_out):
+            nonlocal checked
+            assert np.array_equal(got_ids, oslots), (t, l)
+            assert np.array_equal(got_prec, oprec), (t, l)
+            assert np.max(np.abs(got_w - owo)) <= 1e-6, (t, l)
+            if xb is not None:
+                def rec(e, p, l=l):
+                    q = l * E + int(e)
+                    return (fp4_host.array[q * rb4:(q + 1) * rb4] if p == 0
+                            else int2_host.array[q * rb2:(q + 1) * rb2])
+                ref = O.layer_forward(O.bf16_bits_to_f64(xb), oids, owo, rec, H, I, prec=oprec)
+                err = max_rel(got_out, ref)
+                assert err <= TOL_BF16_MAX_REL, (t, l, err)
+                checked += 1
+
         for t in range(T):
             for l in range(L):
                 row = t * L + l
+                r = row if nosync else 0
                 if (t, l) in pred:
-                    cache.prefetch(*pred[(t, l)], copy=copy_stream)
+                    cache.prefetch(*pred[(t, l)], copy=pf_stream)
                     oc.prefetch(*pred[(t, l)])
-                lib.moe_route(lg_dev[row:row + 1], k, ids, w)
-                cache.ensure(l, 1, ids, w, prec, copy=copy_stream)
+                lib.moe_route(lg_dev[row:row + 1], k, ids[r:r + 1], w[r:r + 1])
+                cache.ensure(l, 1, ids[r:r + 1], w[r:r + 1], prec[r:r + 1], copy=copy_stream)
                 xb = W.slotcache_x(seed, t, l, H)
-                lib.moe_expert_forward(layer, bf16_dev(xb), 1, k, ids, prec, w, out, ws)
+                lib.moe_expert_forward(layer, bf16_dev(xb), 1, k, ids[r:r + 1], prec[r:r + 1], w[r:r + 1],
+                                       out[r:r + 1], ws)
                 oids, ow = routes[(t, l)]
                 oslots, oprec, owo, _ = oc.step(l, oids, ow)
+                assert np.array_equal(cache.slot_map(), oc.slot_map()), (t, l)   # host state
+                xchk = xb if t % check_every == 0 else None
+                if nosync:
+                    pending.append((t, l, r, oslots, oprec, owo, oids, xchk))
+                    continue
                 torch.cuda.synchronize()
-                assert np.array_equal(ids.cpu().numpy(), oslots), (t, l)
-                assert np.array_equal(prec.cpu().numpy(), oprec), (t, l)
-                assert np.max(np.abs(w.cpu().numpy() - owo)) <= 1e-6, (t, l)
-                assert np.array_equal(cache.slot_map(), oc.slot_map()), (t, l)
-                if t % check_every == 0:
-                    def rec(e, p, l=l):
-                        q = l * E + int(e)
-                        return (fp4_host.array[q * rb4:(q + 1) * rb4] if p == 0
-                                else int2_host.array[q * rb2:(q + 1) * rb2])
-                    ref = O.layer_forward(O.bf16_bits_to_f64(xb), oids, owo, rec, H, I, prec=oprec)
-                    err = max_rel(out.float().cpu().numpy(), ref)
-                    assert err <= TOL_BF16_MAX_REL, (t, l, err)
-                    checked += 1
+                check(t, l, r, oslots, oprec, owo, oids, xchk, ids.cpu().numpy(), prec.cpu().numpy(),
+                      w.cpu().numpy(), out.float().cpu().numpy())
+        if nosync:
+            torch.cuda.synchronize()
+            gi, gp, gw, go = ids.cpu().numpy(), prec.cpu().numpy(), w.cpu().numpy(), out.float().cpu().numpy()
+            for (t, l, r, oslots, oprec, owo, oids, xchk) in pending:
+                check(t, l, r, oslots, oprec, owo, oids, xchk, gi[r:r + 1], gp[r:r + 1], gw[r:r + 1],
+                      go[r:r + 1])
         st = cache.stats()
         log(f"  stats {st}; outputs checked: {checked}")
         assert (st["hits"], st["misses"], st["int2_uses"], st["drops"]) == (oc.hits, oc.misses, oc.int2, oc.drops)
@@ -103,6 +129,8 @@ def _run(gpu_lib, L, E, H, I, S, k, a, b, T, seed, check_every, zipf=1.1, recall
 
 
 def _oracle_tier(tier):
+    tier = dict(tier)
+    tier.pop("poll_us", None)
     return {"int2_slots": tier.get("int2_slots", 0), "policy": tier.get("policy", "lru"),
             "decay": tier.get("lfu_decay", 1.0), "seed": tier.get("lfu_seed"), "ring": tier.get("prefetch_slots", 0)}
 
@@ -113,13 +141,12 @@ def test_slotcache_loop_small(gpu_lib):
     assert st["evictions"] > 0
 
 
-@pytest.mark.parametrize("poll_us", ["0", "1"])
-def test_slotcache_loop_event_wait(gpu_lib, monkeypatch, poll_us):
-    """The host's wait for each call's picks without its poll (0: the kernel's
+@pytest.mark.parametrize("poll_us", [-1, 1])
+def test_slotcache_loop_event_wait(gpu_lib, poll_us):
+    """The host's wait for each call's picks without its poll (-1: the kernel's
     completion event only) or with a 1 us poll budget (the poll mostly gives up
     and falls back to the event): slot maps and outputs as with the poll."""
-    monkeypatch.setenv("MOE_CACHE_POLL_US", poll_us)
-    _run(gpu_lib, L=3, E=16, H=512, I=256, S=16, k=4, a=2, b=3, T=12, seed=76, check_every=3)
+    _run(gpu_lib, L=3, E=16, H=512, I=256, S=16, k=4, a=2, b=3, T=12, seed=76, check_every=3, poll_us=poll_us)
 
 
 def test_slotcache_loop_fused_b1_path(gpu_lib):
@@ -128,11 +155,53 @@ def test_slotcache_loop_fused_b1_path(gpu_lib):
 
 
 def test_slotcache_loop_full_size(gpu_lib):
-    """The slot-cache decode workload's shape: 8 layers x 256 experts, H 4096,
-    I 2048, 512 slots, top-6, ladder (2,4); 16 tokens, outputs on every 4th."""
+    """The slot-cache decode workload in full: 8 layers x 256 experts, H 4096,
+    I 2048, 512 slots, top-6, ladder (2,4), all 512 tokens, queued with no
+    synchronisation between calls (as the benchmark runs it); slots,
+    precisions and weights checked at every call, outputs on every 64th token."""
     cfg = W.WORKLOADS["slotcache"]
     _run(gpu_lib, L=cfg["L"], E=cfg["E"], H=cfg["H"], I=cfg["I"], S=cfg["slots"], k=cfg["k"],
-         a=cfg["ladder"][0], b=cfg["ladder"][1], T=16, seed=W.WORKLOADS["slotcache"]["seed"], check_every=4)
+         a=cfg["ladder"][0], b=cfg["ladder"][1], T=cfg["T"], seed=W.WORKLOADS["slotcache"]["seed"],
+         check_every=64, nosync=True)
+
+
+def test_slotcache_loop_no_sync_small(gpu_lib):
+    """The small loop queued without synchronisation, prefetches on a stream
+    of their own: every call's rows checked after one final sync."""
+    st = _run(gpu_lib, L=3, E=16, H=512, I=256, S=16, k=4, a=2, b=3, T=30, seed=77, check_every=3,
+              recall=0.75, m=6, prefetch_slots=8, nosync=True)
+    assert st["ring_hits"] > 0 and st["evictions"] > 0
+
+
+def test_slotcache_one_compute_stream(gpu_lib):
+    """A cache's calls run on one compute stream: a call on another stream is
+    rejected (the host reuses buffers the previous call's kernels may still
+    read); after moe_cache_reset another stream is accepted."""
+    import torch
+    lib = gpu_lib
+    L, E, H, I, S, k = 1, 8, 512, 256, 8, 2
+    rb4 = O.fp4_expert_nbytes(H, I)
+    fp4_host = lib.PinnedBuffer(L * E * rb4)
+    arena = torch.empty(S * rb4, dtype=torch.uint8, device="cuda")
+    cache = lib.Cache(L, E, H, I, S, k, k, k, 1, fp4_host, None, arena, None)
+    try:
+        ids = dev(np.array([[1, 2]], np.int32))
+        w = dev(np.array([[0.6, 0.4]], np.float32))
+        prec = torch.empty((1, k), dtype=torch.int8, device="cuda")
+        cache.ensure(0, 1, ids, w, prec)
+        other = torch.cuda.Stream()
+        with torch.cuda.stream(other):
+            with pytest.raises(lib.MoeError) as ei:
+                cache.ensure(0, 1, ids, w, prec)
+        assert ei.value.status == 1 and "one compute stream" in str(ei.value)
+        cache.reset()
+        with torch.cuda.stream(other):
+            cache.ensure(0, 1, dev(np.array([[3, 4]], np.int32)), w, prec)
+        torch.cuda.synchronize()
+        assert prec.cpu().numpy().tolist() == [[0, 0]]
+    finally:
+        cache.destroy()
+        fp4_host.free()
 
 
 def test_slotcache_loop_int2_tier_lfu(gpu_lib):
