@@ -7,7 +7,11 @@ bytes per FP4 expert): one step = route one token's fp32 logits (top-8,
 renormalised) + the SwiGLU MLP of the 8 selected experts and the shared
 expert on MXFP4 weights + the weighted combine to a bf16 output, issued as one
 moe_layer_decode call (two kernels).  Each step uses fresh seeded logits and
-activations; every expert is resident in HBM.
+activations; every expert is resident in HBM.  The model has many such layers
+(43): the timed steps rotate over --layers resident layers (8 by default,
+27.5 GB), each with its own experts and shared expert, so consecutive steps
+share no weights and none of a step's bytes can come from the 256 MB
+last-level cache; single-layer steady and cold latencies are reported beside.
 
 Prints one JSON line: tokens/s of the whole step, the achieved HBM bandwidth
 of the dominant kernel (gate/up GEMV) against the 8 TB/s peak, and the CPU
@@ -48,6 +52,8 @@ def parse():
                          "slotcache-prefill: 4096-token prompt chunks through the same 8 layers by whole-layer "
                          "streaming into two layer buffers of the cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=8,
+                    help="decode-b1: resident layers the timed steps rotate over (step s runs layer s mod L)")
     ap.add_argument("--tp-share", type=int, default=1,
                     help="decode-b1 on rank 0's share of G-way tensor parallelism (experts cut along I)")
     ap.add_argument("--slot-tier", action="store_true",
@@ -65,7 +71,7 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_hash(files=("decode_b1.hip", "route_dev.h", "common.h")) -> str:
+def kernel_hash(files=("decode_b1.hip", "b1_dev.h", "route_dev.h", "common.h")) -> str:
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "mxfp4_routed_expert_renorm_amd", "csrc", f), "rb") as fh:
@@ -109,12 +115,10 @@ def host_threads() -> int:
     return max(1, min(16, n))
 
 
-def cpu_baseline(min_seconds: float, threads: int = 1):
-    """The oracle as it stands, on whole tokens of the same workload, until at
-    least min_seconds of CPU work; BLAS limited to `threads` threads."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-
+def _oracle_tokens(min_seconds: float, first_step: int, stride: int):
+    """Whole tokens of the batch-1 decode workload through the oracle, until
+    at least min_seconds of timed oracle work; inputs are generated untimed.
+    Returns (tokens, seconds)."""
     from mxfp4_routed_expert_renorm_amd import workloads as W
     from oracle import moe_oracle as O
 
@@ -122,37 +126,60 @@ def cpu_baseline(min_seconds: float, threads: int = 1):
     seed = cfg["seed"]
     H, I, k = cfg["H"], cfg["I"], cfg["k"]
     toks, t_used = 0, 0.0
-    with threadpool_limits(limits=threads):
-        while t_used < min_seconds or toks == 0:
-            d = W.make_layer_inputs(cfg, seed, step=toks, with_bank=False)
-            lg = d["logits"]
-            ids, _ = O.route(lg, k)
-            recs = {int(e): W.fp4_record(seed, W.S_BANK, int(e), H, I) for e in ids[0]}
-            shared = W.fp4_record(seed, W.S_SHARED, 0, H, I)
-            x = O.bf16_bits_to_f64(d["x"])
-            t0 = time.perf_counter()
-            ids, w = O.route(lg, k)
-            out = O.layer_forward(x, ids, w, lambda e: recs[int(e)], H, I, shared_rec=shared)
-            O.round_to_bf16(out)
-            t_used += time.perf_counter() - t0
-            toks += 1
-    return {"value": toks / t_used, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{toks} token(s) of the batch-1 decode workload (route + 9 experts dequantised "
-                      f"and evaluated in float64 + combine), BLAS limited to {threads} thread(s); "
-                      f"input generation excluded; {t_used:.1f} s"}
+    while t_used < min_seconds or toks == 0:
+        d = W.make_layer_inputs(cfg, seed, step=first_step + toks * stride, with_bank=False)
+        lg = d["logits"]
+        ids, _ = O.route(lg, k)
+        recs = {int(e): W.fp4_record(seed, W.S_BANK, int(e), H, I) for e in ids[0]}
+        shared = W.fp4_record(seed, W.S_SHARED, 0, H, I)
+        x = O.bf16_bits_to_f64(d["x"])
+        t0 = time.perf_counter()
+        ids, w = O.route(lg, k)
+        out = O.layer_forward(x, ids, w, lambda e: recs[int(e)], H, I, shared_rec=shared)
+        O.round_to_bf16(out)
+        t_used += time.perf_counter() - t0
+        toks += 1
+    return toks, t_used
 
 
-def step_latency(torch, step, steps, flush_bytes=1 << 30):
+def cpu_baseline(min_seconds: float, threads: int = 1):
+    """The oracle as it stands, on whole tokens of the same workload, BLAS
+    limited to one thread per worker; with threads > 1, that many host threads
+    each run whole tokens at once (NumPy releases the interpreter lock in its
+    array work) and the rates of the threads add up."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        if threads == 1:
+            toks, t_used = _oracle_tokens(min_seconds, 0, 1)
+            return {"value": toks / t_used, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                    "sample": f"{toks} token(s) of the batch-1 decode workload (route + 9 experts dequantised "
+                              f"and evaluated in float64 + combine), one thread; input generation excluded; "
+                              f"{t_used:.1f} s"}
+        with ThreadPoolExecutor(threads) as ex:
+            res = list(ex.map(lambda i: _oracle_tokens(min_seconds, i, threads), range(threads)))
+    value = sum(n / t for n, t in res)
+    ntok = sum(n for n, _ in res)
+    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{ntok} token(s) of the batch-1 decode workload on {threads} threads at once (each thread: "
+                      f"whole tokens, route + 9 experts dequantised and evaluated in float64 + combine, BLAS one "
+                      f"thread); value = the sum of the threads' tokens per second of their own timed work; input "
+                      f"generation excluded; at least {min_seconds:.0f} s per thread"}
+
+
+def step_latency(torch, step, steps, flush_bytes=1 << 30, flush=True):
     """Per-step latency with HIP events on the launch stream, eager: "steady"
-    back to back, and "cold" with an untimed 1 GiB write before every step,
-    which leaves none of the step's weights in the 256 MB MALL."""
+    back to back, and (flush) "cold" with an untimed 1 GiB write before every
+    step, which leaves none of the step's weights in the 256 MB MALL."""
     import numpy as np
-    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(flush_bytes if flush else 1, dtype=torch.uint8, device="cuda")
     out = {}
-    for name, flush in (("steady", False), ("cold", True)):
+    for name, flush_it in (("steady", False), ("cold", True))[:2 if flush else 1]:
         evs = []
         for s in steps:
-            if flush:
+            if flush_it:
                 scratch.fill_(s & 0xff)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -206,16 +233,18 @@ def main():
     return bench_decode_b1(args)
 
 
-def resident_bank(W, lib, torch, cfg, seed, dev):
-    """The layer's 256 FP4 records (slot = expert id) and the shared record, in HBM."""
+def resident_bank(W, lib, torch, cfg, seed, dev, layer=0):
+    """A layer's 256 FP4 records (slot = expert id) and its shared record, in
+    HBM.  Layer l's expert e is record l * E + e of the seeded bank (layer 0 is
+    the workload's own bank), its shared expert record l of the shared stream."""
     E, H, I = cfg["E"], cfg["H"], cfg["I"]
     rec_bytes = lib.moe_fp4_expert_bytes(H, I)
     bank = torch.empty((E, rec_bytes), dtype=torch.uint8, device=dev)
     host = np.empty((16, rec_bytes), np.uint8)
     for e0 in range(0, E, 16):
-        W.fp4_bank(seed, W.S_BANK, 16, H, I, out=host, first_index=e0)
+        W.fp4_bank(seed, W.S_BANK, 16, H, I, out=host, first_index=layer * E + e0)
         bank[e0:e0 + 16].copy_(torch.from_numpy(host))
-    shared = torch.from_numpy(W.fp4_record(seed, W.S_SHARED, 0, H, I)).to(dev)
+    shared = torch.from_numpy(W.fp4_record(seed, W.S_SHARED, layer, H, I)).to(dev)
     return bank, shared, rec_bytes
 
 
@@ -246,19 +275,25 @@ def bench_decode_b1(args):
     rec_bytes = lib.moe_fp4_expert_bytes(H, I)
 
     t0 = time.time()
-    print(f"[bench] generating {E}+1 experts ({(E + 1) * rec_bytes / 1e9:.2f} GB) and {nsteps} steps of inputs",
-          file=sys.stderr, flush=True)
-    bank, shared, rec_bytes = resident_bank(W, lib, torch, cfg, seed, dev)
     G = args.tp_share
-    if G > 1:  # rank 0's slice of every expert: I/G rows of w1, w3 and columns of w2
-        rec_bytes = lib.moe_fp4_expert_bytes(H, I // G)
-        share = torch.empty((E, rec_bytes), dtype=torch.uint8, device=dev)
-        shared_share = torch.empty((1, rec_bytes), dtype=torch.uint8, device=dev)
-        lib.moe_tp_slice(bank, H, I, G, 0, share)
-        lib.moe_tp_slice(shared[None, :], H, I, G, 0, shared_share)
-        torch.cuda.synchronize()
-        del bank
-        bank, shared, I = share, shared_share[0], I // G
+    NL = max(1, args.layers)
+    print(f"[bench] generating {NL} layers of {E}+1 experts ({NL * (E + 1) * rec_bytes / 1e9:.2f} GB) and "
+          f"{nsteps} steps of inputs", file=sys.stderr, flush=True)
+    layers_mem = []
+    for l in range(NL):
+        bank, shared, rec_bytes = resident_bank(W, lib, torch, cfg, seed, dev, layer=l)
+        if G > 1:  # rank 0's slice of every expert: I/G rows of w1, w3 and columns of w2
+            rec_bytes = lib.moe_fp4_expert_bytes(H, I // G)
+            share = torch.empty((E, rec_bytes), dtype=torch.uint8, device=dev)
+            shared_share = torch.empty((1, rec_bytes), dtype=torch.uint8, device=dev)
+            lib.moe_tp_slice(bank, H, I, G, 0, share)
+            lib.moe_tp_slice(shared[None, :], H, I, G, 0, shared_share)
+            torch.cuda.synchronize()
+            del bank
+            bank, shared = share, shared_share[0]
+        layers_mem.append((bank, shared))
+    if G > 1:
+        I = I // G
     xs = np.stack([W.make_layer_inputs(cfg, seed, s, with_bank=False)["x"][0] for s in range(nsteps)])
     lgs = np.stack([W.make_layer_inputs(cfg, seed, s, with_bank=False)["logits"][0] for s in range(nsteps)])
     x_d = torch.from_numpy(xs).to(dev).view(torch.bfloat16)          # [steps, H]
@@ -267,13 +302,16 @@ def bench_decode_b1(args):
     w_d = torch.empty((nsteps, k), dtype=torch.float32, device=dev)
     out_d = torch.empty((nsteps, H), dtype=torch.bfloat16, device=dev)
     ws = lib.expert_workspace(H, I, T, k, True, device=dev)
-    layer = lib.make_layer(H, I, fp4_base=bank, fp4_stride=rec_bytes, num_slots=E, shared=shared)
+    layers = [lib.make_layer(H, I, fp4_base=bk, fp4_stride=rec_bytes, num_slots=E, shared=sh) for bk, sh in layers_mem]
     torch.cuda.synchronize()
     print(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     def step(s):
-        # route + expert MLP + combine of one token: two kernel launches
-        lib.moe_layer_decode(layer, lg_d[s], x_d[s:s + 1], k, ids_d[s], w_d[s], out_d[s:s + 1], ws)
+        # route + expert MLP + combine of one token on layer s mod L: two kernel launches
+        lib.moe_layer_decode(layers[s % NL], lg_d[s], x_d[s:s + 1], k, ids_d[s], w_d[s], out_d[s:s + 1], ws)
+
+    def step_one_layer(s):
+        lib.moe_layer_decode(layers[0], lg_d[s], x_d[s:s + 1], k, ids_d[s], w_d[s], out_d[s:s + 1], ws)
 
     if args.calibrate_copy:
         calibration_copy(torch, dev)
@@ -324,8 +362,10 @@ def bench_decode_b1(args):
         "vs_baseline": None,
         "dtype": "mxfp4-w/bf16-x/f32-acc",
         "data": "synthetic (seeded; fresh logits and activations every step)",
-        "config": {"workload": cfg["name"] + (f"-tp{G}-share0" if G > 1 else ""), "experts": E,
+        "config": {"workload": cfg["name"] + (f"-tp{G}-share0" if G > 1 else "") +
+                   (f"-{NL}layers-rotated" if NL > 1 else ""), "experts": E,
                    "shared_experts": 1, "hidden": H, "expert_intermediate": I, "top_k": k, "tokens_per_step": T,
+                   "layers": NL, "layer_of_step": "s mod layers",
                    "expert_bytes": rec_bytes, "weight_bytes_per_step": step_bytes, "launch": args.mode,
                    "tp_share": G},
         "step_hbm_GBps": round(step_bytes * value / 1e9, 1),
@@ -337,7 +377,9 @@ def bench_decode_b1(args):
                      "kernel_hash": khash},
         "kernel_avg_us": per_kernel,
     }
-    result["step_latency_us"] = step_latency(torch, step, range(Wm, nsteps))
+    result["step_latency_us"] = step_latency(torch, step, range(Wm, nsteps), flush=False)
+    if NL > 1:  # one resident layer: its shared expert and repeats can sit in the last-level cache
+        result["single_layer_step_latency_us"] = step_latency(torch, step_one_layer, range(Wm, nsteps))
     peak_m = measured_read_peak(torch, lib)
     result["hbm_read_peak_measured_GBps"] = peak_m
     result["roofline"]["frac_vs_measured_peak"] = round(achieved / peak_m, 4)

@@ -398,16 +398,12 @@ def prefill_forward(x, ids, w, get_record, H: int, I: int, shared_rec=None, toke
     """Prefill layer with MXFP8 activations: x is quantised per 32 along H, the
     SwiGLU output h per 32 along I, each feeding the FP4-weight products.
     tokens (optional) restricts the evaluation to a subset of token indices.
-    Returns float64 [len(tokens), H]."""
+    Each expert is dequantised once and applied to every (token, rank) pair
+    that selected it (so memory holds one expert at a time); the outputs are
+    then combined per token in rank order.  Returns float64 [len(tokens), H]."""
     x = np.asarray(x, np.float64)
     T, k = ids.shape
-    tokens = range(T) if tokens is None else tokens
-    wcache = {}
-
-    def weights(e):
-        if e not in wcache:
-            wcache[e] = expert_weights(get_record(e), H, I, 0)
-        return wcache[e]
+    tokens = list(range(T)) if tokens is None else list(tokens)
 
     def one(xq, W1, W3, W2):
         g = W1 @ xq
@@ -416,15 +412,26 @@ def prefill_forward(x, ids, w, get_record, H: int, I: int, shared_rec=None, toke
         hc, hs = quant_mxfp8(h[None, :])
         return W2 @ dequant_mxfp8(hc, hs)[0]
 
-    shared_w = expert_weights(shared_rec, H, I, 0) if shared_rec is not None else None
-    rows = []
+    xq = {}
     for t in tokens:
         xc, xs = quant_mxfp8(x[t][None, :])
-        xq = dequant_mxfp8(xc, xs)[0]
-        ys = np.stack([one(xq, *weights(int(ids[t, r]))) for r in range(k)])
-        ysh = one(xq, *shared_w) if shared_w is not None else None
-        rows.append(combine(ys, np.asarray(w[t], np.float64), ysh))
-    return np.stack(rows)
+        xq[t] = dequant_mxfp8(xc, xs)[0]
+    ys = np.zeros((len(tokens), k, H))
+    pairs = {}
+    for j, t in enumerate(tokens):
+        for r in range(k):
+            pairs.setdefault(int(ids[t, r]), []).append((j, r))
+    for e in sorted(pairs):
+        We = expert_weights(get_record(e), H, I, 0)
+        for j, r in pairs[e]:
+            ys[j, r] = one(xq[tokens[j]], *We)
+        del We
+    ysh = None
+    if shared_rec is not None:
+        Ws = expert_weights(shared_rec, H, I, 0)
+        ysh = np.stack([one(xq[t], *Ws) for t in tokens])
+    return np.stack([combine(ys[j], np.asarray(w[t], np.float64), None if ysh is None else ysh[j])
+                     for j, t in enumerate(tokens)])
 
 
 # ============================================================================

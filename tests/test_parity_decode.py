@@ -626,7 +626,7 @@ def test_batched_bf16_mfma_path(gpu_lib, T, E, k, with_shared, bad, I):
 def test_layer_decode_b64_full_size(gpu_lib):
     """The batch-64 decode shape (256 experts + shared, H 4096, I 2048, top-6,
     Zipf-skewed routing) in the launch configuration the benchmark times;
-    outputs compared on a seeded sample of tokens."""
+    every token's output compared."""
     torch = _torch()
     cfg = W.WORKLOADS["decode-b64"]
     seed = W.WORKLOADS["decode-b64"]["seed"]
@@ -644,10 +644,18 @@ def test_layer_decode_b64_full_size(gpu_lib):
     assert np.array_equal(ids.cpu().numpy(), oids)
     x64 = O.bf16_bits_to_f64(d["x"])
     got = to_f64(out)
-    rng = np.random.default_rng(44)
-    for t in sorted(rng.choice(T, 3, replace=False).tolist()):
-        ys = [O.expert_mlp(x64[t], *O.expert_weights(bank[int(e)], H, I)) for e in oids[t]]
-        ref = O.combine(np.stack(ys), ow[t], O.expert_mlp(x64[t], *O.expert_weights(shared, H, I)))
+    # every token; each distinct expert dequantised once, its (token, rank)
+    # pairs evaluated together
+    ys = np.zeros((T, k, H))
+    for e in np.unique(oids):
+        We = O.expert_weights(bank[int(e)], H, I)
+        for t, r in zip(*np.nonzero(oids == e)):
+            ys[t, r] = O.expert_mlp(x64[t], *We)
+    Ws = O.expert_weights(shared, H, I)
+    worst = 0.0
+    for t in range(T):
+        ref = O.combine(ys[t], ow[t], O.expert_mlp(x64[t], *Ws))
         err = max_rel(got[t], ref)
-        log(f"b64 token {t}: max-rel {err:.3e}")
-        assert err <= TOL_BF16_MAX_REL
+        worst = max(worst, err)
+        assert err <= TOL_BF16_MAX_REL, (t, err)
+    log(f"b64: {len(np.unique(oids))} distinct experts, worst token max-rel {worst:.3e} over {T} tokens")
