@@ -192,6 +192,25 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* logits, int E, 
                             int k, int32_t* ids, float* w, void* out, moe_dtype ot, void* workspace,
                             size_t workspace_bytes, moe_stream_t stream);
 
+/* moe_layer_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace is a static array inside the library, one per device, kept until
+ * the process ends (4 MiB: the first 4 KiB hold the words the single launch
+ * keeps between calls, the rest, moe_noalloc_scratch_bytes(), the per-call
+ * workspace).  Arguments, results and errors are those of moe_layer_decode;
+ * in addition:
+ *   - MOE_ENOMEM when moe_expert_workspace_sync_offset(H, I, 1, k, has_shared)
+ *     exceeds moe_noalloc_scratch_bytes();
+ *   - the first call on a device clears its array with a kernel on `stream`,
+ *     so that call must not be made under stream capture (MOE_EINVAL if it is);
+ *     later calls may be captured;
+ *   - every call on a device shares that device's array: calls that may
+ *     overlap on one device (different streams, no ordering between them) race
+ *     and give wrong results.  Nothing is allocated or freed by any call. */
+moe_status moe_layer_decode_noalloc(const moe_layer* layer, const float* logits, int E, const void* x, moe_dtype xt,
+                                    int k, int32_t* ids, float* w, void* out, moe_dtype ot, moe_stream_t stream);
+size_t moe_noalloc_scratch_bytes(void);
+
 /* Weighted combine ([P1] §What the expert cache actually does: the expert GEMM
  * takes topk_weights; [P2] §Not all six experts matter equally: survivors
  * renormalised):  out[t] = sum_{r < k, prec[t][r] >= 0} w[t][r] * y[t][r]
@@ -419,6 +438,7 @@ typedef enum {
   MOE_PROF_READ = 11,       /* streaming-read reference */
   MOE_PROF_CACHE = 12,      /* slot cache: picks to the host, rewritten ids back */
   MOE_PROF_FUSED = 13,      /* fused batch-1 step: routing, gate/up, down and combine in one launch */
+  MOE_PROF_SCRATCH = 14,    /* one-time clear of the static scratch (moe_layer_decode_noalloc) */
   MOE_PROF_KINDS = 16
 } moe_prof_kind;
 

@@ -76,6 +76,9 @@ _SIGS = {
                                    c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "moe_layer_decode": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_void_p, c_int, c_int, c_void_p,
                                  c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
+    "moe_layer_decode_noalloc": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_void_p, c_int, c_int,
+                                         c_void_p, c_void_p, c_void_p, c_int, c_void_p]),
+    "moe_noalloc_scratch_bytes": (c_size_t, []),
     "moe_combine": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p]),
     "moe_debug_dequant": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
     "moe_debug_stream_read": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
@@ -168,6 +171,10 @@ def moe_expert_workspace_sync_offset(H, I, T, k, has_shared) -> int:
     return load().moe_expert_workspace_sync_offset(H, I, T, k, int(bool(has_shared)))
 
 
+def moe_noalloc_scratch_bytes() -> int:
+    return load().moe_noalloc_scratch_bytes()
+
+
 def expert_workspace(H, I, T, k, has_shared, device="cuda"):
     """A device workspace for moe_expert_forward / moe_layer_decode, zeroed
     (the single-launch batch-1 step keeps call tags in it from call to call)."""
@@ -231,6 +238,16 @@ def moe_layer_decode(layer: moe_layer, logits, x, k, ids, w, out, workspace, str
                                  _dt(out), _p(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream))
     _check("moe_layer_decode", st)
+    return out
+
+
+def moe_layer_decode_noalloc(layer: moe_layer, logits, x, k, ids, w, out, stream=None):
+    """moe_layer_decode with the library's static per-device scratch as its
+    workspace (no allocation in the call)."""
+    E = logits.shape[-1]
+    st = load().moe_layer_decode_noalloc(ctypes.byref(layer), _p(logits), E, _p(x), _dt(x), k, _p(ids), _p(w),
+                                         _p(out), _dt(out), _stream(stream))
+    _check("moe_layer_decode_noalloc", st)
     return out
 
 
@@ -411,7 +428,7 @@ class Cache:
 # --------------------------------------------------------------------- timing
 
 PROF_KINDS = ("route", "router_logits", "gateup", "down", "combine", "group", "plan", "quant",
-              "gemm_gateup", "gemm_down", "dequant", "read", "cache", "fused")
+              "gemm_gateup", "gemm_down", "dequant", "read", "cache", "fused", "scratch")
 MOE_PROF_KINDS = 16
 
 

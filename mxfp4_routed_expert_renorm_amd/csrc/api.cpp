@@ -142,9 +142,16 @@ static moe_status check_layer(const moe_layer* L, const char* who) {
   return MOE_OK;
 }
 
-moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype xt, int T, int k,
-                              const int32_t* slot_ids, const int8_t* prec, const float* w, void* out, moe_dtype ot,
-                              void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+}  // extern "C"
+
+namespace moe {
+
+// The expert MLP of moe_expert_forward.  sync: the words the single launch
+// keeps between calls; NULL puts them at the end of the workspace (the public
+// entry point's layout), and then the workspace must cover them too.
+moe_status expert_forward_impl(const moe_layer* layer, const void* x, moe_dtype xt, int T, int k,
+                               const int32_t* slot_ids, const int8_t* prec, const float* w, void* out, moe_dtype ot,
+                               void* workspace, size_t workspace_bytes, uint32_t* sync, hipStream_t s) {
   moe_status st = check_layer(layer, "moe_expert_forward");
   if (st != MOE_OK) return st;
   REQUIRE(T >= 0 && T <= 65536, MOE_ESHAPE, "moe_expert_forward: T=%d outside 0..65536", T);
@@ -157,7 +164,8 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype x
   REQUIRE(aligned(x, 16) && aligned(out, 16) && aligned(workspace, 256), MOE_EINVAL,
           "moe_expert_forward: x/out must be 16-byte and workspace 256-byte aligned");
   const int has_shared = layer->shared ? 1 : 0;
-  const size_t need = moe_expert_workspace_bytes(layer->H, layer->I, T, k, has_shared);
+  const size_t need = sync ? moe_expert_workspace_sync_offset(layer->H, layer->I, T, k, has_shared)
+                           : moe_expert_workspace_bytes(layer->H, layer->I, T, k, has_shared);
   REQUIRE(workspace_bytes >= need, MOE_ENOMEM, "moe_expert_forward: workspace %zu bytes < %zu needed",
           workspace_bytes, need);
   const int nkeys = layer->num_slots + (layer->int2_base ? layer->num_int2 : 0) + 1;
@@ -170,8 +178,7 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype x
   float* y = (float*)(ws + align256(P * layer->I * 4));
   int32_t* plan = (int32_t*)(ws + align256(P * layer->I * 4) + align256(P * layer->H * 4));
   float* yout = w ? y : (float*)out;
-  hipStream_t s = (hipStream_t)stream;
-  uint32_t* sync = (uint32_t*)(ws + moe_expert_workspace_sync_offset(layer->H, layer->I, T, k, has_shared));
+  if (!sync) sync = (uint32_t*)(ws + moe_expert_workspace_sync_offset(layer->H, layer->I, T, k, has_shared));
   if (T == 1 && w && fused_path_ok(layer, K1, xt == MOE_BF16, ot == MOE_BF16, prec != nullptr))
     return launch_fused_b1(layer, nullptr, 0, x, k, const_cast<int32_t*>(slot_ids), const_cast<float*>(w),
                            (uint16_t*)h, out, sync, s);
@@ -188,9 +195,10 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype x
   return MOE_OK;
 }
 
-moe_status moe_layer_decode(const moe_layer* layer, const float* logits, int E, const void* x, moe_dtype xt, int k,
-                            int32_t* ids, float* w, void* out, moe_dtype ot, void* workspace, size_t workspace_bytes,
-                            moe_stream_t stream) {
+// moe_layer_decode with the same sync convention as expert_forward_impl.
+moe_status layer_decode_impl(const moe_layer* layer, const float* logits, int E, const void* x, moe_dtype xt, int k,
+                             int32_t* ids, float* w, void* out, moe_dtype ot, void* workspace, size_t workspace_bytes,
+                             uint32_t* sync, hipStream_t s) {
   moe_status st = check_layer(layer, "moe_layer_decode");
   if (st != MOE_OK) return st;
   REQUIRE(E >= 1 && E <= 1024, MOE_ESHAPE, "moe_layer_decode: E=%d outside 1..1024", E);
@@ -205,11 +213,12 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* logits, int E, 
   REQUIRE(aligned(x, 16) && aligned(out, 16) && aligned(workspace, 256), MOE_EINVAL,
           "moe_layer_decode: x/out must be 16-byte and workspace 256-byte aligned");
   const int has_shared = layer->shared ? 1 : 0;
-  const size_t need = moe_expert_workspace_bytes(layer->H, layer->I, 1, k, has_shared);
+  const size_t need = sync ? moe_expert_workspace_sync_offset(layer->H, layer->I, 1, k, has_shared)
+                           : moe_expert_workspace_bytes(layer->H, layer->I, 1, k, has_shared);
   REQUIRE(workspace_bytes >= need, MOE_ENOMEM, "moe_layer_decode: workspace %zu bytes < %zu needed", workspace_bytes,
           need);
-  hipStream_t s = (hipStream_t)stream;
-  uint32_t* sync = (uint32_t*)((char*)workspace + moe_expert_workspace_sync_offset(layer->H, layer->I, 1, k, has_shared));
+  if (!sync)
+    sync = (uint32_t*)((char*)workspace + moe_expert_workspace_sync_offset(layer->H, layer->I, 1, k, has_shared));
   if (fused_path_ok(layer, k + has_shared, xt == MOE_BF16, ot == MOE_BF16, false) &&
       b1_route_ok(E, layer->num_slots))
     return launch_fused_b1(layer, logits, E, x, k, ids, w, (uint16_t*)workspace, out, sync, s);
@@ -217,7 +226,25 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* logits, int E, 
     return launch_b1(layer, logits, E, x, k, ids, nullptr, w, (uint16_t*)workspace, out, s);
   st = launch_route(logits, 1, E, k, ids, w, s);
   if (st != MOE_OK) return st;
-  return moe_expert_forward(layer, x, xt, 1, k, ids, nullptr, w, out, ot, workspace, workspace_bytes, stream);
+  return expert_forward_impl(layer, x, xt, 1, k, ids, nullptr, w, out, ot, workspace, workspace_bytes, sync, s);
+}
+
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype xt, int T, int k,
+                              const int32_t* slot_ids, const int8_t* prec, const float* w, void* out, moe_dtype ot,
+                              void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  return expert_forward_impl(layer, x, xt, T, k, slot_ids, prec, w, out, ot, workspace, workspace_bytes, nullptr,
+                             (hipStream_t)stream);
+}
+
+moe_status moe_layer_decode(const moe_layer* layer, const float* logits, int E, const void* x, moe_dtype xt, int k,
+                            int32_t* ids, float* w, void* out, moe_dtype ot, void* workspace, size_t workspace_bytes,
+                            moe_stream_t stream) {
+  return layer_decode_impl(layer, logits, E, x, xt, k, ids, w, out, ot, workspace, workspace_bytes, nullptr,
+                           (hipStream_t)stream);
 }
 
 moe_status moe_combine(const float* y, const float* w, const int8_t* prec, int T, int k, int H, int has_shared,
