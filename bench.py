@@ -339,10 +339,10 @@ def bench_decode_b1(args):
     print(f"[bench] kernel averages (us): {per_kernel}", file=sys.stderr, flush=True)
     ms, n = prof["gateup"]      # the dominant kernel of the two launches
     dom_kernel = ("gateup_b1_kernel (routing + batch-1 gate/up GEMV + SwiGLU)" if G == 1 else
-                  f"gate/up GEMV of the generic path on a 1/{G} share (I = {I})")
+                  f"gateup_b1s_kernel (routing + batch-1 gate/up GEMV + SwiGLU of a 1/{G} share, I = {I})")
+    # the 9 experts' w1 and w3 codes and scales, the logits row, the activation
+    # row, the bf16 SwiGLU outputs written
     dom_bytes = k1 * 2 * (H * I // 2 + H * I // 32) + E * 4 + H * 2 + k1 * I * 2
-    if G > 1:  # the generic gate/up reads ids (not logits) and writes fp32 h
-        dom_bytes = k1 * 2 * (H * I // 2 + H * I // 32) + k * 4 + H * 2 + k1 * I * 4
     dom_avg_s = ms / n / 1e3
     achieved = dom_bytes / dom_avg_s / 1e9
 

@@ -175,8 +175,9 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype x
  * expert GEMM over the slot buffers; [P2] §The number: at batch 1 the layer is
  * a stream of expert bytes).  For bf16 activations and output with H, I in
  * {2048, 4096} and k + has_shared <= 12, the routing runs inside the gate/up
- * kernel and the layer is two launches; otherwise moe_route then
- * moe_expert_forward run.  With MOE_LAYER_SINGLE_LAUNCH in layer->flags, at
+ * kernel and the layer is two launches; the same holds for the narrow experts
+ * of a tensor-parallel share (H in {2048, 4096}, I in {256, 512, 1024}, k +
+ * has_shared <= 12); otherwise moe_route then moe_expert_forward run.  With MOE_LAYER_SINGLE_LAUNCH in layer->flags, at
  * H = 4096, I = 2048, k + has_shared <= 9, on a device of at least 256 CUs,
  * the whole step (routing, gate/up, down and combine) is ONE launch whose
  * workgroups hand the SwiGLU outputs to each other through the workspace;

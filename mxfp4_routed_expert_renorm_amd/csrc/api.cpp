@@ -48,6 +48,10 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
                           void* out, void* workspace, hipStream_t s);
 bool b1_path_ok(int H, int I, int K1, bool xbf16, bool obf16);
 bool b1_route_ok(int E, int num_slots);
+bool b1s_path_ok(int H, int I, int K1, bool xbf16, bool obf16, bool has_prec);
+bool b1s_route_ok(int E, int num_slots);
+moe_status launch_b1s(const moe_layer* L, const float* logits, int E, const void* x, int k, int32_t* slot_ids,
+                      float* w, uint16_t* h, void* out, hipStream_t s);
 moe_status launch_b1(const moe_layer* L, const float* logits, int E, const void* x, int k, int32_t* slot_ids,
                      const int8_t* prec, float* w, uint16_t* h, void* out, hipStream_t s);
 size_t decode_plan_ints(int P);
@@ -185,6 +189,9 @@ moe_status expert_forward_impl(const moe_layer* layer, const void* x, moe_dtype 
   if (T == 1 && w && b1_path_ok(layer->H, layer->I, K1, xt == MOE_BF16, ot == MOE_BF16))  // reads slot_ids and w only
     return launch_b1(layer, nullptr, 0, x, k, const_cast<int32_t*>(slot_ids), prec, const_cast<float*>(w),
                      (uint16_t*)h, out, s);
+  if (T == 1 && w && b1s_path_ok(layer->H, layer->I, K1, xt == MOE_BF16, ot == MOE_BF16, prec != nullptr))
+    return launch_b1s(layer, nullptr, 0, x, k, const_cast<int32_t*>(slot_ids), const_cast<float*>(w), (uint16_t*)h,
+                      out, s);
   // batches of bf16 tokens, all FP4, weighted output: bf16 MFMA on weights dequantised in registers
   if (T >= 2 && w && !prec && xt == MOE_BF16 && ot == MOE_BF16 && decode_mfma_ok(layer->H, layer->I) &&
       P * (size_t)layer->I * 2 < ((size_t)1 << 31) && (size_t)T * layer->H * 2 < ((size_t)1 << 31))
@@ -224,6 +231,9 @@ moe_status layer_decode_impl(const moe_layer* layer, const float* logits, int E,
     return launch_fused_b1(layer, logits, E, x, k, ids, w, (uint16_t*)workspace, out, sync, s);
   if (b1_path_ok(layer->H, layer->I, k + has_shared, xt == MOE_BF16, ot == MOE_BF16) && b1_route_ok(E, layer->num_slots))
     return launch_b1(layer, logits, E, x, k, ids, nullptr, w, (uint16_t*)workspace, out, s);
+  if (b1s_path_ok(layer->H, layer->I, k + has_shared, xt == MOE_BF16, ot == MOE_BF16, false) &&
+      b1s_route_ok(E, layer->num_slots))
+    return launch_b1s(layer, logits, E, x, k, ids, w, (uint16_t*)workspace, out, s);
   st = launch_route(logits, 1, E, k, ids, w, s);
   if (st != MOE_OK) return st;
   return expert_forward_impl(layer, x, xt, 1, k, ids, nullptr, w, out, ot, workspace, workspace_bytes, sync, s);

@@ -71,3 +71,118 @@ def test_tp_partial_outputs_sum_to_the_layer(gpu_lib, T, G):
     ref = np.stack([O.layer_forward(x[t].astype(np.float64)[None, :], ids[t:t + 1], w[t:t + 1],
                                     lambda e: bank[int(e)], H, I, shared_rec=shared)[0] for t in range(T)])
     assert rel_l2(full, ref) <= TOL_F32_REL_L2
+
+
+# ---------------------------------------------------------------- model width
+# One GPU's share at the decode workload's width (H 4096, I 2048 split G ways:
+# 256, 512 or 1024 rows per share), run by the batch-1 step the benchmark
+# times: routing inside the gate/up launch, then down + combine.
+
+_WIDE = {}
+
+
+def _wide_bank():
+    """24 experts + shared at H 4096, I 2048 (host records and their oracle
+    weights, dequantised once)."""
+    if not _WIDE:
+        H, I, E = 4096, 2048, 24
+        _WIDE["bank"] = W.fp4_bank(71, 1, E, H, I)
+        _WIDE["shared"] = W.fp4_record(71, 2, 0, H, I)
+        _WIDE["w"] = {}
+    return _WIDE
+
+
+def _wide_weights(key):
+    st = _wide_bank()
+    if key not in st["w"]:
+        rec = st["shared"] if key < 0 else st["bank"][key]
+        st["w"][key] = O.expert_weights(rec, 4096, 2048)
+    return st["w"][key]
+
+
+def _share_ref(x64, ids, w, G, g, with_shared=True):
+    """The oracle's partial layer output of share g: every selected expert's
+    SwiGLU over rows [g I/G, (g+1) I/G) of w1 and w3 and the same columns of
+    w2, combined with the routing weights (dropped ranks: id outside the bank)."""
+    Is = 2048 // G
+    band = slice(g * Is, (g + 1) * Is)
+
+    def mlp(key):
+        W1, W3, W2 = _wide_weights(key)
+        return O.expert_mlp(x64, W1[band], W3[band], W2[:, band])
+
+    ys = np.stack([mlp(int(e)) if 0 <= e < 24 else np.zeros(4096) for e in ids])
+    return O.combine(ys, np.where((ids >= 0) & (ids < 24), w, 0.0), mlp(-1) if with_shared else None)
+
+
+@pytest.mark.parametrize("G,g", [(8, 0), (8, 7), (4, 2), (2, 1)])
+def test_tp_share_decode_at_model_width(gpu_lib, G, g):
+    """moe_layer_decode on share g of G: ids and weights equal the oracle's
+    routing, the output the oracle's partial sum over the share's bands."""
+    import torch
+    from tests.gpu_util import TOL_BF16_MAX_REL, bf16_dev, max_rel, to_f64
+    st = _wide_bank()
+    H, I, E, k = 4096, 2048, 24, 8
+    bank_d, shared_d = dev(st["bank"]), dev(st["shared"][None, :])
+    sb, ss = _share_bank(gpu_lib, bank_d, H, I, G, g), _share_bank(gpu_lib, shared_d, H, I, G, g)
+    Is = I // G
+    layer = gpu_lib.make_layer(H, Is, fp4_base=sb, fp4_stride=sb.shape[1], num_slots=E, shared=ss[0])
+    ws = gpu_lib.expert_workspace(H, Is, 1, k, True)
+    ntok = 3
+    xs = W.bf16_normal(72, (G, g), (ntok, H))
+    lg = W.router_logits(72, (G, g, 1), ntok, E)
+    lg_d, x_d = dev(lg), bf16_dev(xs)
+    ids = torch.full((ntok, k), -3, dtype=torch.int32, device="cuda")
+    w = torch.full((ntok, k), -3.0, dtype=torch.float32, device="cuda")
+    out = torch.empty((ntok, H), dtype=torch.bfloat16, device="cuda")
+    log(f"TP share {g}/{G} (I = {Is}) at H 4096: {ntok} tokens back to back")
+    for t in range(ntok):
+        gpu_lib.moe_layer_decode(layer, lg_d[t], x_d[t:t + 1], k, ids[t], w[t], out[t:t + 1], ws)
+    torch.cuda.synchronize()
+    oids, ow = O.route(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.max(np.abs(w.cpu().numpy() - ow)) <= 1e-6
+    got = to_f64(out)
+    for t in range(ntok):
+        ref = _share_ref(O.bf16_bits_to_f64(xs[t:t + 1])[0], oids[t], ow[t], G, g)
+        err = max_rel(got[t], ref)
+        log(f"  token {t}: max-rel {err:.3e}")
+        assert err <= TOL_BF16_MAX_REL, (t, err)
+
+
+@pytest.mark.parametrize("with_shared", [True, False])
+def test_tp_share_given_ids_and_the_shares_sum_to_the_layer(gpu_lib, with_shared):
+    """moe_expert_forward at T = 1 on every share of an 8-way split, from given
+    ids with dropped ranks: each share matches the oracle's partial output,
+    and the eight partials add up to the oracle's full layer."""
+    import torch
+    from tests.gpu_util import TOL_BF16_MAX_REL, bf16_dev, max_rel, to_f64
+    st = _wide_bank()
+    H, I, E, k, G = 4096, 2048, 24, 8, 8
+    bank_d, shared_d = dev(st["bank"]), dev(st["shared"][None, :])
+    ids = np.array([[5, 23, -1, 0, 17, 24, 9, 2]], np.int32)
+    wts = np.random.default_rng(73).random((1, k)).astype(np.float32)
+    xs = W.bf16_normal(73, (1,), (1, H))
+    x64 = O.bf16_bits_to_f64(xs)[0]
+    total = np.zeros(H)
+    for g in range(G):
+        sb, ss = _share_bank(gpu_lib, bank_d, H, I, G, g), _share_bank(gpu_lib, shared_d, H, I, G, g)
+        layer = gpu_lib.make_layer(H, I // G, fp4_base=sb, fp4_stride=sb.shape[1], num_slots=E,
+                                   shared=ss[0] if with_shared else None)
+        ws = gpu_lib.expert_workspace(H, I // G, 1, k, with_shared)
+        out = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+        gpu_lib.moe_expert_forward(layer, bf16_dev(xs), 1, k, dev(ids), None, dev(wts), out, ws)
+        torch.cuda.synchronize()
+        got = to_f64(out)[0]
+        ref = _share_ref(x64, ids[0], wts[0].astype(np.float64), G, g, with_shared)
+        err = max_rel(got, ref)
+        log(f"share {g}/8 shared={with_shared}: max-rel {err:.3e}")
+        assert err <= TOL_BF16_MAX_REL, (g, err)
+        total += got
+    full = O.combine(np.stack([O.expert_mlp(x64, *_wide_weights(int(e))) if 0 <= e < 24 else np.zeros(H)
+                               for e in ids[0]]),
+                     np.where((ids[0] >= 0) & (ids[0] < 24), wts[0].astype(np.float64), 0.0),
+                     O.expert_mlp(x64, *_wide_weights(-1)) if with_shared else None)
+    err = max_rel(total, full)
+    log(f"sum of the 8 shares vs the full layer: max-rel {err:.3e}")
+    assert err <= TOL_BF16_MAX_REL
