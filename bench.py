@@ -660,6 +660,15 @@ def bench_slotcache(args):
     print(f"[bench] setup {time.time() - t0:.1f} s; pinned copy rate {h2d_peak:.1f} GB/s",
           file=sys.stderr, flush=True)
 
+    # token-to-token repeat rate of the trace's routing (the share of a token's
+    # top-k, per layer, that the previous token also picked), from the
+    # library's routing of every row before the timed loop
+    rids_d = torch.empty((T * L, k), dtype=torch.int32, device=dev)
+    rw_d = torch.empty((T * L, k), dtype=torch.float32, device=dev)
+    lib.moe_route(lg_d, k, rids_d, rw_d)
+    rids = rids_d.cpu().numpy().reshape(T, L, k)
+    repeat = float(np.mean([len(set(rids[t, l]) & set(rids[t - 1, l])) / k
+                            for t in range(1, T) for l in range(L)]))
     cache = lib.Cache(L, E, H, I, S, k, a, b, 1, fp4_host, int2_host, arena, staging, prefetch_slots=R, **tier)
     layer = cache.layer()
     t_tok = []
@@ -698,6 +707,7 @@ def bench_slotcache(args):
                                   "(stand-in for a trained predictor)") if R else None},
         "steady_state_ms_per_token": round(steady * 1e3, 4),
         "cache": {**st, "hit_rate": round(st["hits"] / uses, 4)},
+        "routing_repeat_rate": round(repeat, 4),
         "h2d_GBps": round(st["bytes_h2d"] / elapsed / 1e9, 2),
         "h2d_bytes_per_token": int(st["bytes_h2d"] / T),
         "pinned_copy_GBps_measured": round(h2d_peak, 1),

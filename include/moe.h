@@ -63,7 +63,11 @@ typedef enum {
   MOE_ESTATE = 6         /* call out of order (e.g. cache used after an error) */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* Element types of activations and outputs.  A plain integer rather than an
+ * enum type, so that any value a caller passes is a valid argument (and is
+ * rejected with MOE_EINVAL unless it is one of these). */
+typedef int32_t moe_dtype;
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
 
 typedef void* moe_stream_t; /* hipStream_t */
 

@@ -59,5 +59,57 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB_PATH
 
 
+# Host-side sanitizers (AddressSanitizer + UndefinedBehaviorSanitizer) for the
+# library's host code: the .cpp sources (entry points, slot-cache policy and
+# bookkeeping, profiling, tensor-parallel slicing) are compiled with the
+# sanitizers on their host pass only; the kernels' objects are the regular
+# build's.  The result loads into a Python process that preloads the ASan
+# runtime (asan_runtime()).
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(BUILD, "san", "libmoe_mi355x_san.so")
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (to preload)."""
+    p = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = p.stdout.strip()
+    if p.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        cands = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+        if not cands:
+            raise RuntimeError("the compiler's shared ASan runtime was not found")
+        path = cands[-1]
+    return path
+
+
+def build_host_sanitized(jobs: int | None = None) -> str:
+    """libmoe_mi355x_san.so: host code instrumented, kernels as in build()."""
+    hip_srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    hip_objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in hip_srcs]
+    if not all(os.path.exists(o) and os.path.getmtime(o) >= os.path.getmtime(s) for s, o in zip(hip_srcs, hip_objs)):
+        build(jobs=jobs)
+    sdir = os.path.dirname(SAN_LIB)
+    os.makedirs(sdir, exist_ok=True)
+    cpp_srcs = sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
+    cpp_objs = [os.path.join(sdir, os.path.basename(s) + ".o") for s in cpp_srcs]
+
+    def comp(src, obj):
+        cmd = [hipcc(), *HIP_FLAGS, "-O1", *SAN_FLAGS, "-c", src, "-o", obj]
+        p = subprocess.run(cmd, capture_output=True, text=True)
+        if p.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{p.stdout}\n{p.stderr}")
+
+    with cf.ThreadPoolExecutor(jobs or min(len(cpp_srcs), 8)) as ex:
+        list(ex.map(comp, cpp_srcs, cpp_objs))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, "-shared-libsan", "-o", tmp,
+           *cpp_objs, *hip_objs]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{p.stdout}\n{p.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -9,6 +9,12 @@ if ROOT not in sys.path:
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
+# The host-sanitizer test reruns CPU suites in a child process against the
+# sanitizer-instrumented build of the library; it names that build here.
+if os.environ.get("MOE_TEST_LIBRARY"):
+    from mxfp4_routed_expert_renorm_amd import binding as _binding
+    _binding.LIB_PATH = os.environ["MOE_TEST_LIBRARY"]
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")

@@ -138,6 +138,21 @@ def test_layer_decode_validation(lib):
     assert st == 1 and "dtype" in msg
 
 
+def test_layer_decode_noalloc_validation(lib):
+    """The allocation-free decode refuses a NULL layer, a bad k and a layer
+    whose workspace exceeds the static scratch before it touches a device."""
+    call = lambda layer, k=8: _status(lib, "moe_layer_decode_noalloc", layer, FAKE, 256, FAKE, 1, k, FAKE, FAKE,
+                                      FAKE, 1, None)
+    st, msg = call(None)
+    assert st == 1 and "layer is NULL" in msg
+    big = B.moe_layer(8192, 8192, 0x1000, lib.moe_fp4_expert_bytes(8192, 8192), 256, None, 0, 0, 0x2000)
+    st, msg = call(ctypes.byref(big), k=0)
+    assert st == 1 and "k=0" in msg
+    st, msg = call(ctypes.byref(big), k=64)
+    assert st == 4 and "static scratch" in msg
+    assert lib.moe_expert_workspace_sync_offset(8192, 8192, 1, 64, 1) > lib.moe_noalloc_scratch_bytes()
+
+
 def test_last_error_is_thread_local(lib):
     import threading
     _status(lib, "moe_route", FAKE, 1, 8, 9, FAKE, FAKE, None)
