@@ -435,6 +435,83 @@ def prefill_forward(x, ids, w, get_record, H: int, I: int, shared_rec=None, toke
 
 
 # ============================================================================
+# 7b. the 2-bit fallback copy of an MXFP4 expert (offline clip search)
+# ============================================================================
+# P2 (opening section; §Rig, model & methodology) re-quantises every expert
+# to 2-bit codes with one fp8 E4M3 scale per 32 weights, the scale "chosen by
+# clip search", and states no more.  Reading: per 32-weight group of the
+# dequantised FP4 weights, each clip ratio alpha of CLIP_ALPHAS proposes the
+# scale s = E4M3(alpha * amax / 1.5) (nearest, ties to even: the levels
+# +-1.5 s then reach alpha * amax), each weight takes the nearest level
+# (code = clamp(round_half_even(w / s + 1.5), 0, 3)), and the ratio with the
+# least squared error sum(w - w_hat)^2, summed in element order, wins; ties
+# go to the larger alpha.  A scale that rounds to 0 gives every weight the
+# level 0 (code 2).  All arithmetic is float64, one IEEE operation at a time.
+
+CLIP_ALPHAS = (1.00, 0.95, 0.90, 0.85, 0.80, 0.75, 0.70, 0.65, 0.60, 0.55, 0.50)
+
+
+def quant_int2_clip(W: np.ndarray):
+    """[rows, cols] float64 weights -> (2-bit codes uint8 [rows, cols] (0..3),
+    E4M3 scale bytes uint8 [rows, cols/32]) by the clip search above."""
+    W = np.asarray(W, np.float64)
+    rows, cols = W.shape
+    g = W.reshape(rows * (cols // 32), 32)
+    amax = np.abs(g).max(axis=1)
+    best_err = np.full(g.shape[0], np.inf)
+    best_codes = np.full(g.shape, 2, dtype=np.uint8)
+    best_scale = np.zeros(g.shape[0], dtype=np.uint8)
+    for alpha in CLIP_ALPHAS:
+        t = (alpha * amax) / 1.5
+        sc = e4m3_encode(t)
+        s = e4m3_value(sc)
+        ok = s > 0.0
+        safe = np.where(ok, s, 1.0)
+        c = np.clip(np.rint(g / safe[:, None] + 1.5), 0.0, 3.0)
+        c = np.where(ok[:, None], c, 2.0)
+        w_hat = (c - 1.5) * s[:, None]
+        err = np.zeros(g.shape[0])
+        for j in range(32):                 # element order
+            d = g[:, j] - w_hat[:, j]
+            err = err + d * d
+        better = err < best_err              # strict: ties keep the larger alpha
+        best_err = np.where(better, err, best_err)
+        best_codes = np.where(better[:, None], c.astype(np.uint8), best_codes)
+        best_scale = np.where(better, sc, best_scale)
+    return best_codes.reshape(rows, cols), best_scale.reshape(rows, cols // 32)
+
+
+def pack_int2_codes(c: np.ndarray) -> np.ndarray:
+    """[rows, cols] 2-bit codes -> [rows, cols/4] bytes, element 4j+q in bits
+    2q..2q+1 of byte j (the packing unpack_int2_codes reads)."""
+    c = np.asarray(c, np.uint8)
+    out = np.zeros((c.shape[0], c.shape[1] // 4), dtype=np.uint8)
+    for q in range(4):
+        out |= (c[:, q::4] & 0x3) << (2 * q)
+    return out
+
+
+def int2_record_from_fp4(rec: np.ndarray, H: int, I: int, rows=None) -> np.ndarray:
+    """The 2-bit record (layout of int2_expert_nbytes) of one MXFP4 record.
+    rows (optional): {matrix name: row indices} to compute only those rows;
+    the other rows' bytes are left 0."""
+    p = split_record(rec, H, I, 4)
+    shapes = {"w1": (I, H), "w3": (I, H), "w2": (H, I)}
+    codes, scales = {}, {}
+    for name in ("w1", "w3", "w2"):
+        r, c = shapes[name]
+        idx = np.arange(r) if rows is None else np.asarray(rows[name])
+        W = dequant_mxfp4(p[name + "_codes"][idx], p[name + "_scales"][idx])
+        cq, sq = quant_int2_clip(W)
+        codes[name] = np.zeros((r, c // 4), np.uint8)
+        scales[name] = np.zeros((r, c // 32), np.uint8)
+        codes[name][idx] = pack_int2_codes(cq)
+        scales[name][idx] = sq
+    return np.concatenate([codes["w1"].ravel(), codes["w3"].ravel(), codes["w2"].ravel(),
+                           scales["w1"].ravel(), scales["w3"].ravel(), scales["w2"].ravel()])
+
+
+# ============================================================================
 # 8. the slot cache with the precision ladder
 # ============================================================================
 
