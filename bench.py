@@ -603,9 +603,20 @@ def bench_slotcache(args):
     int2_host = lib.PinnedBuffer(L * E * rb2)
     for p in range(L * E):
         W.fp4_record(seed, W.S_BANK, p, H, I, out=fp4_host.array[p * rb4:(p + 1) * rb4])
-        W.int2_record(seed, W.S_INT2, p, H, I, out=int2_host.array[p * rb2:(p + 1) * rb2])
         if p % 256 == 255:
             print(f"[bench] {p + 1}/{L * E} host records", file=sys.stderr, flush=True)
+    # the 2-bit fallback copies are made from the FP4 records (clip search on
+    # the GPU, moe_int2_from_fp4), 64 records at a time
+    nb = 64
+    src_d = torch.empty((nb, rb4), dtype=torch.uint8, device=dev)
+    dst_d = torch.empty((nb, rb2), dtype=torch.uint8, device=dev)
+    for p0 in range(0, L * E, nb):
+        n = min(nb, L * E - p0)
+        src_d[:n].copy_(torch.from_numpy(fp4_host.array[p0 * rb4:(p0 + n) * rb4]).view(n, rb4))
+        lib.moe_int2_from_fp4(src_d[:n], H, I, dst_d[:n])
+        torch.from_numpy(int2_host.array[p0 * rb2:(p0 + n) * rb2]).view(n, rb2).copy_(dst_d[:n])
+    del src_d, dst_d
+    print(f"[bench] 2-bit copies of the {L * E} records made", file=sys.stderr, flush=True)
     R = args.prefetch
     arena = torch.empty((S + R) * rb4, dtype=torch.uint8, device=dev)
     tier = {}
@@ -694,7 +705,8 @@ def bench_slotcache(args):
         "value": round(T / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": T, "warmup": 0,
         "ms_per_step": round(elapsed / T * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp4+int2-w/bf16-x/f32-acc",
-        "data": "synthetic (seeded; per-layer Zipf(1.1) logits, fresh activations per token and layer)",
+        "data": "synthetic (seeded; per-layer Zipf(1.1) logits, fresh activations per token and layer; "
+                "2-bit copies made from the FP4 records by clip search)",
         "config": {"workload": cfg["name"] + ("-int2tier100-lfu" if tier else "") + (f"-ring{R}" if R else ""),
                    "layers": L, "experts": E,
                    "slots": S, "top_k": k, "ladder": [a, b], "tokens": T, "cold_start": True,

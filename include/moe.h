@@ -269,6 +269,24 @@ moe_status moe_tp_slice(const uint8_t* src, size_t src_stride, int n, int H, int
  * [rows][K/32] uint8; K a multiple of 32. */
 moe_status moe_quant_mxfp8(const void* x, int rows, int K, uint8_t* codes, uint8_t* scales, moe_stream_t stream);
 
+/* The 2-bit fallback copies of n MXFP4 expert records ("An elephant through a
+ * straw", opening section and §Rig, model & methodology: 2-bit codes with one
+ * fp8 E4M3 scale per 32 weights, the scale chosen by clip search, made
+ * offline).  Per 32-weight group of the dequantised weights, each clip ratio
+ * alpha in 1.00, 0.95, ..., 0.50 proposes the E4M3 scale s nearest to
+ * alpha * amax / 1.5 (ties to even); each weight takes the nearest level
+ * (c - 1.5) s, c = clamp(round half to even(w / s + 1.5), 0, 3); the ratio
+ * with the least squared error (summed in element order) wins, ties to the
+ * larger ratio; a zero scale gives code 2 throughout.  float64 throughout.
+ *   src: device, n FP4 records (moe_fp4_expert_bytes(H, I)) src_stride apart,
+ *        16-byte aligned; dst: device, n 2-bit records
+ *        (moe_int2_expert_bytes(H, I)) dst_stride apart, 8-byte aligned.
+ * Strides matter only for n > 1; src_stride a multiple of 16, dst_stride of 8.
+ * H, I positive multiples of 32; 0 <= n <= 65535.  E8M0 scale byte 255 (NaN)
+ * is outside the input domain. */
+moe_status moe_int2_from_fp4(const uint8_t* src, size_t src_stride, int n, int H, int I, uint8_t* dst,
+                             size_t dst_stride, moe_stream_t stream);
+
 /* Workspace bytes of moe_prefill_forward. */
 size_t moe_prefill_workspace_bytes(int H, int I, int T, int k, int has_shared);
 

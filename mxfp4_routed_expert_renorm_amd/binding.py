@@ -84,6 +84,7 @@ _SIGS = {
     "moe_debug_stream_read": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "moe_tp_slice": (c_int, [c_void_p, c_size_t, c_int, c_int, c_int, c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "moe_quant_mxfp8": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "moe_int2_from_fp4": (c_int, [c_void_p, c_size_t, c_int, c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "moe_prefill_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "moe_prefill_forward": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_int, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -269,6 +270,15 @@ def moe_tp_slice(src, H, I, G, g, dst, stream=None):
         return t.stride(0) if t.shape[0] > 1 else t.shape[1]
     _check("moe_tp_slice", load().moe_tp_slice(_p(src), row_stride(src), src.shape[0], H, I, G, g, _p(dst),
                                                row_stride(dst), _stream(stream)))
+    return dst
+
+
+def moe_int2_from_fp4(src, H, I, dst, stream=None):
+    """2-bit copies of FP4 records: src uint8 [n, stride] -> dst uint8 [n, stride'] (clip search)."""
+    def row_stride(t):
+        return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    _check("moe_int2_from_fp4", load().moe_int2_from_fp4(_p(src), row_stride(src), src.shape[0], H, I, _p(dst),
+                                                         row_stride(dst), _stream(stream)))
     return dst
 
 
