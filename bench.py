@@ -56,6 +56,9 @@ def parse():
                     help="decode-b1: resident layers the timed steps rotate over (step s runs layer s mod L)")
     ap.add_argument("--tp-share", type=int, default=1,
                     help="decode-b1 on rank 0's share of G-way tensor parallelism (experts cut along I)")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="decode-b1: layers flagged MOE_LAYER_SINGLE_LAUNCH (routing through combine in one kernel; "
+                         "hidden 4096 with I 2048, or I 256 with --tp-share 8)")
     ap.add_argument("--slot-tier", action="store_true",
                     help="slotcache workload with a 100-slot 2-bit device tier and LFU eviction "
                          "(decay 0.95, counts seeded from a separate 64-token routing trace)")
@@ -302,7 +305,9 @@ def bench_decode_b1(args):
     w_d = torch.empty((nsteps, k), dtype=torch.float32, device=dev)
     out_d = torch.empty((nsteps, H), dtype=torch.bfloat16, device=dev)
     ws = lib.expert_workspace(H, I, T, k, True, device=dev)
-    layers = [lib.make_layer(H, I, fp4_base=bk, fp4_stride=rec_bytes, num_slots=E, shared=sh) for bk, sh in layers_mem]
+    lflags = lib.MOE_LAYER_SINGLE_LAUNCH if args.single_launch else 0
+    layers = [lib.make_layer(H, I, fp4_base=bk, fp4_stride=rec_bytes, num_slots=E, shared=sh, flags=lflags)
+              for bk, sh in layers_mem]
     torch.cuda.synchronize()
     print(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
@@ -334,15 +339,23 @@ def bench_decode_b1(args):
     # written and read back, the ids and weights, the bf16 output row
     step_alg_bytes = k1 * rec_bytes + E * 4 + H * 2 + 2 * k1 * I * 2 + k * 8 + H * 2
     khash = kernel_hash()
-    traffic = traffic_from_profiles(khash) if G == 1 else None
+    traffic = traffic_from_profiles(khash) if G == 1 and not args.single_launch else None
     per_kernel = {n: round(v[0] / v[1] * 1e3, 3) for n, v in prof.items()}
     print(f"[bench] kernel averages (us): {per_kernel}", file=sys.stderr, flush=True)
-    ms, n = prof["gateup"]      # the dominant kernel of the two launches
-    dom_kernel = ("gateup_b1_kernel (routing + batch-1 gate/up GEMV + SwiGLU)" if G == 1 else
-                  f"gateup_b1s_kernel (routing + batch-1 gate/up GEMV + SwiGLU of a 1/{G} share, I = {I})")
-    # the 9 experts' w1 and w3 codes and scales, the logits row, the activation
-    # row, the bf16 SwiGLU outputs written
-    dom_bytes = k1 * 2 * (H * I // 2 + H * I // 32) + E * 4 + H * 2 + k1 * I * 2
+    if "fused" in prof:  # the single launch: the whole step is one kernel
+        ms, n = prof["fused"]
+        dom_kernel = ("fused_b1_kernel (routing through combine, one launch)" if G == 1 else
+                      f"fused_b1s_kernel (routing through combine of a 1/{G} share, I = {I}, one launch)")
+        # the step's algorithmic bytes (the SwiGLU outputs cross workgroups
+        # through memory: written once and read back)
+        dom_bytes = step_alg_bytes
+    else:
+        ms, n = prof["gateup"]      # the dominant kernel of the two launches
+        dom_kernel = ("gateup_b1_kernel (routing + batch-1 gate/up GEMV + SwiGLU)" if G == 1 else
+                      f"gateup_b1s_kernel (routing + batch-1 gate/up GEMV + SwiGLU of a 1/{G} share, I = {I})")
+        # the 9 experts' w1 and w3 codes and scales, the logits row, the
+        # activation row, the bf16 SwiGLU outputs written
+        dom_bytes = k1 * 2 * (H * I // 2 + H * I // 32) + E * 4 + H * 2 + k1 * I * 2
     dom_avg_s = ms / n / 1e3
     achieved = dom_bytes / dom_avg_s / 1e9
 
@@ -363,7 +376,8 @@ def bench_decode_b1(args):
         "dtype": "mxfp4-w/bf16-x/f32-acc",
         "data": "synthetic (seeded; fresh logits and activations every step)",
         "config": {"workload": cfg["name"] + (f"-tp{G}-share0" if G > 1 else "") +
-                   (f"-{NL}layers-rotated" if NL > 1 else ""), "experts": E,
+                   (f"-{NL}layers-rotated" if NL > 1 else "") + ("-single-launch" if args.single_launch else ""),
+                   "experts": E,
                    "shared_experts": 1, "hidden": H, "expert_intermediate": I, "top_k": k, "tokens_per_step": T,
                    "layers": NL, "layer_of_step": "s mod layers",
                    "expert_bytes": rec_bytes, "weight_bytes_per_step": step_bytes, "launch": args.mode,

@@ -61,6 +61,9 @@ size_t fused_sync_bytes();
 bool fused_path_ok(const moe_layer* L, int K1, bool xbf16, bool obf16, bool has_prec);
 moe_status launch_fused_b1(const moe_layer* L, const float* logits, int E, const void* x, int k, int32_t* slot_ids,
                            float* w, uint16_t* h, void* out, uint32_t* sync, hipStream_t s);
+bool fused_s_path_ok(const moe_layer* L, int K1, bool xbf16, bool obf16, bool has_prec);
+moe_status launch_fused_b1s(const moe_layer* L, const float* logits, int E, const void* x, int k, int32_t* slot_ids,
+                            float* w, uint16_t* h, void* out, uint32_t* sync, hipStream_t s);
 moe_status launch_decode_mfma(const moe_layer* Lr, const void* x, int T, int k, const int32_t* slot_ids, const float* w,
                               void* out, uint16_t* h, float* y, int32_t* plan, hipStream_t s);
 
@@ -189,6 +192,9 @@ moe_status expert_forward_impl(const moe_layer* layer, const void* x, moe_dtype 
   if (T == 1 && w && b1_path_ok(layer->H, layer->I, K1, xt == MOE_BF16, ot == MOE_BF16))  // reads slot_ids and w only
     return launch_b1(layer, nullptr, 0, x, k, const_cast<int32_t*>(slot_ids), prec, const_cast<float*>(w),
                      (uint16_t*)h, out, s);
+  if (T == 1 && w && fused_s_path_ok(layer, K1, xt == MOE_BF16, ot == MOE_BF16, prec != nullptr))
+    return launch_fused_b1s(layer, nullptr, 0, x, k, const_cast<int32_t*>(slot_ids), const_cast<float*>(w),
+                            (uint16_t*)h, out, sync, s);
   if (T == 1 && w && b1s_path_ok(layer->H, layer->I, K1, xt == MOE_BF16, ot == MOE_BF16, prec != nullptr))
     return launch_b1s(layer, nullptr, 0, x, k, const_cast<int32_t*>(slot_ids), const_cast<float*>(w), (uint16_t*)h,
                       out, s);
@@ -231,6 +237,9 @@ moe_status layer_decode_impl(const moe_layer* layer, const float* logits, int E,
     return launch_fused_b1(layer, logits, E, x, k, ids, w, (uint16_t*)workspace, out, sync, s);
   if (b1_path_ok(layer->H, layer->I, k + has_shared, xt == MOE_BF16, ot == MOE_BF16) && b1_route_ok(E, layer->num_slots))
     return launch_b1(layer, logits, E, x, k, ids, nullptr, w, (uint16_t*)workspace, out, s);
+  if (fused_s_path_ok(layer, k + has_shared, xt == MOE_BF16, ot == MOE_BF16, false) &&
+      b1s_route_ok(E, layer->num_slots))
+    return launch_fused_b1s(layer, logits, E, x, k, ids, w, (uint16_t*)workspace, out, sync, s);
   if (b1s_path_ok(layer->H, layer->I, k + has_shared, xt == MOE_BF16, ot == MOE_BF16, false) &&
       b1s_route_ok(E, layer->num_slots))
     return launch_b1s(layer, logits, E, x, k, ids, w, (uint16_t*)workspace, out, s);

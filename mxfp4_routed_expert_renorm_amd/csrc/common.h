@@ -147,6 +147,16 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
 }
 
+// sum over each aligned group of 8 lanes, in every lane of the group: the
+// quads' butterflies, then the mirror within the 8 (lane i and 7 - i hold
+// the two quads' sums)
+__device__ __forceinline__ float group8_sum_dpp(float v) {
+  v += dpp_f32<dpp::kQuadXor1>(v);
+  v += dpp_f32<dpp::kQuadXor2>(v);
+  v += dpp_f32<dpp::kRowHalfMirror>(v);
+  return v;
+}
+
 // sum over the 64 lanes, valid in lane 63
 __device__ __forceinline__ float wave_sum_to_lane63(float v) {
   v += dpp_f32<dpp::kQuadXor1>(v);

@@ -17,7 +17,7 @@
 //     order).  Computing wavefront w (0..7) takes row 8u+w over all of H,
 //     with a few groups' rows in flight at a time, and leaves each group's
 //     SwiGLU output in LDS; wavefront 0 then publishes the unit's h with
-//     write-through stores and raises the unit's done flag.
+//     write-through stores and arrives at the handoff below.
 //   - Down unit u: output rows 16u..16u+15 for every group.  Copying
 //     wavefront c (8..15) loads W2 rows 16u+2c', 16u+2c'+1 (c' = c - 8) of
 //     every group and their scale bytes into registers, then moves each
@@ -35,17 +35,17 @@
 //   - The items' results meet in LDS; 16 threads sum each output row over the
 //     groups in rank order (shared expert last, weight 1) and round once.
 //
-// Cross-workgroup handoff.  h and the done flags are written with
-// agent-scope stores, which write through to the device's coherence point,
-// after the storing wavefront's earlier stores have completed (vmcnt 0, and
-// that wavefront has no other memory operation in flight).  A reader polls
-// the flags with agent-scope loads and only then reads h with ordinary loads;
-// no workgroup reads h before every flag is up, and a launch starts with
-// invalidated caches, so no stale copy of h can be hit.  The flags hold a
-// launch tag: a workgroup's tag is its own flag plus one, since only that
-// workgroup writes its flag.  Nothing is reset between launches, so the flags
-// must start equal (a zeroed workspace) and launches that share them must
-// not overlap.
+// Cross-workgroup handoff.  h is written with agent-scope stores, which write
+// through to the device's coherence point; once they have completed (vmcnt 0,
+// and the storing wavefront has no other memory operation in flight) the
+// unit arrives: its launch tag, then two levels of arrival counters (eight
+// groups of 32 units, then one word), all with agent-scope atomics.  A
+// reader polls that one word with agent-scope loads and only then reads h
+// with ordinary loads; no workgroup reads h before every unit has arrived,
+// and a launch starts with invalidated caches, so no stale copy of h can be
+// hit.  A unit's tag is its own tag word plus one, since only that unit
+// writes it.  Nothing is reset between launches, so the sync words must start
+// at zero (a zeroed workspace) and launches that share them must not overlap.
 //
 // Every workgroup must be resident at once: the host launches this kernel
 // only on a device with at least 256 CUs.  Waits are bounded; a wait that
@@ -54,13 +54,14 @@
 #include "common.h"
 #include "route_dev.h"
 #include "b1_dev.h"
+#include "handoff_dev.h"
 
 namespace moe {
 
 namespace {
 
 constexpr int kFH = 4096, kFI = 2048;
-constexpr int kFUnits = 256;             // gate/up units = down units = workgroups
+constexpr int kFUnits = kHandoffUnits;   // gate/up units = down units = workgroups
 constexpr int kFRowsGU = kFI / kFUnits;  // 8 gate/up rows per unit
 constexpr int kFRowsDN = kFH / kFUnits;  // 16 down rows per unit
 constexpr int kFWaves = 16, kFThreads = 64 * kFWaves;
@@ -91,8 +92,8 @@ struct FusedArgs {
   float* w;             // [k]
   uint32_t* h;          // [kFMaxG][kFI] bf16, group-major, as bf16 pairs
   void* out;            // [kFH] bf16
-  uint32_t* done;       // [kFUnits] launch tags
-  uint32_t* err;        // set to nonzero when a wait gives up
+  uint32_t* sync;       // the handoff's words, kept between launches
+  uint32_t* err;        // its error word: bit 0 the handoff gave up, bit 1 a W2 wait did
 };
 
 struct alignas(16) FusedSmem {
@@ -171,9 +172,8 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
         s.s3[q] = rec[L.w3s + (size_t)row * kRowS + c];
       }
     };
-    // this launch's tag (wavefront 0 publishes and waits with it): only this
-    // workgroup writes its flag
-    const uint32_t tag = __hip_atomic_load(&a.done[unit], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    // this launch's tag (wavefront 0 arrives and waits with it)
+    const uint32_t tag = handoff_tag(a.sync, unit);
     // 1. the activation, the routing inputs (wavefront 0), the shared
     // expert's row: none of it needs the routing
     B1Chunk x0, x1;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
     lds_barrier();  // B1: the unit's SwiGLU outputs are in LDS
 
     // 4. wavefront 0 publishes the unit's h (bf16 pairs, write-through),
-    // then its done flag, then waits for every unit
+    // then arrives and waits for every unit
     if (wave == 0) {
       if (lane < 4 * ng) {
         const int g = lane >> 2, p = lane & 3;
@@ -254,19 +254,7 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
                            __HIP_MEMORY_SCOPE_AGENT);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the h stores have completed
-      if (lane == 0) __hip_atomic_store(&a.done[unit], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      uint32_t it = 0;
-      for (;;) {
-        bool ok = true;
-#pragma unroll
-        for (int q = 0; q < kFUnits / 64; ++q)
-          ok &= __hip_atomic_load(&a.done[q * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
-        if (__all(ok)) break;
-        if (++it > kFSpin) {
-          if (lane == 0) atomicOr(a.err, 1u);
-          break;
-        }
-      }
+      handoff_arrive_wait(a.sync, unit, tag, kFSpin);
       if (lane == 0) __hip_atomic_store(&sm.go, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
 
@@ -403,8 +391,9 @@ void launch_fused_nb(const FusedArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// workspace bytes the fused step keeps between launches (its done flags)
-size_t fused_sync_bytes() { return 2 * kFUnits * 4; }
+// workspace bytes the single-launch steps keep between launches (the
+// handoff's tags and counters)
+size_t fused_sync_bytes() { return kHandoffSyncBytes; }
 
 // The fused step covers the pages' model shape with bf16 activations and
 // output, all-FP4 ranks, up to 8 of them plus the shared expert, on a device
@@ -439,8 +428,8 @@ moe_status launch_fused_b1(const moe_layer* L, const float* logits, int E, const
   a.w = w;
   a.h = (uint32_t*)h;
   a.out = out;
-  a.done = sync;
-  a.err = sync + kFUnits;
+  a.sync = sync;
+  a.err = sync + kSyncErr;
   const int K1 = k + (L->shared ? 1 : 0);
   const int nb = K1 <= 4 ? 4 : K1 <= 7 ? 7 : 9;
   if (L->shared) {

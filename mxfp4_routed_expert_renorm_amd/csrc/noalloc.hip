@@ -3,10 +3,10 @@
 //
 // Layout of the array (one copy per device, held until the process ends):
 //   [0, kSyncBytes)            the words the single-launch step keeps between
-//                              calls (a flag per workgroup, then the error
-//                              word at +1024), at a fixed place so that calls
-//                              of different shapes find them where the last
-//                              call left them;
+//                              calls (a launch tag per workgroup, the error
+//                              word at +1024, the arrival counters), at a
+//                              fixed place so that calls of different shapes
+//                              find them where the last call left them;
 //   [kSyncBytes, kScratchBytes) the per-call workspace (SwiGLU outputs, rank
 //                              outputs, plans), rewritten by every call.
 // The host learns each device's address of the array once, with that device
@@ -15,6 +15,7 @@
 #include <mutex>
 
 #include "common.h"
+#include "handoff_dev.h"
 
 namespace moe {
 
@@ -25,6 +26,7 @@ moe_status layer_decode_impl(const moe_layer* layer, const float* logits, int E,
 namespace {
 
 constexpr size_t kSyncBytes = 4096;
+static_assert(kSyncBytes >= kHandoffSyncBytes, "the single-launch steps' words fit");
 constexpr size_t kScratchBytes = size_t(4) << 20;  // 4 MiB per device
 constexpr int kMaxDevices = 64;
 

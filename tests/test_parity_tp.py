@@ -186,3 +186,186 @@ def test_tp_share_given_ids_and_the_shares_sum_to_the_layer(gpu_lib, with_shared
     err = max_rel(total, full)
     log(f"sum of the 8 shares vs the full layer: max-rel {err:.3e}")
     assert err <= TOL_BF16_MAX_REL
+
+
+# ------------------------------------------------ single launch of a 1/8 share
+# MOE_LAYER_SINGLE_LAUNCH at H 4096, I 256: routing, gate/up, SwiGLU, down and
+# combine in one launch, the units handing their SwiGLU outputs to each other
+# through the workspace.  Calls go back to back, so the per-call tags advance.
+
+def _err_word(gpu_lib, ws, Is, k, with_shared):
+    off = gpu_lib.moe_expert_workspace_sync_offset(4096, Is, 1, k, with_shared)
+    return int(ws[off + 1024:off + 1028].cpu().numpy().view(np.uint32)[0])
+
+
+@pytest.mark.parametrize("g,k", [(0, 8), (5, 8), (3, 6), (7, 3)])
+def test_tp_share_single_launch_decode(gpu_lib, g, k):
+    """moe_layer_decode on share g of 8 in one launch, k ranks plus the shared
+    expert (9, 7 and 4 groups: each batch size of the kernel): routing equal to
+    the oracle's, outputs the oracle's partial sums, error word zero."""
+    import torch
+    from tests.gpu_util import TOL_BF16_MAX_REL, bf16_dev, max_rel, to_f64
+    st = _wide_bank()
+    H, I, E, G = 4096, 2048, 24, 8
+    bank_d, shared_d = dev(st["bank"]), dev(st["shared"][None, :])
+    sb, ss = _share_bank(gpu_lib, bank_d, H, I, G, g), _share_bank(gpu_lib, shared_d, H, I, G, g)
+    layer = gpu_lib.make_layer(H, I // G, fp4_base=sb, fp4_stride=sb.shape[1], num_slots=E, shared=ss[0],
+                               flags=gpu_lib.MOE_LAYER_SINGLE_LAUNCH)
+    ws = gpu_lib.expert_workspace(H, I // G, 1, k, True)
+    ntok = 4
+    xs = W.bf16_normal(74, (g, k), (ntok, H))
+    lg = W.router_logits(74, (g, k, 1), ntok, E)
+    lg_d, x_d = dev(lg), bf16_dev(xs)
+    ids = torch.full((ntok, k), -3, dtype=torch.int32, device="cuda")
+    w = torch.full((ntok, k), -3.0, dtype=torch.float32, device="cuda")
+    out = torch.empty((ntok, H), dtype=torch.bfloat16, device="cuda")
+    log(f"single-launch TP share {g}/8, k {k}: {ntok} tokens back to back")
+    for t in range(ntok):
+        gpu_lib.moe_layer_decode(layer, lg_d[t], x_d[t:t + 1], k, ids[t], w[t], out[t:t + 1], ws)
+    torch.cuda.synchronize()
+    assert _err_word(gpu_lib, ws, I // G, k, True) == 0
+    oids, ow = O.route(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.max(np.abs(w.cpu().numpy() - ow)) <= 1e-6
+    got = to_f64(out)
+    for t in range(ntok):
+        ref = _share_ref(O.bf16_bits_to_f64(xs[t:t + 1])[0], oids[t], ow[t], G, g)
+        err = max_rel(got[t], ref)
+        log(f"  token {t}: max-rel {err:.3e}")
+        assert err <= TOL_BF16_MAX_REL, (t, err)
+
+
+@pytest.mark.parametrize("with_shared", [True, False])
+def test_tp_share_single_launch_given_ids_with_drops(gpu_lib, with_shared):
+    """moe_expert_forward at T = 1 in one launch on every share of an 8-way
+    split, from given ids with dropped ranks (without the shared expert the
+    eight ranks fill the 9-group batch but one): each share matches the
+    oracle's partial output and the two-launch step's output within the
+    tolerance, and the eight partials add up to the full layer."""
+    import torch
+    from tests.gpu_util import TOL_BF16_MAX_REL, bf16_dev, max_rel, to_f64
+    st = _wide_bank()
+    H, I, E, k, G = 4096, 2048, 24, 8, 8
+    bank_d, shared_d = dev(st["bank"]), dev(st["shared"][None, :])
+    cases = [np.array([[5, 23, -1, 0, 17, 24, 9, 2]], np.int32),
+             np.array([[-1, -1, -1, -1, -1, -1, -1, -1]], np.int32),
+             np.array([[-1, 30, -1, 11, -1, -1, -1, -1]], np.int32)]
+    wts = np.random.default_rng(75).random((len(cases), k)).astype(np.float32)
+    xs = W.bf16_normal(75, (1,), (len(cases), H))
+    total = np.zeros((len(cases), H))
+    for g in range(G):
+        sb, ss = _share_bank(gpu_lib, bank_d, H, I, G, g), _share_bank(gpu_lib, shared_d, H, I, G, g)
+        outs = {}
+        for flags in (gpu_lib.MOE_LAYER_SINGLE_LAUNCH, 0):
+            layer = gpu_lib.make_layer(H, I // G, fp4_base=sb, fp4_stride=sb.shape[1], num_slots=E,
+                                       shared=ss[0] if with_shared else None, flags=flags)
+            ws = gpu_lib.expert_workspace(H, I // G, 1, k, with_shared)
+            out = torch.empty((len(cases), H), dtype=torch.bfloat16, device="cuda")
+            for i, ids in enumerate(cases):
+                gpu_lib.moe_expert_forward(layer, bf16_dev(xs[i:i + 1]), 1, k, dev(ids), None, dev(wts[i:i + 1]),
+                                           out[i:i + 1], ws)
+            torch.cuda.synchronize()
+            if flags:
+                assert _err_word(gpu_lib, ws, I // G, k, with_shared) == 0
+            outs[flags] = to_f64(out)
+        got = outs[gpu_lib.MOE_LAYER_SINGLE_LAUNCH]
+        for i, ids in enumerate(cases):
+            x64 = O.bf16_bits_to_f64(xs[i:i + 1])[0]
+            ref = _share_ref(x64, ids[0], wts[i].astype(np.float64), G, g, with_shared)
+            if not with_shared and np.all(ids < 0):
+                assert np.all(got[i] == 0.0), (g, i)   # nothing to combine: exact zeros
+                continue
+            err = max_rel(got[i], ref)
+            log(f"share {g}/8 case {i} shared={with_shared}: max-rel {err:.3e}")
+            assert err <= TOL_BF16_MAX_REL, (g, i, err)
+            assert max_rel(got[i], outs[0][i]) <= 2 * TOL_BF16_MAX_REL, (g, i)
+        total += got
+    for i, ids in enumerate(cases):
+        if not with_shared and np.all(ids < 0):
+            continue
+        x64 = O.bf16_bits_to_f64(xs[i:i + 1])[0]
+        full = O.combine(np.stack([O.expert_mlp(x64, *_wide_weights(int(e))) if 0 <= e < 24 else np.zeros(H)
+                                   for e in ids[0]]),
+                         np.where((ids[0] >= 0) & (ids[0] < 24), wts[i].astype(np.float64), 0.0),
+                         O.expert_mlp(x64, *_wide_weights(-1)) if with_shared else None)
+        assert max_rel(total[i], full) <= TOL_BF16_MAX_REL, i
+
+
+def test_tp_share_single_launch_wide_router(gpu_lib):
+    """300 experts (more than 256 logits: sixteen per lane in the kernel's
+    routing), top-8 + shared, on a bank made at the share's own width: routing
+    and outputs equal to the oracle's."""
+    import torch
+    from tests.gpu_util import TOL_BF16_MAX_REL, bf16_dev, max_rel, to_f64
+    H, Is, E, k = 4096, 256, 300, 8
+    bank = W.fp4_bank(76, 1, E, H, Is)
+    shared = W.fp4_record(76, 2, 0, H, Is)
+    bank_d, shared_d = dev(bank), dev(shared[None, :])
+    layer = gpu_lib.make_layer(H, Is, fp4_base=bank_d, fp4_stride=bank.shape[1], num_slots=E, shared=shared_d[0],
+                               flags=gpu_lib.MOE_LAYER_SINGLE_LAUNCH)
+    ws = gpu_lib.expert_workspace(H, Is, 1, k, True)
+    ntok = 3
+    xs = W.bf16_normal(76, (3,), (ntok, H))
+    lg = W.router_logits(76, (4,), ntok, E)
+    lg_d, x_d = dev(lg), bf16_dev(xs)
+    ids = torch.full((ntok, k), -3, dtype=torch.int32, device="cuda")
+    w = torch.full((ntok, k), -3.0, dtype=torch.float32, device="cuda")
+    out = torch.empty((ntok, H), dtype=torch.bfloat16, device="cuda")
+    for t in range(ntok):
+        gpu_lib.moe_layer_decode(layer, lg_d[t], x_d[t:t + 1], k, ids[t], w[t], out[t:t + 1], ws)
+    torch.cuda.synchronize()
+    assert _err_word(gpu_lib, ws, Is, k, True) == 0
+    oids, ow = O.route(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.max(np.abs(w.cpu().numpy() - ow)) <= 1e-6
+    got = to_f64(out)
+    for t in range(ntok):
+        x64 = O.bf16_bits_to_f64(xs[t:t + 1])[0]
+        ys = np.stack([O.expert_mlp(x64, *O.expert_weights(bank[int(e)], H, Is)) for e in oids[t]])
+        ref = O.combine(ys, ow[t], O.expert_mlp(x64, *O.expert_weights(shared, H, Is)))
+        err = max_rel(got[t], ref)
+        log(f"  token {t}: max-rel {err:.3e}")
+        assert err <= TOL_BF16_MAX_REL, (t, err)
+
+
+def test_tp_share_single_launch_graph_replays(gpu_lib):
+    """Four single-launch calls of share 2/8 captured in a HIP graph and
+    replayed three times with eager calls on the same workspace between the
+    replays: every replay equals the eager result bit for bit."""
+    import torch
+    from tests.gpu_util import bf16_dev
+    st = _wide_bank()
+    H, I, E, k, G, g = 4096, 2048, 24, 8, 8, 2
+    bank_d, shared_d = dev(st["bank"]), dev(st["shared"][None, :])
+    sb, ss = _share_bank(gpu_lib, bank_d, H, I, G, g), _share_bank(gpu_lib, shared_d, H, I, G, g)
+    layer = gpu_lib.make_layer(H, I // G, fp4_base=sb, fp4_stride=sb.shape[1], num_slots=E, shared=ss[0],
+                               flags=gpu_lib.MOE_LAYER_SINGLE_LAUNCH)
+    ws = gpu_lib.expert_workspace(H, I // G, 1, k, True)
+    steps = 4
+    lg_d = dev(W.router_logits(77, (1,), steps, E))
+    x_d = bf16_dev(W.bf16_normal(77, (2,), (steps, H)))
+    ids = torch.empty((steps, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((steps, k), dtype=torch.float32, device="cuda")
+    ref = torch.empty((steps, H), dtype=torch.bfloat16, device="cuda")
+    for s in range(steps):
+        gpu_lib.moe_layer_decode(layer, lg_d[s], x_d[s:s + 1], k, ids[s], w[s], ref[s:s + 1], ws)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(ref)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(gr, stream=stream):
+            for s in range(steps):
+                gpu_lib.moe_layer_decode(layer, lg_d[s], x_d[s:s + 1], k, ids[s], w[s], out[s:s + 1], ws)
+    torch.cuda.current_stream().wait_stream(stream)
+    scratch = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+    for rep in range(3):
+        out.zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
+        gpu_lib.moe_layer_decode(layer, lg_d[rep], x_d[rep:rep + 1], k, ids[rep], w[rep], scratch, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(scratch, ref[rep:rep + 1]), rep
+    assert _err_word(gpu_lib, ws, I // G, k, True) == 0
