@@ -142,10 +142,10 @@ moe_status moe_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int
 /* Workspace bytes moe_expert_forward and moe_layer_decode need for T tokens,
  * top-k, with or without the shared expert.
  * The last part of the workspace, from moe_expert_workspace_sync_offset(...)
- * on, holds words that the single-launch batch-1 step keeps from one call to
- * the next (a completion flag per workgroup carrying a call tag, then an error
- * word).  Zero the whole workspace once after allocating it; after that the
- * library keeps those words consistent itself.  Calls that may run at the same
+ * on, holds words that the single-launch batch-1 steps keep from one call to
+ * the next (a call tag per workgroup, an error word, arrival counters).  Zero
+ * the whole workspace once after allocating it; after that the library keeps
+ * those words consistent itself.  Calls that may run at the same
  * time (on different streams) must use different workspaces.  The error word
  * (the uint32 at sync offset + 1024) becomes nonzero only if a call's
  * cross-workgroup wait gave up, which happens only when the device could not
@@ -182,7 +182,8 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x, moe_dtype x
  * kernel and the layer is two launches; the same holds for the narrow experts
  * of a tensor-parallel share (H in {2048, 4096}, I in {256, 512, 1024}, k +
  * has_shared <= 12); otherwise moe_route then moe_expert_forward run.  With MOE_LAYER_SINGLE_LAUNCH in layer->flags, at
- * H = 4096, I = 2048, k + has_shared <= 9, on a device of at least 256 CUs,
+ * H = 4096 with I = 2048 (the full expert) or I = 256 (a 1/8 tensor-parallel
+ * share), k + has_shared <= 9, on a device of at least 256 CUs,
  * the whole step (routing, gate/up, down and combine) is ONE launch whose
  * workgroups hand the SwiGLU outputs to each other through the workspace;
  * moe_expert_forward at T = 1 with prec NULL takes the same single launch
