@@ -5,10 +5,12 @@ caller's workspace, through the C ABI.
 Both entry points run the same kernels in the same order, so the routing ids,
 weights and outputs must agree bit for bit.  Calls follow each other with no
 synchronisation, as a serving loop makes them: a call at the model shape
-(H 4096, I 2048, top-8 + shared), then a smaller one (H 2048, I 1024, top-4,
-no shared expert) that rewrites the scratch, then the model shape again; once
-with the two-launch step and once with the single launch, whose per-workgroup
-flags the scratch keeps from call to call."""
+(H 4096, I 2048, top-8 + shared), one on a 1/8 tensor-parallel share
+(I 256), a smaller one (H 2048, I 1024, top-4, no shared expert) that
+rewrites the scratch, the share again, then the model shape again; once with
+the two-launch steps and once with the single launches (both the full-width
+and the share's kernel), whose tags and arrival counters the scratch keeps
+from call to call and from one kernel to the other."""
 import numpy as np
 import pytest
 
@@ -48,8 +50,9 @@ def _run(gpu_lib, c, flags, noalloc):
 def test_noalloc_matches_layer_decode_big_small_big(gpu_lib, flags):
     import torch
     big = _case(4096, 2048, 24, 8, True, 10)
+    share = _case(4096, 256, 24, 8, True, 30)
     small = _case(2048, 1024, 16, 4, False, 20)
-    seq = [("big", big), ("small", small), ("big", big)]
+    seq = [("big", big), ("share", share), ("small", small), ("share", share), ("big", big)]
     got = []
     for name, c in seq:
         log(f"noalloc: {name} H {c['H']} I {c['I']} E {c['E']} k {c['k']} flags {flags}")
