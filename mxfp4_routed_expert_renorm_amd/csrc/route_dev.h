@@ -28,28 +28,32 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
 }
 
-// wavefront maximum / minimum of an unsigned value, returned uniformly: DPP
-// lane moves (butterflies in quads, mirrors in rows of 16, then row
-// broadcasts), lanes without a source contribute the identity
+// wavefront maximum / minimum of an unsigned value, in every lane: DPP lane
+// moves within each row of 16 (butterflies in quads, then the mirrors), then
+// gfx950's permlane swaps across row pairs and across the two halves.
+// Nothing goes through a scalar register, so a selection round has no
+// vector-to-scalar round trip.
 template <bool MAX>
 __device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
-  constexpr int id = MAX ? 0 : -1;
-  auto step = [&](uint32_t w) { return MAX ? (w > v ? w : v) : (w < v ? w : v); };
-  v = step((uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, dpp::kQuadXor1, 0xF, 0xF, false));
-  v = step((uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, dpp::kQuadXor2, 0xF, 0xF, false));
-  v = step((uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, dpp::kRowHalfMirror, 0xF, 0xF, false));
-  v = step((uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, dpp::kRowMirror, 0xF, 0xF, false));
-  v = step((uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, dpp::kRowBcast15, 0xA, 0xF, false));
-  v = step((uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, dpp::kRowBcast31, 0xC, 0xF, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  auto step = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, dpp::kQuadXor1, 0xF, 0xF, false));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, dpp::kQuadXor2, 0xF, 0xF, false));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, dpp::kRowHalfMirror, 0xF, 0xF, false));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, dpp::kRowMirror, 0xF, 0xF, false));
+  // every lane now holds its row's result; rows 2j and 2j+1 swap (p[0] the
+  // even row's, p[1] the odd row's), then the halves (q[0] the low half's)
+  const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = step(p[0], p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return step(q[0], q[1]);
 }
 
 // Route one token's logits row [E] with the whole wavefront: on return lane
 // r < k holds the r-th selected expert and its renormalised weight (other
 // lanes: expert 0, weight 0).  Every lane must call it (DPP and readlane).
-// Each round takes the wavefront maximum of the 32-bit images; among the
-// positions holding it the lowest expert id wins (a ballot settles the
-// common single-holder case, a wavefront minimum over ids the rest).
+// Each round takes the wavefront maximum of the 32-bit images, then the
+// wavefront minimum of the expert ids holding it (the lowest id wins a tie),
+// both left in every lane.
 // The two halves of route_wave, for callers that issue other loads between
 // the logits loads and the selection: lane l loads experts l + 64 j.
 template <int EPL>
@@ -88,12 +92,7 @@ __device__ __forceinline__ void route_select(const float (&lv)[EPL], int E, int 
     uint32_t cid = 0xffffffffu;  // this lane's lowest expert id holding m
 #pragma unroll
     for (int j = EPL - 1; j >= 0; --j) cid = key[j] == m ? (uint32_t)(lane + 64 * j) : cid;
-    const uint64_t holders = __ballot(cid != 0xffffffffu);
-    uint32_t win;
-    if (__popcll(holders) == 1)
-      win = (uint32_t)__builtin_amdgcn_readlane((int)cid, __builtin_ctzll(holders));
-    else
-      win = wave_ext_u32<false>(cid);
+    const uint32_t win = wave_ext_u32<false>(cid);
 #pragma unroll
     for (int j = 0; j < EPL; ++j) key[j] = (uint32_t)(lane + 64 * j) == win ? 0u : key[j];
     if (lane == r) {
