@@ -109,6 +109,13 @@ def test_single_launch_top6(gpu_lib):
     _decode_tokens(gpu_lib, gpu_lib.MOE_LAYER_SINGLE_LAUNCH, steps=(5, 6), k=6)
 
 
+@pytest.mark.parametrize("k", [3, 1])
+def test_single_launch_small_k(gpu_lib, k):
+    """k = 3 and k = 1 (four and two groups: the 4-group batch of the single
+    launch, most of its slots repeating the last group)."""
+    _decode_tokens(gpu_lib, gpu_lib.MOE_LAYER_SINGLE_LAUNCH, steps=(7, 8), k=k)
+
+
 @pytest.mark.parametrize("with_shared", [True, False])
 def test_single_launch_given_ids_with_drops(gpu_lib, with_shared):
     """moe_expert_forward at T = 1 from given slot ids and weights: invalid

@@ -198,10 +198,10 @@ def _err_word(gpu_lib, ws, Is, k, with_shared):
     return int(ws[off + 1024:off + 1028].cpu().numpy().view(np.uint32)[0])
 
 
-@pytest.mark.parametrize("g,k", [(0, 8), (5, 8), (3, 6), (7, 3)])
+@pytest.mark.parametrize("g,k", [(0, 8), (5, 8), (3, 6), (7, 3), (2, 1)])
 def test_tp_share_single_launch_decode(gpu_lib, g, k):
     """moe_layer_decode on share g of 8 in one launch, k ranks plus the shared
-    expert (9, 7 and 4 groups: each batch size of the kernel): routing equal to
+    expert (9, 7, 4 and 2 groups: each batch size of the kernel): routing equal to
     the oracle's, outputs the oracle's partial sums, error word zero."""
     import torch
     from tests.gpu_util import TOL_BF16_MAX_REL, bf16_dev, max_rel, to_f64
