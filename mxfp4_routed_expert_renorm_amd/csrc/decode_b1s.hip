@@ -12,9 +12,11 @@
 // gateup_b1s_kernel: SPL wavefronts share one gate/up row, each taking H/SPL
 //   of its reduction (EL elements per lane, 8 or 16 FP4 bytes), so the grid
 //   has I * SPL / 4 workgroups.  Each wavefront routes the token itself from
-//   the logits row, requests its slice of the row of every selected expert
-//   up front, reduces its partial sums, and the row's first wavefront adds
-//   the SPL partials in wavefront order and applies SwiGLU.
+//   the logits row, requesting its slice of each selected expert's row right
+//   after the round that picks it (at this width the step is a chain of
+//   trips, so the rounds overlap the first rows' trips), reduces its partial
+//   sums, and the row's first wavefront adds the SPL partials in wavefront
+//   order and applies SwiGLU.
 //
 // down_b1s_kernel: LPR = I / 32 lanes per output row, one 32-element chunk
 //   (16 FP4 bytes, one scale) per lane, so a wavefront covers 64 / LPR output
@@ -125,26 +127,40 @@ __global__ __launch_bounds__(256) void gateup_b1s_kernel(B1SArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (SH) issue(sl[0], a.shared);
 
-  // 2. the token's ranks (routed here when logits are given)
+  // 2. the token's ranks.  Routed here when logits are given: the experts are
+  // the slots (every pick is valid), and each rank's slice is requested as
+  // soon as its round picks it, so the selection overlaps the first rows'
+  // trips; batch slots past the k ranks repeat rank k-1 and are not stored.
+  // With given ids the valid ranks are listed first, then requested.
+  int kx[NB];
+  if constexpr (SH) kx[0] = k;
+  int nact;
   if constexpr (EPL > 0) {
     float my_w;
-    route_select<EPL>(lv, a.E, k, &my_slot, &my_w);
+    route_select_each<EPL, NB - S0>(lv, a.E, k, &my_slot, &my_w, [&](auto rc, uint32_t e) {
+      constexpr int r = decltype(rc)::value;
+      issue(sl[S0 + r], a.fp4_base + (size_t)e * a.fp4_stride);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     if (blockIdx.x == 0 && wave == 0 && lane < k) {
       a.slot_ids[lane] = my_slot;
       a.w[lane] = my_w;
     }
-  }
-  const uint64_t m = __ballot(lane < k && my_slot >= 0 && my_slot < a.num_slots);
-  const int nf = __popcll(m);
-  const int nact = S0 + nf;
-  int kx[NB];
-  if constexpr (SH) kx[0] = k;
 #pragma unroll
-  for (int u = S0; u < NB; ++u) {  // batch slots past the active groups repeat the last one and are not stored
-    const int r = nf > 0 ? nth_set_bit(m, min(u - S0, nf - 1)) : -1;
-    kx[u] = r;
-    const uint8_t* rec = r >= 0 ? a.fp4_base + (size_t)__builtin_amdgcn_readlane(my_slot, r) * a.fp4_stride : a.shared;
-    if (rec) issue(sl[u], rec);
+    for (int u = S0; u < NB; ++u) kx[u] = min(u - S0, k - 1);
+    nact = S0 + k;
+  } else {
+    const uint64_t m = __ballot(lane < k && my_slot >= 0 && my_slot < a.num_slots);
+    const int nf = __popcll(m);
+    nact = S0 + nf;
+#pragma unroll
+    for (int u = S0; u < NB; ++u) {  // batch slots past the active groups repeat the last one and are not stored
+      const int r = nf > 0 ? nth_set_bit(m, min(u - S0, nf - 1)) : -1;
+      kx[u] = r;
+      const uint8_t* rec =
+          r >= 0 ? a.fp4_base + (size_t)__builtin_amdgcn_readlane(my_slot, r) * a.fp4_stride : a.shared;
+      if (rec) issue(sl[u], rec);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // every load above is out before the first slice is consumed
 

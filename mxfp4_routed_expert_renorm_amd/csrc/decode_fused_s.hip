@@ -114,8 +114,16 @@ __global__ __launch_bounds__(256, 1) void fused_b1s_kernel(FusedSArgs a) {
   const uint8_t* rec0 = SH ? a.shared : a.fp4_base;
   if constexpr (SH) issue_gu(0, a.shared);
 
-  // 2. the token's ranks: every wavefront routes (or reads) them itself
-  if constexpr (EPL > 0) route_select<EPL>(lv, a.E, k, &my_slot, &my_w);
+  // 2. the token's ranks: every wavefront routes (or reads) them itself.
+  // Routed here, each rank's slice is requested as soon as its round picks it
+  // (the experts are the slots, every pick valid; slots past the k ranks
+  // repeat rank k-1); with given ids the valid ranks are listed, then requested.
+  if constexpr (EPL > 0)
+    route_select_each<EPL, NB - S0>(lv, a.E, k, &my_slot, &my_w, [&](auto rc, uint32_t e) {
+      constexpr int r = decltype(rc)::value;
+      issue_gu(S0 + r, a.fp4_base + (size_t)e * a.fp4_stride);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   const bool valid = lane < k && my_slot >= 0 && my_slot < a.num_slots;
   const uint64_t m = __ballot(valid);
   const int nf = __popcll(m), ng = S0 + nf;
@@ -135,8 +143,10 @@ __global__ __launch_bounds__(256, 1) void fused_b1s_kernel(FusedSArgs a) {
     const int r = nth_set_bit(m, g - S0);
     return a.fp4_base + (size_t)__builtin_amdgcn_readlane(my_slot, r) * a.fp4_stride;
   };
+  if constexpr (EPL == 0) {
 #pragma unroll
-  for (int g = S0; g < NB; ++g) issue_gu(g, grec(g));
+    for (int g = S0; g < NB; ++g) issue_gu(g, grec(g));
+  }
 
   // 3. the W2 chunks of this lane's down rows, for its half of the groups
   const int drow = unit * kSRowsDN + 8 * (wave & 1) + (lane >> 3), dc = lane & 7, half = wave >> 1;

@@ -11,6 +11,8 @@
 // over their logits alone, so the full-E denominator is never formed.
 #pragma once
 
+#include <utility>
+
 #include "common.h"
 
 namespace moe {
@@ -73,39 +75,87 @@ __device__ __forceinline__ void route_wave(const float* __restrict__ row, int E,
   route_select<EPL>(v, E, k, my_e, my_w);
 }
 
+// The parts of the selection.  route_keys: the lane's order-preserving images
+// (experts past E hold 0, "no candidate").  route_round: one round — the
+// wavefront maximum m, the lowest expert id holding it (win, in every lane),
+// that candidate removed, and lane r keeping (m, win).  route_finish: the
+// softmax over the k selected logits, lane r < k getting rank r's weight.
 template <int EPL>
-__device__ __forceinline__ void route_select(const float (&lv)[EPL], int E, int k, int* my_e, float* my_w) {
+__device__ __forceinline__ void route_keys(const float (&lv)[EPL], int E, uint32_t (&key)[EPL]) {
   const int lane = threadIdx.x & 63;
-  uint32_t key[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
     key[j] = sel_key(lv[j]) & (0u - (uint32_t)(e < E));  // arithmetic mask: no branch around the load
   }
-  uint32_t kv = 0;  // lane r keeps the r-th selected image
-  int ee = 0;
-  for (int r = 0; r < k; ++r) {
-    uint32_t best = key[0];
+}
+
+template <int EPL>
+__device__ __forceinline__ uint32_t route_round(uint32_t (&key)[EPL], int r, uint32_t& kv, int& ee) {
+  const int lane = threadIdx.x & 63;
+  uint32_t best = key[0];
 #pragma unroll
-    for (int j = 1; j < EPL; ++j) best = key[j] > best ? key[j] : best;
-    const uint32_t m = wave_ext_u32<true>(best);
-    uint32_t cid = 0xffffffffu;  // this lane's lowest expert id holding m
+  for (int j = 1; j < EPL; ++j) best = key[j] > best ? key[j] : best;
+  const uint32_t m = wave_ext_u32<true>(best);
+  uint32_t cid = 0xffffffffu;  // this lane's lowest expert id holding m
 #pragma unroll
-    for (int j = EPL - 1; j >= 0; --j) cid = key[j] == m ? (uint32_t)(lane + 64 * j) : cid;
-    const uint32_t win = wave_ext_u32<false>(cid);
+  for (int j = EPL - 1; j >= 0; --j) cid = key[j] == m ? (uint32_t)(lane + 64 * j) : cid;
+  const uint32_t win = wave_ext_u32<false>(cid);
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) key[j] = (uint32_t)(lane + 64 * j) == win ? 0u : key[j];
-    if (lane == r) {
-      kv = m;
-      ee = (int)win;
-    }
+  for (int j = 0; j < EPL; ++j) key[j] = (uint32_t)(lane + 64 * j) == win ? 0u : key[j];
+  if (lane == r) {
+    kv = m;
+    ee = (int)win;
   }
+  return win;
+}
+
+__device__ __forceinline__ void route_finish(uint32_t kv, int ee, int k, int* my_e, float* my_w) {
+  const int lane = threadIdx.x & 63;
   const float v = key_value(kv);
   const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
   const float z = (lane < k) ? expf(v - vmax) : 0.0f;
   const float s = wave_sum(z);
   *my_e = ee;
   *my_w = (lane < k) ? z / s : 0.0f;
+}
+
+template <int EPL>
+__device__ __forceinline__ void route_select(const float (&lv)[EPL], int E, int k, int* my_e, float* my_w) {
+  uint32_t key[EPL];
+  route_keys<EPL>(lv, E, key);
+  uint32_t kv = 0;  // lane r keeps the r-th selected image
+  int ee = 0;
+  for (int r = 0; r < k; ++r) route_round<EPL>(key, r, kv, ee);
+  route_finish(kv, ee, k, my_e, my_w);
+}
+
+// f(std::integral_constant<int, r>()) for r = rs... in order
+template <class F, int... rs>
+__device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int, rs...>) {
+  (f(std::integral_constant<int, rs>()), ...);
+}
+
+// route_select with the rounds unrolled to R >= k and a call after each one,
+// for a caller that requests each rank's data as soon as its round picks it:
+// on_pick(std::integral_constant<int, r>(), e) with e the rank-r expert,
+// wavefront-uniform; the rounds past k pass rank k-1's expert again, so the
+// caller issues the same number of requests whatever k is.
+template <int EPL, int R, class OnPick>
+__device__ __forceinline__ void route_select_each(const float (&lv)[EPL], int E, int k, int* my_e, float* my_w,
+                                                  OnPick&& on_pick) {
+  uint32_t key[EPL];
+  route_keys<EPL>(lv, E, key);
+  uint32_t kv = 0;
+  int ee = 0;
+  uint32_t last = 0;
+  auto round = [&](auto rc) {
+    constexpr int r = decltype(rc)::value;
+    if (r < k) last = __builtin_amdgcn_readfirstlane(route_round<EPL>(key, r, kv, ee));
+    on_pick(rc, last);
+  };
+  for_each_index(round, std::make_integer_sequence<int, R>());
+  route_finish(kv, ee, k, my_e, my_w);
 }
 
 }  // namespace moe
