@@ -526,6 +526,21 @@ def test_layer_decode_shapes(gpu_lib, E, k, with_shared, out_f32):
     _layer_decode_case(gpu_lib, E, 2048, 2048, k, with_shared, seed=90 + E + k, out_f32=out_f32)
 
 
+@pytest.mark.parametrize("H,I,E,k,with_shared", [
+    (2048, 256, 64, 8, True),      # H 2048, I 256: two wavefronts per gate/up row
+    (2048, 512, 100, 6, True),     # one wavefront per row; E not a multiple of 64
+    (2048, 1024, 300, 4, False),   # 16 logits per lane, no shared expert
+    (4096, 512, 64, 11, True),     # 12 groups: the largest batch of the narrow kernels
+    (4096, 1024, 64, 1, True),     # k = 1
+])
+def test_layer_decode_narrow_experts(gpu_lib, H, I, E, k, with_shared):
+    """Tensor-parallel-share widths (the narrow-expert batch-1 kernels):
+    routing inside the gate/up launch, each rank's slice requested right after
+    the round that picks it, equal bit for bit to moe_route + moe_expert_forward
+    from the same ids and within tolerance of the oracle."""
+    _layer_decode_case(gpu_lib, E, H, I, k, with_shared, seed=97 + H // 1024 + I // 256 + k)
+
+
 def test_layer_decode_generic_shape(gpu_lib):
     """A shape outside the batch-1 kernels (H 512) runs moe_route then the
     generic expert kernels; same contract."""
