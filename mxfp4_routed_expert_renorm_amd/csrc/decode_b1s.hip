@@ -204,6 +204,23 @@ __global__ __launch_bounds__(256) void gateup_b1s_kernel(B1SArgs a) {
   if (lane < nact) a.h[(size_t)kv * I + row] = f32_to_bf16(silu_mul_b1(gv, uv));
 }
 
+// sum over each aligned group of N = 8, 16 or 32 lanes, in every lane of the
+// group, on DPP lane moves (quad butterflies, the mirrors within 8 and 16
+// lanes) and, for 32, the swap of row pairs: no LDS round trips
+template <int N>
+__device__ __forceinline__ float lanes_sum(float v) {
+  static_assert(N == 8 || N == 16 || N == 32, "8, 16 or 32 lanes");
+  v += dpp_f32<dpp::kQuadXor1>(v);
+  v += dpp_f32<dpp::kQuadXor2>(v);
+  v += dpp_f32<dpp::kRowHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f32<dpp::kRowMirror>(v);
+  if constexpr (N == 32) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  return v;
+}
+
 template <int LPR, int NB, bool SH>
 __global__ __launch_bounds__(256) void down_b1s_kernel(B1SArgs a) {
   static_assert(LPR == 8 || LPR == 16 || LPR == 32, "I is 256, 512 or 1024");
@@ -291,7 +308,7 @@ __global__ __launch_bounds__(256) void down_b1s_kernel(B1SArgs a) {
     }
   }
   if constexpr (SH) acc += part_of(0);
-  const float v = group_sum<LPR>(acc);
+  const float v = lanes_sum<LPR>(acc);
   if (c == 0) ((uint16_t*)a.out)[orow] = f32_to_bf16(v);
 }
 
