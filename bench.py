@@ -591,6 +591,7 @@ def bench_prefill(args):
         "gemm_weight_GBps": round(wbytes / gemm_s / 1e9, 1),
         "gemm_weight_hbm_frac": round(wbytes / gemm_s / 1e9 / HBM_PEAK_GBPS, 4),
         "kernel_avg_us": kus,
+        "kernel_us_per_step": {n: round(v[0] / K * 1e3, 3) for n, v in prof.items()},
     }
     print(json.dumps(result), flush=True)
 

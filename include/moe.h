@@ -137,6 +137,18 @@ moe_status moe_route(const float* logits, int T, int E, int k, int32_t* ids, flo
 moe_status moe_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int32_t* offsets,
                      int32_t* perm, moe_stream_t stream);
 
+/* moe_group spread over many workgroups, for tens of thousands of keys: each
+ * 512-key chunk is counted into its own histogram, one workgroup scans the
+ * histograms per key, then each chunk places its keys in input order.  Same
+ * result as moe_group, bit for bit.  scratch: device, 4-byte aligned, at
+ * least moe_group_scratch_bytes(n, nkeys) bytes (the chunks' histograms;
+ * caller-owned, rewritten by every call).  When that is 0 (n <= 2048 or
+ * nkeys > 1024) moe_group's one-workgroup grouping runs and scratch may be
+ * NULL.  Limits and errors as moe_group. */
+size_t moe_group_scratch_bytes(int n, int nkeys);
+moe_status moe_group_wide(const int32_t* keys, int n, int nkeys, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, void* scratch, moe_stream_t stream);
+
 /* ------------------------------------------------------------ expert MLP */
 
 /* Workspace bytes moe_expert_forward and moe_layer_decode need for T tokens,

@@ -70,6 +70,8 @@ _SIGS = {
     "moe_router_logits": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p]),
     "moe_route": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "moe_group": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_group_scratch_bytes": (c_size_t, [c_int, c_int]),
+    "moe_group_wide": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_expert_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "moe_expert_workspace_sync_offset": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "moe_expert_forward": (c_int, [ctypes.POINTER(moe_layer), c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
@@ -207,6 +209,17 @@ def moe_route(logits, k, ids, w, stream=None):
 def moe_group(keys, nkeys, counts, offsets, perm, stream=None):
     n = keys.numel()
     _check("moe_group", load().moe_group(_p(keys), n, nkeys, _p(counts), _p(offsets), _p(perm), _stream(stream)))
+    return counts, offsets, perm
+
+
+def moe_group_scratch_bytes(n, nkeys):
+    return load().moe_group_scratch_bytes(n, nkeys)
+
+
+def moe_group_wide(keys, nkeys, counts, offsets, perm, scratch, stream=None):
+    n = keys.numel()
+    _check("moe_group_wide", load().moe_group_wide(_p(keys), n, nkeys, _p(counts), _p(offsets), _p(perm),
+                                                   _p(scratch), _stream(stream)))
     return counts, offsets, perm
 
 

@@ -44,6 +44,9 @@ moe_status launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hip
 bool decode_shape_ok(int H, int I);
 size_t prefill_workspace_bytes(int H, int I, int T, int k, int has_shared);
 moe_status launch_quant_mxfp8(const void* x, long rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s);
+size_t group_wide_scratch_ints(int n, int nkeys);
+moe_status launch_group_wide(const int32_t* keys, int n, int nkeys, int32_t* counts, int32_t* offsets,
+                             int32_t* perm, int32_t* scratch, hipStream_t s);
 moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int k, const int32_t* ids, const float* w,
                           void* out, void* workspace, hipStream_t s);
 bool b1_path_ok(int H, int I, int K1, bool xbf16, bool obf16);
@@ -118,6 +121,22 @@ moe_status moe_group(const int32_t* keys, int n, int nkeys, int32_t* counts, int
   REQUIRE(nkeys >= 1 && nkeys <= 4096, MOE_ESHAPE, "moe_group: nkeys=%d outside 1..4096", nkeys);
   REQUIRE(counts && offsets && (n == 0 || (keys && perm)), MOE_EINVAL, "moe_group: NULL pointer");
   return launch_group(keys, n, nkeys, counts, offsets, perm, (hipStream_t)stream);
+}
+
+size_t moe_group_scratch_bytes(int n, int nkeys) {
+  if (n < 0 || n > (1 << 20) || nkeys < 1 || nkeys > 4096) return 0;
+  return group_wide_scratch_ints(n, nkeys) * sizeof(int32_t);
+}
+
+moe_status moe_group_wide(const int32_t* keys, int n, int nkeys, int32_t* counts, int32_t* offsets, int32_t* perm,
+                          void* scratch, moe_stream_t stream) {
+  REQUIRE(n >= 0 && n <= (1 << 20), MOE_ESHAPE, "moe_group_wide: n=%d outside 0..2^20", n);
+  REQUIRE(nkeys >= 1 && nkeys <= 4096, MOE_ESHAPE, "moe_group_wide: nkeys=%d outside 1..4096", nkeys);
+  REQUIRE(counts && offsets && (n == 0 || (keys && perm)), MOE_EINVAL, "moe_group_wide: NULL pointer");
+  REQUIRE(group_wide_scratch_ints(n, nkeys) == 0 || (scratch && aligned(scratch, 4)), MOE_EINVAL,
+          "moe_group_wide: scratch is NULL or not 4-byte aligned (%zu bytes needed)",
+          group_wide_scratch_ints(n, nkeys) * sizeof(int32_t));
+  return launch_group_wide(keys, n, nkeys, counts, offsets, perm, (int32_t*)scratch, (hipStream_t)stream);
 }
 
 size_t moe_expert_workspace_sync_offset(int H, int I, int T, int k, int has_shared) {

@@ -905,6 +905,10 @@ PrefillWs prefill_ws_layout(int H, int I, int T, int K1) {
 
 }  // namespace
 
+size_t group_wide_scratch_ints(int n, int nkeys);
+moe_status launch_group_wide(const int32_t* keys, int n, int nkeys, int32_t* counts, int32_t* offsets,
+                             int32_t* perm, int32_t* scratch, hipStream_t s);
+
 size_t prefill_workspace_bytes(int H, int I, int T, int k, int has_shared) {
   return prefill_ws_layout(H, I, T, k + (has_shared ? 1 : 0)).total;
 }
@@ -953,7 +957,11 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
     launch(MOE_PROF_PLAN, prefill_keys_kernel, dim3((P + 255) / 256), dim3(256), 0, s, a);
     MOE_LAUNCH_CHECK();
   }
-  st = launch_group(a.keys, P, E + 1, a.counts, a.offsets, a.perm, s);
+  // tens of thousands of pairs group over many workgroups; h's region is free
+  // until the gate/up GEMM and holds their per-chunk histograms
+  if (group_wide_scratch_ints(P, E + 1) * 4 > lay.hs - lay.hq)
+    return fail(MOE_EINVAL, "moe_prefill_forward: grouping scratch exceeds the h region");
+  st = launch_group_wide(a.keys, P, E + 1, a.counts, a.offsets, a.perm, (int32_t*)(ws + lay.hq), s);
   if (st != MOE_OK) return st;
   {
     launch(MOE_PROF_PLAN, prefill_items_kernel<kMT>, dim3(1), dim3(64), 0, s, a.counts, a.offsets, E + 1, a.items);

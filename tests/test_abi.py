@@ -91,6 +91,18 @@ def test_group_validation(lib):
     assert st == 2
 
 
+def test_group_wide_validation(lib):
+    assert lib.moe_group_scratch_bytes(2048, 257) == 0          # small: the one-workgroup grouping
+    assert lib.moe_group_scratch_bytes(36864, 257) == 72 * 257 * 4
+    assert lib.moe_group_scratch_bytes(36864, 2000) == 0        # many keys: the one-workgroup grouping
+    st, msg = _status(lib, "moe_group_wide", FAKE, 36864, 257, FAKE, FAKE, FAKE, None, None)
+    assert st == 1 and "scratch" in msg
+    st, msg = _status(lib, "moe_group_wide", FAKE, 36864, 257, FAKE, FAKE, FAKE, 0x1002, None)
+    assert st == 1 and "aligned" in msg
+    st, msg = _status(lib, "moe_group_wide", FAKE, -1, 257, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == 2
+
+
 def test_expert_forward_validation(lib):
     good = B.moe_layer(256, 128, 0x1000, lib.moe_fp4_expert_bytes(256, 128), 8, None, 0, 0, None)
     ws = lib.moe_expert_workspace_bytes(256, 128, 4, 2, 0)

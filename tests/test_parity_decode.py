@@ -202,6 +202,39 @@ def test_group_skips_out_of_range_keys(gpu_lib):
     assert np.array_equal(perm.cpu().numpy(), pos[op])
 
 
+def test_group_wide_bit_exact(gpu_lib):
+    """The many-workgroup grouping (per-chunk histograms in scratch) gives the
+    one-workgroup grouping's counts, offsets and permutation bit for bit,
+    at prefill sizes, ragged tails and with out-of-range keys skipped."""
+    torch = _torch()
+    rng = np.random.default_rng(19)
+    for n, nk, lo in [(2049, 257, 0), (36864, 257, 0), (100000, 257, 0), (70001, 1000, 0), (5000, 1024, 0),
+                      (36864, 257, -5), (4096, 1, 0), (36864, 2000, 0)]:
+        keys = rng.integers(lo, nk, n).astype(np.int32)
+        valid = (keys >= 0) & (keys < nk)
+        nv = int(valid.sum())
+        sb = gpu_lib.moe_group_scratch_bytes(n, nk)
+        assert sb == (0 if nk > 1024 else -(-n // 512) * nk * 4)
+        scratch = torch.empty(max(sb // 4, 1), dtype=torch.int32, device="cuda")
+        outs = []
+        for wide in (True, False):
+            counts = torch.full((nk,), -7, dtype=torch.int32, device="cuda")
+            offsets = torch.full((nk + 1,), -7, dtype=torch.int32, device="cuda")
+            perm = torch.full((nv,), -1, dtype=torch.int32, device="cuda")
+            if wide:
+                gpu_lib.moe_group_wide(dev(keys), nk, counts, offsets, perm, scratch)
+            else:
+                gpu_lib.moe_group(dev(keys), nk, counts, offsets, perm)
+            torch.cuda.synchronize()
+            outs.append([t.cpu().numpy() for t in (counts, offsets, perm)])
+        pos = np.nonzero(valid)[0]
+        oc, oo, op = O.group_pairs(keys[valid], nk)
+        for c, o, pm in outs:
+            assert np.array_equal(c, oc), (n, nk)
+            assert np.array_equal(o, oo), (n, nk)
+            assert np.array_equal(pm, pos[op]), (n, nk)
+
+
 def test_dequant_fp4_scaled_convert_bit_exact_all_codes_all_scales(gpu_lib):
     """The decode of the batch-1, single-launch and batched-decode kernels:
     the scaled FP4-to-bf16 convert with the E8M0 scale as its operand, for
