@@ -855,7 +855,11 @@ __global__ __launch_bounds__(kDThreads) void dgemm_kernel(PrefillArgs a) {
   }
 }
 
-// out[t] = sum_{r<k} w[t][r] * y[t][r] (+ y[t][k]), y bf16, rank order, one rounding
+// out[t] = sum_{r<k} w[t][r] * y[t][r] (+ y[t][k]), y bf16, rank order, one
+// rounding.  NK1 > 0: at most NK1 batch slots, every rank's load issued
+// before the first is used (a thread's loads would otherwise go out one
+// rank at a time); NK1 = 0: any K1.
+template <int NK1>
 __global__ __launch_bounds__(256) void combine_bf16y_kernel(const uint16_t* __restrict__ y, const float* __restrict__ w,
                                                             int T, int k, int K1, int H, uint16_t* __restrict__ out) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
@@ -863,15 +867,29 @@ __global__ __launch_bounds__(256) void combine_bf16y_kernel(const uint16_t* __re
   if (idx >= (long)T * oct) return;
   const int t = (int)(idx / oct), j = (int)(idx % oct) * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r = 0; r < K1; ++r) {
-    const uint4 v = *(const uint4*)(y + ((size_t)t * K1 + r) * H + j);
-    const float wr = r < k ? w[(size_t)t * k + r] : 1.0f;
+  auto add = [&](const uint4 v, float wr) {
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       acc[2 * q] = fmaf(wr, bf16_lo(d[q]), acc[2 * q]);
       acc[2 * q + 1] = fmaf(wr, bf16_hi(d[q]), acc[2 * q + 1]);
     }
+  };
+  if constexpr (NK1 > 0) {
+    uint4 v[NK1];
+    float wr[NK1];
+#pragma unroll
+    for (int r = 0; r < NK1; ++r) {  // unconditional (clamped) loads: a fixed count in flight
+      const int rr = min(r, K1 - 1);
+      v[r] = ld_stream16((const uint8_t*)(y + ((size_t)t * K1 + rr) * H + j));
+      wr[r] = w[(size_t)t * k + min(r, k - 1)];
+    }
+#pragma unroll
+    for (int r = 0; r < NK1; ++r)
+      if (r < K1) add(v[r], r < k ? wr[r] : 1.0f);
+  } else {
+    for (int r = 0; r < K1; ++r)
+      add(*(const uint4*)(y + ((size_t)t * K1 + r) * H + j), r < k ? w[(size_t)t * k + r] : 1.0f);
   }
   uint32_t o[4];
 #pragma unroll
@@ -982,8 +1000,15 @@ moe_status launch_prefill(const moe_layer* Lr, int E, const void* x, int T, int 
   }
   {
     const long n = (long)T * (H / 8);
-    launch(MOE_PROF_COMBINE, combine_bf16y_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, w, T, k, K1,
-                       H, (uint16_t*)out);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (K1 <= 5)
+      launch(MOE_PROF_COMBINE, combine_bf16y_kernel<5>, grid, dim3(256), 0, s, a.y, w, T, k, K1, H, (uint16_t*)out);
+    else if (K1 <= 9)
+      launch(MOE_PROF_COMBINE, combine_bf16y_kernel<9>, grid, dim3(256), 0, s, a.y, w, T, k, K1, H, (uint16_t*)out);
+    else if (K1 <= 17)
+      launch(MOE_PROF_COMBINE, combine_bf16y_kernel<17>, grid, dim3(256), 0, s, a.y, w, T, k, K1, H, (uint16_t*)out);
+    else
+      launch(MOE_PROF_COMBINE, combine_bf16y_kernel<0>, grid, dim3(256), 0, s, a.y, w, T, k, K1, H, (uint16_t*)out);
     MOE_LAUNCH_CHECK();
   }
   return MOE_OK;
