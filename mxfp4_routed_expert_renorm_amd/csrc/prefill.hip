@@ -78,36 +78,33 @@ __device__ __forceinline__ int mx_shared_exp(float amax) {
 }
 
 // one thread per 32-element block of a bf16 row-major [rows][K] matrix
+// four lanes per 32-element block, eight elements each: a wavefront's loads
+// cover 1 KiB of contiguous activations; the block's maximum meets over the
+// quad by two DPP steps (a maximum does not depend on the order)
 __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __restrict__ x, long nblk,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
-  const long b = (long)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblk) return;
-  const uint4* src = (const uint4*)(x + b * 32);
-  float v[32];
+  const long i8 = (long)blockIdx.x * 256 + threadIdx.x;  // this lane's 8 elements
+  const long b = i8 >> 2;
+  if (b >= nblk) return;  // whole quads only: a quad shares b
+  const uint4 q = *(const uint4*)(x + i8 * 8);
+  const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+  float v[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 q = src[i];
-    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[8 * i + 2 * j] = bf16_lo(d[j]);
-      v[8 * i + 2 * j + 1] = bf16_hi(d[j]);
-    }
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = bf16_lo(d[j]);
+    v[2 * j + 1] = bf16_hi(d[j]);
   }
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, dpp_f32<dpp::kQuadXor1>(amax));
+  amax = fmaxf(amax, dpp_f32<dpp::kQuadXor2>(amax));
   const int sh = mx_shared_exp(amax);
-  uint32_t out[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    out[i] = e4m3_encode4(ldexpf(v[4 * i], -sh), ldexpf(v[4 * i + 1], -sh), ldexpf(v[4 * i + 2], -sh),
-                          ldexpf(v[4 * i + 3], -sh));
-  uint4* dst = (uint4*)(codes + b * 32);
-  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-  scales[b] = (uint8_t)(sh + 127);
+  const uint32_t o0 = e4m3_encode4(ldexpf(v[0], -sh), ldexpf(v[1], -sh), ldexpf(v[2], -sh), ldexpf(v[3], -sh));
+  const uint32_t o1 = e4m3_encode4(ldexpf(v[4], -sh), ldexpf(v[5], -sh), ldexpf(v[6], -sh), ldexpf(v[7], -sh));
+  *(uint2*)(codes + i8 * 8) = make_uint2(o0, o1);
+  if ((i8 & 3) == 0) scales[b] = (uint8_t)(sh + 127);
 }
 
 // ------------------------------------------------------------------ planning
@@ -934,8 +931,8 @@ size_t prefill_workspace_bytes(int H, int I, int T, int k, int has_shared) {
 moe_status launch_quant_mxfp8(const void* x, long rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s) {
   const long nblk = rows * (K / 32);
   if (nblk == 0) return MOE_OK;
-  launch(MOE_PROF_QUANT, quant_mxfp8_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, (const uint16_t*)x,
-                     nblk, codes, scales);
+  launch(MOE_PROF_QUANT, quant_mxfp8_kernel, dim3((unsigned)((4 * nblk + 255) / 256)), dim3(256), 0, s,
+         (const uint16_t*)x, nblk, codes, scales);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
