@@ -209,7 +209,7 @@ def test_group_wide_bit_exact(gpu_lib):
     torch = _torch()
     rng = np.random.default_rng(19)
     for n, nk, lo in [(2049, 257, 0), (36864, 257, 0), (100000, 257, 0), (70001, 1000, 0), (5000, 1024, 0),
-                      (36864, 257, -5), (4096, 1, 0), (36864, 2000, 0)]:
+                      (36864, 257, -5), (4096, 1, 0), (36864, 2000, 0), (1 << 20, 1024, 0)]:
         keys = rng.integers(lo, nk, n).astype(np.int32)
         valid = (keys >= 0) & (keys < nk)
         nv = int(valid.sum())
