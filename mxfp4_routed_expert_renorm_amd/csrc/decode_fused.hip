@@ -19,21 +19,24 @@
 //     SwiGLU output in LDS; wavefront 0 then publishes the unit's h with
 //     write-through stores and arrives at the handoff below.
 //   - Down unit u: output rows 16u..16u+15 for every group.  Copying
-//     wavefront c (8..15) loads W2 rows 16u+2c', 16u+2c'+1 (c' = c - 8) of
-//     every group and their scale bytes into registers, then moves each
-//     group's pair into LDS as it lands and raises a flag there.  The routed
+//     wavefront c (8..15) requests W2 rows 16u+2c', 16u+2c'+1 (c' = c - 8)
+//     of every group and their scale bytes into registers.  The routed
 //     groups' rows are requested only once every computing wavefront has
 //     requested its last gate/up row, so they queue behind the gate/up
 //     stream and land while the workgroups hand h over.
-//   - The computing wavefronts then wait until every gate/up unit is done,
-//     load h for the (at most two) groups of their down items, and compute
-//     each item (one group's W2 row dotted with its h) once its rows are in
-//     LDS, overlapping the tail of the W2 stream.  Vector loads retire in
-//     issue order, so a wavefront with W2 rows in flight could not use h
-//     loaded after them before every row landed: hence the copying and the
-//     computing wavefronts are distinct.
-//   - The items' results meet in LDS; 16 threads sum each output row over the
-//     groups in rank order (shared expert last, weight 1) and round once.
+//   - Once every unit's h is out, the computing wavefronts copy all of it
+//     into LDS (at most 36 KiB, one request per thread and 8 KiB).  The down
+//     products then split by group: each copying wavefront dots its two rows
+//     of the earlier half of the routed groups and of the shared expert
+//     straight from its registers; the computing wavefront of the same
+//     index takes the same two rows of the later half, whose W2 chunks the
+//     copying wavefronts put in LDS while the units handed h over.  Each
+//     sums its groups per lane (weighted, rank order), one reduction per row;
+//     the copying wavefront adds the two row sums and the shared expert's
+//     (weight 1) and rounds once.  Vector loads retire in issue order, so a
+//     wavefront with W2 rows in flight could not use h it requested after
+//     them before every row had landed: hence h goes through LDS, loaded by
+//     the computing wavefronts, which have nothing in flight by then.
 //
 // Cross-workgroup handoff.  h is written with agent-scope stores, which write
 // through to the device's coherence point; once they have completed (vmcnt 0,
@@ -96,12 +99,15 @@ struct FusedArgs {
   uint32_t* err;        // its error word: bit 0 the handoff gave up, bit 1 a W2 wait did
 };
 
+constexpr int kFHalf = kFMaxG / 2;       // groups whose down rows the computing wavefronts take
+
 struct alignas(16) FusedSmem {
-  uint8_t w2c[kFMaxG][kFRowsDN][kW2Row];  // W2 code rows of the unit, per group
-  uint8_t w2s[kFMaxG][kW2Scales];         // their scale bytes
+  uint8_t w2c[kFHalf][kFRowsDN][kW2Row];  // W2 rows of the later groups, for the computing wavefronts
+  uint8_t w2s[kFHalf][kFRowsDN][kW2RowS]; // their scale bytes
+  uint32_t hb[kFMaxG][kFI / 2];           // every unit's h, bf16 pairs, once the handoff has passed
+  float part[kFRowsDN];                   // the computing wavefronts' sums of those groups, per output row
+  uint32_t stored;                        // copying wavefronts whose later groups' rows are in LDS
   float hrow[kFMaxG][kFRowsGU];           // SwiGLU outputs of the unit's gate/up rows
-  float res[kFMaxG][kFRowsDN];            // down items: group g's W2 row r . h_g
-  uint32_t ready[kFMaxG][kFCopiers];      // group g's W2 row pair c is in LDS
   int gslot[kFMaxG];                      // slot of each routed group
   float gw[kFMaxG];                       // weight of each routed group
   int ng;                                 // groups with work
@@ -134,11 +140,11 @@ struct GURow {
   uint32_t s1[2], s3[2];
 };
 
-// one copying wavefront's share of a group's W2: two code rows and their
-// 128 scale bytes (two per lane)
+// one copying wavefront's share of a group's W2: two code rows and, per
+// lane, the scale byte of its block in each
 struct W2Pair {
   uint4 r0, r1;
-  uint32_t s;
+  uint32_t s0, s1;
 };
 
 template <int NB, int EPL, bool SH, int WIN>
@@ -153,11 +159,35 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
   const RecordLayout L = record_layout(kFH, kFI, 4);
   constexpr size_t kRowB = kFH / 2, kRowS = kFH / 32;  // w1/w3 row: code bytes, scale bytes
 
-  if (tid < kFMaxG * kFCopiers) (&sm.ready[0][0])[tid] = 0u;
   if (tid == 0) {
     sm.issued = 0u;
     sm.go = 0u;
+    sm.stored = 0u;
   }
+  // groups [S0, GS) and the shared expert: the copying wavefronts, from
+  // registers; groups [GS, NB): the computing wavefronts, from LDS
+  constexpr int GS = S0 + (NB - S0 + 1) / 2;
+  static_assert(NB - GS <= kFHalf, "the later groups' rows fit LDS");
+  // one group's W2 chunks of rows 2p, 2p+1 of the unit (codes, lane's block
+  // scale) . h of the group, per lane
+  auto dot2rows = [&](uint4 c0, uint4 c1, uint32_t s0, uint32_t s1, int g, float& d0, float& d1) {
+    B1Chunk hx;
+    hx.load_lds((const uint8_t*)sm.hb[g], (size_t)lane * 32);
+    float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
+    hx.fp4_acc(c0, e8m0_to_f32(s0), a0, a1);
+    hx.fp4_acc(c1, e8m0_to_f32(s1), b0, b1);
+    d0 = a0 + a1;
+    d1 = b0 + b1;
+  };
+  // wavefront 0 raises go once every unit's h is out (or its wait gave up)
+  auto wait_go = [&]() {
+    uint32_t it = 0;
+    while (__hip_atomic_load(&sm.go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u) {
+      if (++it > 4 * kFSpin) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+  };
 
   if (wave < kFCompute) {
     // ------------------------------------------------ computing wavefronts
@@ -258,6 +288,48 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
       if (lane == 0) __hip_atomic_store(&sm.go, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
 
+    // 5. once every unit's h is out: this workgroup's copy of it, into LDS
+    // (36 KiB at most, one request per thread and 8 KiB)
+    wait_go();
+    for (int i = tid; i < ng * (kFI / 8); i += 64 * kFCompute) ((uint4*)sm.hb)[i] = ((const uint4*)a.h)[i];
+    lds_barrier();  // B2: h is in LDS
+
+    // 6. output rows 2w, 2w+1 of the unit over the later groups [GS, ng),
+    // their W2 chunks from LDS, stored by the copying wavefronts while the
+    // units handed h over; the two row sums meet the copying wavefronts'
+    // in LDS
+    {
+      uint32_t it = 0;
+      while (__hip_atomic_load(&sm.stored, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)kFCopiers) {
+        if (++it > 4 * kFSpin) {
+          if (lane == 0) atomicOr(a.err, 2u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      asm volatile("" ::: "memory");
+    }
+    float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+    for (int g = GS; g < NB; ++g) {
+      if (g < ng) {
+        const int q = g - GS, r0 = 2 * wave;
+        const uint4 c0 = *(const uint4*)(sm.w2c[q][r0] + lane * 16);
+        const uint4 c1 = *(const uint4*)(sm.w2c[q][r0 + 1] + lane * 16);
+        float d0, d1;
+        dot2rows(c0, c1, sm.w2s[q][r0][lane], sm.w2s[q][r0 + 1][lane], g, d0, d1);
+        acc0 = fmaf(sm.gw[g], d0, acc0);
+        acc1 = fmaf(sm.gw[g], d1, acc1);
+      }
+    }
+    acc0 = wave_sum_to_lane63(acc0);
+    acc1 = wave_sum_to_lane63(acc1);
+    if (lane == 63) {
+      sm.part[2 * wave] = acc0;
+      sm.part[2 * wave + 1] = acc1;
+    }
+    lds_barrier();  // B3: the later groups' sums are in LDS
+
   } else {
     // ------------------------------------------------- copying wavefronts
     const int cw = wave - kFCompute;
@@ -265,14 +337,8 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
     auto issue_w2 = [&](W2Pair& p, const uint8_t* rec) {
       p.r0 = ld_stream16(rec + L.w2c + drow * kW2Row + lane * 16);
       p.r1 = ld_stream16(rec + L.w2c + (drow + 1) * kW2Row + lane * 16);
-      p.s = *(const uint16_t*)(rec + L.w2s + drow * kW2RowS + lane * 2);
-    };
-    auto store_w2 = [&](const W2Pair& p, int g) {
-      *(uint4*)(sm.w2c[g][2 * cw] + lane * 16) = p.r0;
-      *(uint4*)(sm.w2c[g][2 * cw + 1] + lane * 16) = p.r1;
-      *(uint16_t*)(sm.w2s[g] + 2 * cw * kW2RowS + lane * 2) = (uint16_t)p.s;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (lane == 0) __hip_atomic_store(&sm.ready[g][cw], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      p.s0 = rec[L.w2s + drow * kW2RowS + lane];
+      p.s1 = rec[L.w2s + (drow + 1) * kW2RowS + lane];
     };
     W2Pair wp[NB];
     // the shared expert's rows need no routing
@@ -295,84 +361,47 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
     for (int g = S0; g < NB; ++g) issue_w2(wp[g], issue_rec(g));
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // B1
-    // each group's rows into LDS as they land
+    // the later groups' rows into LDS for the computing wavefronts (the last
+    // requested, so this waits for every row: they land while the units hand
+    // h over)
 #pragma unroll
-    for (int g = 0; g < NB; ++g) store_w2(wp[g], g);
-  }
-
-  // 5. every wavefront: once every unit's h is out, ng consecutive down items
-  // (group-major (group, row) pairs, at most two groups), each one group's W2
-  // row dotted with its h.  The copying wavefronts have moved all their rows
-  // into LDS by now, so h is the only load in flight for any wavefront here.
-  // The rows of all the wavefront's items are read first and reduced
-  // together, so the items overlap instead of running as a chain.
-  {
-    uint32_t it = 0;
-    while (__hip_atomic_load(&sm.go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u) {
-      if (++it > 4 * kFSpin) break;  // wavefront 0 gives up first and raises go regardless
-      __builtin_amdgcn_s_sleep(1);
+    for (int g = GS; g < NB; ++g) {
+      const int q = g - GS;
+      *(uint4*)(sm.w2c[q][2 * cw] + lane * 16) = wp[g].r0;
+      *(uint4*)(sm.w2c[q][2 * cw + 1] + lane * 16) = wp[g].r1;
+      sm.w2s[q][2 * cw][lane] = (uint8_t)wp[g].s0;
+      sm.w2s[q][2 * cw + 1][lane] = (uint8_t)wp[g].s1;
     }
-    asm volatile("" ::: "memory");
-    const int ng = sm.ng, n = ng;
-    if (n > 0) {
-      const int i0 = n * wave;
-      const int glo = i0 / kFRowsDN, ghi = (i0 + n - 1) / kFRowsDN;
-      B1Chunk hlo, hhi;
-      hlo.load_global(a.h, (size_t)glo * kFI + (size_t)lane * 32);
-      hhi.load_global(a.h, (size_t)ghi * kFI + (size_t)lane * 32);
-      // items of group glo first, then those of ghi: each loop reads one
-      // activation chunk (a per-item choice between the two would copy it)
-      const int nlo = min(n, (glo + 1) * kFRowsDN - i0);
-      float v[kFMaxG];
-      auto item_dot = [&](const B1Chunk& hx, int i) {
-        const int item = i0 + i, g = item / kFRowsDN, r = item % kFRowsDN;
-        if (i % 3 == 0) {  // wait for this batch of three items' rows
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) atomicAdd(&sm.stored, 1u);
+
+    // 5. once every unit's h is out (step 4 of the computing wavefronts) and
+    // in this workgroup's LDS: the wavefront's two output rows over the
+    // earlier groups [S0, GS) (weighted, rank order) and the shared expert
+    // (weight 1), summed per lane from the W2 registers requested above;
+    // then the computing wavefronts' sums of the later groups, one rounding
+    wait_go();
+    lds_barrier();  // B2: h is in LDS
+    float acc0 = 0.0f, acc1 = 0.0f, sh0 = 0.0f, sh1 = 0.0f;
 #pragma unroll
-          for (int j = i; j < i + 3 && j < kFMaxG; ++j) {
-            const int jt = i0 + min(j, n - 1), gj = jt / kFRowsDN, rj = jt % kFRowsDN;
-            uint32_t it2 = 0;
-            while (__hip_atomic_load(&sm.ready[gj][rj / 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u) {
-              if (++it2 > 4 * kFSpin) {
-                if (lane == 0) atomicOr(a.err, 2u);
-                break;
-              }
-              __builtin_amdgcn_s_sleep(1);
-            }
-          }
-          asm volatile("" ::: "memory");
-        }
-        const uint4 c = *(const uint4*)(sm.w2c[g][r] + lane * 16);
-        const float sc = e8m0_to_f32(sm.w2s[g][r * kW2RowS + lane]);
-        float p0 = 0.0f, p1 = 0.0f;
-        hx.fp4_acc(c, sc, p0, p1);
-        return p0 + p1;
-      };
-#pragma unroll
-      for (int i = 0; i < kFMaxG; ++i) v[i] = i < nlo ? item_dot(hlo, i) : 0.0f;
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < kFMaxG; ++i)
-        if (i >= nlo && i < n) v[i] = item_dot(hhi, i);
-#pragma unroll
-      for (int i = 0; i < kFMaxG; ++i) v[i] = wave_sum_to_lane63(v[i]);
-      if (lane == 63) {
-#pragma unroll
-        for (int i = 0; i < kFMaxG; ++i) {
-          const int item = i0 + i;
-          if (i < n) sm.res[item / kFRowsDN][item % kFRowsDN] = v[i];
-        }
+    for (int g = S0; g < GS; ++g) {
+      if (g < ng) {
+        float d0, d1;
+        dot2rows(wp[g].r0, wp[g].r1, wp[g].s0, wp[g].s1, g, d0, d1);
+        acc0 = fmaf(sm.gw[g], d0, acc0);
+        acc1 = fmaf(sm.gw[g], d1, acc1);
       }
     }
-  }
-  lds_barrier();  // B2: every item's result is in LDS
-
-  // 6. each output row: routed groups in rank order, then the shared expert
-  if (tid < kFRowsDN) {
-    const int ng = sm.ng;
-    float acc = 0.0f;
-    for (int g = S0; g < ng; ++g) acc = fmaf(sm.gw[g], sm.res[g][tid], acc);
-    if (SH && ng > 0) acc += sm.res[0][tid];
-    ((uint16_t*)a.out)[unit * kFRowsDN + tid] = f32_to_bf16(acc);
+    if (SH && ng > 0) dot2rows(wp[0].r0, wp[0].r1, wp[0].s0, wp[0].s1, 0, sh0, sh1);
+    acc0 = wave_sum_to_lane63(acc0);
+    acc1 = wave_sum_to_lane63(acc1);
+    sh0 = wave_sum_to_lane63(sh0);
+    sh1 = wave_sum_to_lane63(sh1);
+    lds_barrier();  // B3: the later groups' sums are in LDS
+    if (lane == 63) {
+      ((uint16_t*)a.out)[drow] = f32_to_bf16((acc0 + sm.part[2 * cw]) + sh0);
+      ((uint16_t*)a.out)[drow + 1] = f32_to_bf16((acc1 + sm.part[2 * cw + 1]) + sh1);
+    }
   }
 }
 
