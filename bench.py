@@ -6,7 +6,9 @@ one shared expert, hidden 4096, expert intermediate 2048, top-8, 13,369,344
 bytes per FP4 expert): one step = route one token's fp32 logits (top-8,
 renormalised) + the SwiGLU MLP of the 8 selected experts and the shared
 expert on MXFP4 weights + the weighted combine to a bf16 output, issued as one
-moe_layer_decode call (two kernels).  Each step uses fresh seeded logits and
+moe_layer_decode call: one kernel at full width (the layer flagged for the
+single launch, which the library takes on a device whose CUs hold the whole
+grid; --two-launch asks for the two-kernel step instead).  Each step uses fresh seeded logits and
 activations; every expert is resident in HBM.  The model has many such layers
 (43): the timed steps rotate over --layers resident layers (8 by default,
 27.5 GB), each with its own experts and shared expert, so consecutive steps
@@ -14,8 +16,9 @@ share no weights and none of a step's bytes can come from the 256 MB
 last-level cache; single-layer steady and cold latencies are reported beside.
 
 Prints one JSON line: tokens/s of the whole step, the achieved HBM bandwidth
-of the dominant kernel (gate/up GEMV) against the 8 TB/s peak, and the CPU
-oracle timed on the host on a bounded sample.
+of the dominant kernel (the single launch; with two launches, the gate/up
+GEMV) against the 8 TB/s peak, and the CPU oracle timed on the host on a
+bounded sample.
 """
 from __future__ import annotations
 
@@ -58,7 +61,10 @@ def parse():
                     help="decode-b1 on rank 0's share of G-way tensor parallelism (experts cut along I)")
     ap.add_argument("--single-launch", action="store_true",
                     help="decode-b1: layers flagged MOE_LAYER_SINGLE_LAUNCH (routing through combine in one kernel; "
-                         "hidden 4096 with I 2048, or I 256 with --tp-share 8)")
+                         "hidden 4096 with I 2048, or I 256 with --tp-share 8); the default at full width")
+    ap.add_argument("--two-launch", action="store_true",
+                    help="decode-b1 at full width: the two-launch step (gate/up, then down + combine) instead of "
+                         "the single launch")
     ap.add_argument("--slot-tier", action="store_true",
                     help="slotcache workload with a 100-slot 2-bit device tier and LFU eviction "
                          "(decay 0.95, counts seeded from a separate 64-token routing trace)")
@@ -83,6 +89,7 @@ def kernel_hash(files=("decode_b1.hip", "b1_dev.h", "route_dev.h", "common.h")) 
 
 
 B64_KERNEL_FILES = ("prefill.hip", "common.h")
+FUSED_KERNEL_FILES = ("decode_fused.hip", "handoff_dev.h", "b1_dev.h", "route_dev.h", "common.h")
 
 
 def traffic_from_profiles(khash: str, record: str = "traffic_gateup_decode_b1.json"):
@@ -305,14 +312,18 @@ def bench_decode_b1(args):
     w_d = torch.empty((nsteps, k), dtype=torch.float32, device=dev)
     out_d = torch.empty((nsteps, H), dtype=torch.bfloat16, device=dev)
     ws = lib.expert_workspace(H, I, T, k, True, device=dev)
-    lflags = lib.MOE_LAYER_SINGLE_LAUNCH if args.single_launch else 0
+    # full width: the single launch unless asked for two (it needs every
+    # workgroup resident at once, which the library checks; a 1/G share runs
+    # two launches unless asked, being faster that way)
+    single = args.single_launch or (G == 1 and not args.two_launch)
+    lflags = lib.MOE_LAYER_SINGLE_LAUNCH if single else 0
     layers = [lib.make_layer(H, I, fp4_base=bk, fp4_stride=rec_bytes, num_slots=E, shared=sh, flags=lflags)
               for bk, sh in layers_mem]
     torch.cuda.synchronize()
     print(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     def step(s):
-        # route + expert MLP + combine of one token on layer s mod L: two kernel launches
+        # route + expert MLP + combine of one token on layer s mod L: one kernel launch (or two)
         lib.moe_layer_decode(layers[s % NL], lg_d[s], x_d[s:s + 1], k, ids_d[s], w_d[s], out_d[s:s + 1], ws)
 
     def step_one_layer(s):
@@ -338,8 +349,12 @@ def bench_decode_b1(args):
     # w1, w3, w2), the logits row, the activation row, the bf16 SwiGLU outputs
     # written and read back, the ids and weights, the bf16 output row
     step_alg_bytes = k1 * rec_bytes + E * 4 + H * 2 + 2 * k1 * I * 2 + k * 8 + H * 2
-    khash = kernel_hash()
-    traffic = traffic_from_profiles(khash) if G == 1 and not args.single_launch else None
+    # a single launch that gave up a wait set the workspace's error word: its
+    # outputs would be meaningless, so such a run reports nothing
+    off = lib.moe_expert_workspace_sync_offset(H, I, T, k, True)
+    err = int(ws[off + 1024:off + 1028].view(torch.int32).item())
+    if err != 0:
+        raise SystemExit(f"[bench] the single launch's handoff gave up (error word {err}); no result")
     per_kernel = {n: round(v[0] / v[1] * 1e3, 3) for n, v in prof.items()}
     print(f"[bench] kernel averages (us): {per_kernel}", file=sys.stderr, flush=True)
     if "fused" in prof:  # the single launch: the whole step is one kernel
@@ -349,6 +364,8 @@ def bench_decode_b1(args):
         # the step's algorithmic bytes (the SwiGLU outputs cross workgroups
         # through memory: written once and read back)
         dom_bytes = step_alg_bytes
+        khash = kernel_hash(FUSED_KERNEL_FILES)
+        traffic = traffic_from_profiles(khash, "traffic_fused_decode_b1.json") if G == 1 else None
     else:
         ms, n = prof["gateup"]      # the dominant kernel of the two launches
         dom_kernel = ("gateup_b1_kernel (routing + batch-1 gate/up GEMV + SwiGLU)" if G == 1 else
@@ -356,6 +373,8 @@ def bench_decode_b1(args):
         # the 9 experts' w1 and w3 codes and scales, the logits row, the
         # activation row, the bf16 SwiGLU outputs written
         dom_bytes = k1 * 2 * (H * I // 2 + H * I // 32) + E * 4 + H * 2 + k1 * I * 2
+        khash = kernel_hash()
+        traffic = traffic_from_profiles(khash) if G == 1 else None
     dom_avg_s = ms / n / 1e3
     achieved = dom_bytes / dom_avg_s / 1e9
 
@@ -376,7 +395,7 @@ def bench_decode_b1(args):
         "dtype": "mxfp4-w/bf16-x/f32-acc",
         "data": "synthetic (seeded; fresh logits and activations every step)",
         "config": {"workload": cfg["name"] + (f"-tp{G}-share0" if G > 1 else "") +
-                   (f"-{NL}layers-rotated" if NL > 1 else "") + ("-single-launch" if args.single_launch else ""),
+                   (f"-{NL}layers-rotated" if NL > 1 else "") + ("-single-launch" if "fused" in prof else ""),
                    "experts": E,
                    "shared_experts": 1, "hidden": H, "expert_intermediate": I, "top_k": k, "tokens_per_step": T,
                    "layers": NL, "layer_of_step": "s mod layers",
