@@ -332,8 +332,23 @@ def bench_decode_b1(args):
     if args.calibrate_copy:
         calibration_copy(torch, dev)
 
+    off = lib.moe_expert_workspace_sync_offset(H, I, T, k, True)
+
+    def err_word():
+        return int(ws[off + 1024:off + 1028].view(torch.int32).item())
+
     step(0)
     torch.cuda.synchronize()
+    if single and err_word() != 0:
+        # the single launch's handoff gave up (its grid was not all resident):
+        # the two-launch step instead, on a fresh workspace
+        print("[bench] the single launch's handoff gave up on the first step; running two launches",
+              file=sys.stderr, flush=True)
+        ws = lib.expert_workspace(H, I, T, k, True, device=dev)
+        layers = [lib.make_layer(H, I, fp4_base=bk, fp4_stride=rec_bytes, num_slots=E, shared=sh, flags=0)
+                  for bk, sh in layers_mem]
+        step(0)
+        torch.cuda.synchronize()
 
     elapsed = run_steps(args, torch, step, K, Wm)
     print(f"[bench] timed {K} steps in {elapsed * 1e3:.2f} ms ({args.mode})", file=sys.stderr, flush=True)
@@ -351,8 +366,7 @@ def bench_decode_b1(args):
     step_alg_bytes = k1 * rec_bytes + E * 4 + H * 2 + 2 * k1 * I * 2 + k * 8 + H * 2
     # a single launch that gave up a wait set the workspace's error word: its
     # outputs would be meaningless, so such a run reports nothing
-    off = lib.moe_expert_workspace_sync_offset(H, I, T, k, True)
-    err = int(ws[off + 1024:off + 1028].view(torch.int32).item())
+    err = err_word()
     if err != 0:
         raise SystemExit(f"[bench] the single launch's handoff gave up (error word {err}); no result")
     per_kernel = {n: round(v[0] / v[1] * 1e3, 3) for n, v in prof.items()}
