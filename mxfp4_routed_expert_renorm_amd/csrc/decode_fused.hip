@@ -291,7 +291,21 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
     // 5. once every unit's h is out: this workgroup's copy of it, into LDS
     // (36 KiB at most, one request per thread and 8 KiB)
     wait_go();
-    for (int i = tid; i < ng * (kFI / 8); i += 64 * kFCompute) ((uint4*)sm.hb)[i] = ((const uint4*)a.h)[i];
+    {
+      // every piece requested before the first is stored: one trip, where a
+      // load-store loop waits for each piece in turn.  The index is clamped,
+      // not branched on, so the requests stay in flight together; lanes past
+      // the end load and store the last piece again (the same bytes)
+      constexpr int kStride = 64 * kFCompute, kPer = (NB * (kFI / 8) + kStride - 1) / kStride;
+      const int last = ng * (kFI / 8) - 1;
+      if (last >= 0) {
+        uint4 v[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) v[j] = ((const uint4*)a.h)[min(tid + j * kStride, last)];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) ((uint4*)sm.hb)[min(tid + j * kStride, last)] = v[j];
+      }
+    }
     lds_barrier();  // B2: h is in LDS
 
     // 6. output rows 2w, 2w+1 of the unit over the later groups [GS, ng),
