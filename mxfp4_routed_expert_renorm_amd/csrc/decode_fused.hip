@@ -134,6 +134,47 @@ __device__ __forceinline__ const uint8_t* group_record(const FusedArgs& a, const
   return a.fp4_base + (size_t)sm.gslot[g] * a.fp4_stride;
 }
 
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// A weight row times the activation on the matrix cores, for one token.
+// The row's FP4 weights and the activation sit 32 per lane at the same
+// positions.  In v_mfma_f32_16x16x32_bf16 lane l gives row l%16 of A and
+// column l%16 of B, 8 elements each at the same K positions, so tile entry
+// (m, m) sums exactly the products of the lanes with l%16 = m; over the
+// lane's four MFMAs per 32 weights (8 pairs each) the tile's diagonal sums
+// to the dot product, and the other entries, which pair different
+// positions, are dropped.  Each weight times its power-of-two block scale is
+// a bf16 value, so every product is exact and only the order of the fp32
+// sums differs from v_dot2.  For two rows against the same activation chunk
+// x of the lane (the two MFMA chains interleave): ta += the 32 weights of
+// codes ca (scale sa) times x, tb likewise.
+__device__ __forceinline__ void tile_fp4_acc2(const B1Chunk& x, uint4 ca, float sa, v4f& ta, uint4 cb, float sb,
+                                              v4f& tb) {
+  const uint32_t da[4] = {ca.x, ca.y, ca.z, ca.w}, db[4] = {cb.x, cb.y, cb.z, cb.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v8bf16 b = __builtin_bit_cast(v8bf16, make_uint4(x.p[4 * i], x.p[4 * i + 1], x.p[4 * i + 2], x.p[4 * i + 3]));
+    const uint4 wa = make_uint4(fp4x2_to_bf16x2_scaled<0>(da[i], sa), fp4x2_to_bf16x2_scaled<1>(da[i], sa),
+                                fp4x2_to_bf16x2_scaled<2>(da[i], sa), fp4x2_to_bf16x2_scaled<3>(da[i], sa));
+    ta = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, wa), b, ta, 0, 0, 0);
+    const uint4 wb = make_uint4(fp4x2_to_bf16x2_scaled<0>(db[i], sb), fp4x2_to_bf16x2_scaled<1>(db[i], sb),
+                                fp4x2_to_bf16x2_scaled<2>(db[i], sb), fp4x2_to_bf16x2_scaled<3>(db[i], sb));
+    tb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, wb), b, tb, 0, 0, 0);
+  }
+}
+
+// The lane's share of the dot product held in tile t: the diagonal entry it
+// holds, or zero.  The 16x16 tile sits as entry (4(l/16) + j, l%16) in
+// register j of lane l, so entry (m, m) is register m%4 of lane 16(m/4) + m.
+__device__ __forceinline__ float tile_diag(v4f t, int lane) {
+  const int j = lane & 3;
+  const float lo = (j & 1) ? t[1] : t[0];
+  const float hi = (j & 1) ? t[3] : t[2];
+  const float v = (j & 2) ? hi : lo;
+  return ((lane >> 4) == ((lane & 15) >> 2)) ? v : 0.0f;
+}
+
 // one gate/up row of one group: both halves of H, w1 and w3
 struct GURow {
   uint4 c1[2], c3[2];
@@ -257,18 +298,16 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
 #pragma unroll
     for (int g = 0; g < NB; ++g) {
       GURow& r = ring[g % WIN];
-      float g0 = 0.0f, g1 = 0.0f, u0 = 0.0f, u1 = 0.0f;
-      x0.fp4_acc(r.c1[0], e8m0_to_f32(r.s1[0]), g0, g1);
-      x1.fp4_acc(r.c1[1], e8m0_to_f32(r.s1[1]), g0, g1);
-      x0.fp4_acc(r.c3[0], e8m0_to_f32(r.s3[0]), u0, u1);
-      x1.fp4_acc(r.c3[1], e8m0_to_f32(r.s3[1]), u0, u1);
+      v4f tg = {0.0f, 0.0f, 0.0f, 0.0f}, tu = {0.0f, 0.0f, 0.0f, 0.0f};
+      tile_fp4_acc2(x0, r.c1[0], e8m0_to_f32(r.s1[0]), tg, r.c3[0], e8m0_to_f32(r.s3[0]), tu);
+      tile_fp4_acc2(x1, r.c1[1], e8m0_to_f32(r.s1[1]), tg, r.c3[1], e8m0_to_f32(r.s3[1]), tu);
       if (g + WIN < NB) {
         issue_gu(r, issue_rec(g + WIN));
         if (g + WIN == NB - 1 && lane == 0) atomicAdd(&sm.issued, 1u);
       }
       __builtin_amdgcn_sched_barrier(0);
-      const float gs = wave_sum_to_lane63(g0 + g1);
-      const float us = wave_sum_to_lane63(u0 + u1);
+      const float gs = wave_sum_to_lane63(tile_diag(tg, lane));
+      const float us = wave_sum_to_lane63(tile_diag(tu, lane));
       if (lane == 63 && g < ng) sm.hrow[g][wave] = silu_mul_b1(gs, us);
     }
     lds_barrier();  // B1: the unit's SwiGLU outputs are in LDS
