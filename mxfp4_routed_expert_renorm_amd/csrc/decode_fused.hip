@@ -175,6 +175,13 @@ __device__ __forceinline__ float tile_diag(v4f t, int lane) {
   return ((lane >> 4) == ((lane & 15) >> 2)) ? v : 0.0f;
 }
 
+// A group's h in LDS: lane l's 64 bytes (elements 32l .. 32l+31) as four
+// 16-byte pieces, piece i in slot 4l + ((i + r) & 3) with a per-lane rotation
+// r, so that the lanes' i-th 16-byte reads fall in different banks (with
+// pieces in order, lanes 64 bytes apart would share banks four ways).  The
+// rotation is conflict-free for 32 and for 64 banks of 4 bytes.
+__device__ __forceinline__ int h_slot(int l, int i) { return 4 * l + ((i + ((l >> 1) ^ (l >> 3))) & 3); }
+
 // one gate/up row of one group: both halves of H, w1 and w3
 struct GURow {
   uint4 c1[2], c3[2];
@@ -213,7 +220,11 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
   // scale) . h of the group, per lane
   auto dot2rows = [&](uint4 c0, uint4 c1, uint32_t s0, uint32_t s1, int g, float& d0, float& d1) {
     B1Chunk hx;
-    hx.load_lds((const uint8_t*)sm.hb[g], (size_t)lane * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = ((const uint4*)sm.hb[g])[h_slot(lane, i)];
+      hx.p[4 * i] = v.x, hx.p[4 * i + 1] = v.y, hx.p[4 * i + 2] = v.z, hx.p[4 * i + 3] = v.w;
+    }
     float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
     hx.fp4_acc(c0, e8m0_to_f32(s0), a0, a1);
     hx.fp4_acc(c1, e8m0_to_f32(s1), b0, b1);
@@ -342,7 +353,10 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) v[j] = ((const uint4*)a.h)[min(tid + j * kStride, last)];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) ((uint4*)sm.hb)[min(tid + j * kStride, last)] = v[j];
+        for (int j = 0; j < kPer; ++j) {
+          const int q = min(tid + j * kStride, last);  // group q / 256, piece q % 256 of it
+          ((uint4*)sm.hb)[(q & ~255) + h_slot((q & 255) >> 2, q & 3)] = v[j];
+        }
       }
     }
     lds_barrier();  // B2: h is in LDS
