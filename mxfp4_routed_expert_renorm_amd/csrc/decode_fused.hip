@@ -113,6 +113,8 @@ struct alignas(16) FusedSmem {
   int ng;                                 // groups with work
   uint32_t issued;                        // computing wavefronts that issued their last gate/up row
   uint32_t go;                            // every gate/up unit is done
+  alignas(16) uint8_t xq[2][2][64][32];   // x as MFMA operands: [half of H][hi, lo][lane][32 E4M3 codes]
+  uint8_t xs[64][4];                      // their block scales: [lane][half 0 hi, lo, half 1 hi, lo]
 };
 
 // workgroup barrier that orders LDS only: a fenced __syncthreads would also
@@ -134,39 +136,38 @@ __device__ __forceinline__ const uint8_t* group_record(const FusedArgs& a, const
   return a.fp4_base + (size_t)sm.gslot[g] * a.fp4_stride;
 }
 
-typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// A weight row times the activation on the matrix cores, for one token.
-// The row's FP4 weights and the activation sit 32 per lane at the same
-// positions.  In v_mfma_f32_16x16x32_bf16 lane l gives row l%16 of A and
-// column l%16 of B, 8 elements each at the same K positions, so tile entry
-// (m, m) sums exactly the products of the lanes with l%16 = m; over the
-// lane's four MFMAs per 32 weights (8 pairs each) the tile's diagonal sums
-// to the dot product, and the other entries, which pair different
-// positions, are dropped.  Each weight times its power-of-two block scale is
-// a bf16 value, so every product is exact and only the order of the fp32
-// sums differs from v_dot2.  For two rows against the same activation chunk
-// x of the lane (the two MFMA chains interleave): ta += the 32 weights of
-// codes ca (scale sa) times x, tb likewise.
-__device__ __forceinline__ void tile_fp4_acc2(const B1Chunk& x, uint4 ca, float sa, v4f& ta, uint4 cb, float sb,
-                                              v4f& tb) {
-  const uint32_t da[4] = {ca.x, ca.y, ca.z, ca.w}, db[4] = {cb.x, cb.y, cb.z, cb.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const v8bf16 b = __builtin_bit_cast(v8bf16, make_uint4(x.p[4 * i], x.p[4 * i + 1], x.p[4 * i + 2], x.p[4 * i + 3]));
-    const uint4 wa = make_uint4(fp4x2_to_bf16x2_scaled<0>(da[i], sa), fp4x2_to_bf16x2_scaled<1>(da[i], sa),
-                                fp4x2_to_bf16x2_scaled<2>(da[i], sa), fp4x2_to_bf16x2_scaled<3>(da[i], sa));
-    ta = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, wa), b, ta, 0, 0, 0);
-    const uint4 wb = make_uint4(fp4x2_to_bf16x2_scaled<0>(db[i], sb), fp4x2_to_bf16x2_scaled<1>(db[i], sb),
-                                fp4x2_to_bf16x2_scaled<2>(db[i], sb), fp4x2_to_bf16x2_scaled<3>(db[i], sb));
-    tb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, wb), b, tb, 0, 0, 0);
-  }
+// A weight row times x on the matrix cores, for one token, with
+// v_mfma_scale_f32_16x16x128_f8f6f4 (A: x as E4M3, B: the FP4 weights and
+// their E8M0 block scales exactly as stored, so no weight is converted).
+// Operand layout on gfx950: lane l = 16h + c gives B column c as 32 FP4
+// values at K [32h, 32h+32) with the scale of that block, and A row c as 32
+// E4M3 bytes at K [16h, 16h+16) and [64+16h, 64+16h+16) with the scale of
+// A's K block h.  A row's 16-byte chunk of lane l (weights 32l .. 32l+31,
+// one scale block) is B column c's K block h, so if A row c holds at every K
+// the x element of the weight at that K, tile entry (c, c) sums exactly the
+// products of the lanes with l%16 = c, the tile's diagonal sums to the dot
+// product over the 64 chunks, and the other entries (mismatched positions)
+// are dropped.  x enters as two parts, each E4M3 under a power-of-two scale
+// per 32-element block of x: hi under 2^(E-7) (E = floor(log2) of the
+// block's largest magnitude, so hi stays below 256 and never saturates), lo
+// = the remainder under 2^(E-11).  hi + lo is x exactly for every element
+// within 2^13 of its block's largest (an E4M3 value holds 4 significant
+// bits, bf16 8); below that the remainder's rounding error stays under
+// 2^-21 of the block's largest.  Every product is exact and the tile sums in
+// fp32.  t += row chunks (codes c, scale byte sc) . both parts of x.
+__device__ __forceinline__ v4f tile_fp4_x(v8i xh, v8i xl, uint32_t sh, uint32_t sl, uint4 c, uint32_t sc, v4f t) {
+  const v8i b = {(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+  t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xh, b, t, 0, 4, 0, (int)sh, 0, (int)sc);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xl, b, t, 0, 4, 0, (int)sl, 0, (int)sc);
 }
 
 // The lane's share of the dot product held in tile t: the diagonal entry it
-// holds, or zero.  The 16x16 tile sits as entry (4(l/16) + j, l%16) in
-// register j of lane l, so entry (m, m) is register m%4 of lane 16(m/4) + m.
+// holds, or zero.  The 16x16 result tile sits as entry (4(l/16) + j, l%16)
+// in register j of lane l, so entry (m, m) is register m%4 of lane
+// 16(m/4) + m.
 __device__ __forceinline__ float tile_diag(v4f t, int lane) {
   const int j = lane & 3;
   const float lo = (j & 1) ? t[1] : t[0];
@@ -258,9 +259,7 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
     const uint32_t tag = handoff_tag(a.sync, unit);
     // 1. the activation, the routing inputs (wavefront 0), the shared
     // expert's row: none of it needs the routing
-    B1Chunk x0, x1;
-    x0.load_global(a.x, (size_t)lane * 32);
-    x1.load_global(a.x, (size_t)(64 + lane) * 32);
+    const uint4 xv = ((const uint4*)a.x)[tid];  // x elements 8 tid .. 8 tid + 7
     float lv[EPL > 0 ? EPL : 1];
     int my_slot = -1;
     float my_w = 0.0f;
@@ -275,6 +274,54 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
     GURow ring[WIN];
     if constexpr (SH) issue_gu(ring[0], a.shared);
     __builtin_amdgcn_sched_barrier(0);
+
+    // x split into its two E4M3 parts (tile_fp4_x), placed as the MFMA's A
+    // operand: element e (half p = e / 2048 of H, chunk C = e / 32 % 64 of
+    // it, offset o = e % 32) sits at K = 32 (C / 16) + o of lane 16h + C % 16,
+    // byte j, with (h, j) = (K / 16, K % 16) for K < 64 and
+    // ((K - 64) / 16, 16 + K % 16) above.  Chunk C's scales go to lane C.
+    {
+      const int e0 = 8 * tid, p = e0 >> 11, C = (e0 >> 5) & 63, o = e0 & 31;
+      const int K = 32 * (C >> 4) + o;
+      const int h = K < 64 ? K >> 4 : (K - 64) >> 4, j = K < 64 ? (K & 15) : 16 + (K & 15);
+      const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+      float v[8], m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        m = fmaxf(m, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+      }
+      // the chunk's 32 elements are four neighbouring threads'
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      const int E = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;  // zero or subnormal: -127
+      const int sh = min(127, max(-127, E - 7)), sl = min(127, max(-127, E - 11));
+      float vh[8], vl[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vh[i] = __builtin_amdgcn_ldexpf(v[i], -sh);
+      uint32_t ch[2], cl[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(vh[4 * q], vh[4 * q + 1], 0, false);
+        c = __builtin_amdgcn_cvt_pk_fp8_f32(vh[4 * q + 2], vh[4 * q + 3], c, true);
+        ch[q] = (uint32_t)c;
+        const v2f d0 = __builtin_amdgcn_cvt_pk_f32_fp8(c, false), d1 = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
+        vl[4 * q] = __builtin_amdgcn_ldexpf(vh[4 * q] - d0[0], sh - sl);
+        vl[4 * q + 1] = __builtin_amdgcn_ldexpf(vh[4 * q + 1] - d0[1], sh - sl);
+        vl[4 * q + 2] = __builtin_amdgcn_ldexpf(vh[4 * q + 2] - d1[0], sh - sl);
+        vl[4 * q + 3] = __builtin_amdgcn_ldexpf(vh[4 * q + 3] - d1[1], sh - sl);
+        int l2 = __builtin_amdgcn_cvt_pk_fp8_f32(vl[4 * q], vl[4 * q + 1], 0, false);
+        cl[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(vl[4 * q + 2], vl[4 * q + 3], l2, true);
+      }
+      const int ln = 16 * h + (C & 15);
+      *(uint2*)&sm.xq[p][0][ln][j] = make_uint2(ch[0], ch[1]);
+      *(uint2*)&sm.xq[p][1][ln][j] = make_uint2(cl[0], cl[1]);
+      if ((tid & 3) == 0) {
+        sm.xs[C][2 * p] = (uint8_t)(sh + 127);
+        sm.xs[C][2 * p + 1] = (uint8_t)(sl + 127);
+      }
+    }
 
     // 2. wavefront 0 routes the token and lists the groups
     if (wave == 0) {
@@ -294,9 +341,19 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
         a.w[lane] = my_w;
       }
     }
-    lds_barrier();  // B0: groups listed
+    lds_barrier();  // B0: groups listed, x's parts in LDS
     const int ng = sm.ng;
     auto issue_rec = [&](int g) { return group_record(a, sm, g, ng, S0); };
+    v8i xa[2][2];  // [half of H][hi, lo]
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 u0 = *(const uint4*)&sm.xq[p][q][lane][0], u1 = *(const uint4*)&sm.xq[p][q][lane][16];
+        xa[p][q] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+      }
+    const uint32_t xsw = *(const uint32_t*)sm.xs[lane];
+    const uint32_t xs0h = xsw & 0xffu, xs0l = (xsw >> 8) & 0xffu, xs1h = (xsw >> 16) & 0xffu, xs1l = xsw >> 24;
 
     // 3. gate/up rows of the groups, WIN in flight; each row's SwiGLU output
     // goes to LDS.  Every batch slot is issued (past the active groups: the
@@ -310,8 +367,10 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
     for (int g = 0; g < NB; ++g) {
       GURow& r = ring[g % WIN];
       v4f tg = {0.0f, 0.0f, 0.0f, 0.0f}, tu = {0.0f, 0.0f, 0.0f, 0.0f};
-      tile_fp4_acc2(x0, r.c1[0], e8m0_to_f32(r.s1[0]), tg, r.c3[0], e8m0_to_f32(r.s3[0]), tu);
-      tile_fp4_acc2(x1, r.c1[1], e8m0_to_f32(r.s1[1]), tg, r.c3[1], e8m0_to_f32(r.s3[1]), tu);
+      tg = tile_fp4_x(xa[0][0], xa[0][1], xs0h, xs0l, r.c1[0], r.s1[0], tg);
+      tu = tile_fp4_x(xa[0][0], xa[0][1], xs0h, xs0l, r.c3[0], r.s3[0], tu);
+      tg = tile_fp4_x(xa[1][0], xa[1][1], xs1h, xs1l, r.c1[1], r.s1[1], tg);
+      tu = tile_fp4_x(xa[1][0], xa[1][1], xs1h, xs1l, r.c3[1], r.s3[1], tu);
       if (g + WIN < NB) {
         issue_gu(r, issue_rec(g + WIN));
         if (g + WIN == NB - 1 && lane == 0) atomicAdd(&sm.issued, 1u);
