@@ -153,6 +153,54 @@ def test_single_launch_given_ids_with_drops(gpu_lib, with_shared):
         assert err <= TOL_BF16_MAX_REL, (i, err)
 
 
+def _x_wide_range():
+    """bf16 activations whose 32-element blocks stress the single launch's
+    two-part E4M3 form of x: an all-zero block (+0 and -0), a block whose
+    elements sit 2^-30 below its largest (past the exactly split range), a
+    block of bf16 subnormals, blocks alternating 2^6 and 2^-8 magnitudes, and
+    ordinary N(0,1) blocks elsewhere."""
+    x = W.bf16_normal(7, (43,), (1, 4096)).copy()
+    rng = np.random.default_rng(43)
+    sign = lambda n: np.where(rng.random(n) < 0.5, 0x8000, 0).astype(np.uint16)
+    f32_to_bf16 = lambda v: (np.asarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x[0, 0:32] = sign(32)                                                   # zeros of both signs
+    x[0, 32:64] = f32_to_bf16(rng.standard_normal(32) * 2.0 ** -20)         # tiny against
+    x[0, 32] = f32_to_bf16(1024.0)                                          # one large element
+    x[0, 64:96] = (rng.integers(1, 0x80, 32).astype(np.uint16) | sign(32))  # subnormal bf16
+    alt = np.where(np.arange(64) % 2 == 0, 2.0 ** 6, 2.0 ** -8) * (1.0 + rng.random(64))
+    x[0, 96:160] = f32_to_bf16(alt) | sign(64)
+    x[0, 4064:4096] = f32_to_bf16(rng.standard_normal(32) * 2.0 ** -126)    # block maximum subnormal or near
+    return x
+
+
+def test_single_launch_x_edge_blocks(gpu_lib):
+    """The single launch on activations with zero, subnormal and wide-range
+    blocks (x enters its gate/up matrix-core products as two E4M3 parts):
+    within tolerance of the oracle, with no non-finite output."""
+    torch = _torch()
+    st = _bank(gpu_lib)
+    H, I, k = 4096, 2048, 8
+    desc = _desc(gpu_lib, st, gpu_lib.MOE_LAYER_SINGLE_LAUNCH)
+    ws = gpu_lib.expert_workspace(H, I, 1, k, True)
+    ids = np.array([17, 3, 250, 44, 96, 131, 5, 201], np.int32)
+    wts = np.random.default_rng(44).random((1, k)).astype(np.float32)
+    x = _x_wide_range()
+    out = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+    log("single launch, edge-case activation blocks")
+    gpu_lib.moe_expert_forward(desc, bf16_dev(x), 1, k, dev(ids[None]), None, dev(wts), out, ws)
+    torch.cuda.synchronize()
+    assert _err_word(gpu_lib, ws, k) == 0
+    got = to_f64(out)[0]
+    assert np.all(np.isfinite(got))
+    x64 = O.bf16_bits_to_f64(x)[0]
+    ref = O.expert_mlp(x64, *_expert(st, -1))
+    for r in range(k):
+        ref = ref + float(wts[0, r]) * O.expert_mlp(x64, *_expert(st, int(ids[r])))
+    err = max_rel(got, ref)
+    log(f"  edge blocks: max-rel {err:.3e}")
+    assert err <= TOL_BF16_MAX_REL, err
+
+
 def test_single_launch_graph_replays(gpu_lib):
     """The single launch captured in a HIP graph (four tokens) and replayed
     three times, with eager calls on the same workspace between the replays:
