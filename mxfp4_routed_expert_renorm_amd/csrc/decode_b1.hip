@@ -90,9 +90,8 @@ __global__ __launch_bounds__(256, 2) void gateup_b1_kernel(B1Args a) {
   constexpr int XBYTES = CPL * 64 * 32 * 2;  // H bf16 activations
   static_assert(CPL == 1 || CPL == 2, "H is 2048 or 4096");
   static_assert(NB >= 1 + (SH ? 1 : 0), "batch holds the shared expert and at least one rank");
-  __shared__ __align__(16) uint8_t xs[HAS2 ? XBYTES : 16];  // x as bf16, for the 2-bit rows
-  __shared__ __align__(16) uint8_t xop[CPL][2][64][32];       // x as the MFMA's A operand per 2048: [hi, lo][lane]
-  __shared__ __align__(4) uint8_t xsc[64][4];                // their block scales: [lane][2048-stretch hi, lo, ...]
+  __shared__ __align__(16) uint8_t xs[XBYTES];
+  __shared__ float stab[256];  // E8M0 byte -> scale
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // < I: the grid tiles I
   const int I = a.I, k = a.k;
@@ -127,6 +126,7 @@ __global__ __launch_bounds__(256, 2) void gateup_b1_kernel(B1Args a) {
   }
   __builtin_amdgcn_sched_barrier(0);  // the routing inputs stay ahead of the shared row in the queue
   if constexpr (SH) issue(sl[0], a.shared);
+  stab[threadIdx.x] = e8m0_to_f32(threadIdx.x);
 
   // 2. the token's FP4 ranks (routed here when logits are given)
   if constexpr (EPL > 0) {
@@ -145,26 +145,8 @@ __global__ __launch_bounds__(256, 2) void gateup_b1_kernel(B1Args a) {
   const int nf = __popcll(m);
   constexpr int S0 = SH ? 1 : 0;
   const int nact = S0 + nf;
-  // x split into its two E4M3 parts (tile_fp4_x), placed as the A operand
-  // of each 2048-element stretch (a_operand_pos); pieces of 8 elements
-#pragma unroll
-  for (int q = 0; q < CPL; ++q) {
-    const int e0 = 8 * ((int)threadIdx.x + 256 * q), C = (e0 >> 5) & 63;
-    uint2 hi, lo;
-    int sh, sl2, ln, j;
-    split_e4m3(q == 0 ? xv0 : xv1, hi, lo, sh, sl2);
-    a_operand_pos(C, e0 & 31, ln, j);
-    *(uint2*)&xop[q][0][ln][j] = hi;
-    *(uint2*)&xop[q][1][ln][j] = lo;
-    if ((threadIdx.x & 3) == 0) {
-      xsc[C][2 * q] = (uint8_t)(sh + 127);
-      xsc[C][2 * q + 1] = (uint8_t)(sl2 + 127);
-    }
-  }
-  if constexpr (HAS2) {
-    ((uint4*)xs)[threadIdx.x] = xv0;
-    if (CPL == 2) ((uint4*)xs)[threadIdx.x + 256] = xv1;
-  }
+  ((uint4*)xs)[threadIdx.x] = xv0;
+  if (CPL == 2) ((uint4*)xs)[threadIdx.x + 256] = xv1;
   __syncthreads();
   if (nact > 0) {
     // 3. this row of every FP4 rank (batch slots past the active groups repeat
@@ -180,29 +162,21 @@ __global__ __launch_bounds__(256, 2) void gateup_b1_kernel(B1Args a) {
     }
     __builtin_amdgcn_sched_barrier(0);  // every load above is out before the first row is consumed
 
-    // 4. rows in arrival order, on the matrix cores (tile_fp4_x): the FP4
-    // chunks and their scale bytes go in as loaded, against x's parts
-    v8i xa[CPL][2];
-#pragma unroll
-    for (int q = 0; q < CPL; ++q)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint4 u0 = *(const uint4*)&xop[q][t][lane][0], u1 = *(const uint4*)&xop[q][t][lane][16];
-        xa[q][t] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-      }
-    const uint32_t xsw = *(const uint32_t*)xsc[lane];
+    // 4. rows in arrival order; the block scale rides in the convert, so each
+    // row is one accumulation chain per matrix (two for instruction overlap)
     float gsum[NB], usum[NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      v4f tg = {0.0f, 0.0f, 0.0f, 0.0f}, tu = {0.0f, 0.0f, 0.0f, 0.0f};
+      float g0a = 0.0f, g1a = 0.0f, u0a = 0.0f, u1a = 0.0f;
 #pragma unroll
       for (int q = 0; q < CPL; ++q) {
-        const uint32_t sh = (xsw >> (16 * q)) & 0xffu, slo = (xsw >> (16 * q + 8)) & 0xffu;
-        tg = tile_fp4_x(xa[q][0], xa[q][1], sh, slo, sl[u].c1[q], sl[u].s1[q], tg);
-        tu = tile_fp4_x(xa[q][0], xa[q][1], sh, slo, sl[u].c3[q], sl[u].s3[q], tu);
+        B1Chunk xq;  // re-read per row: LDS bandwidth is cheaper than 16 registers per chunk
+        xq.load_lds(xs, (size_t)(q * 64 + lane) * 32);
+        xq.fp4_acc(sl[u].c1[q], stab[sl[u].s1[q]], g0a, g1a);
+        xq.fp4_acc(sl[u].c3[q], stab[sl[u].s3[q]], u0a, u1a);
       }
-      gsum[u] = wave_sum_to_lane63(tile_diag(tg, lane));
-      usum[u] = wave_sum_to_lane63(tile_diag(tu, lane));
+      gsum[u] = wave_sum_to_lane63(g0a + g1a);
+      usum[u] = wave_sum_to_lane63(u0a + u1a);
     }
     // 5. SwiGLU of the row for every group at once: lane u takes group u
     float gv = 0.0f, uv = 0.0f;

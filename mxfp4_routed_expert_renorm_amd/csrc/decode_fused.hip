@@ -113,8 +113,6 @@ struct alignas(16) FusedSmem {
   int ng;                                 // groups with work
   uint32_t issued;                        // computing wavefronts that issued their last gate/up row
   uint32_t go;                            // every gate/up unit is done
-  alignas(16) uint8_t xq[2][2][64][32];   // x as MFMA operands: [half of H][hi, lo][lane][32 E4M3 codes]
-  uint8_t xs[64][4];                      // their block scales: [lane][half 0 hi, lo, half 1 hi, lo]
 };
 
 // workgroup barrier that orders LDS only: a fenced __syncthreads would also
@@ -135,6 +133,13 @@ __device__ __forceinline__ const uint8_t* group_record(const FusedArgs& a, const
   if (g < S0) return a.shared;
   return a.fp4_base + (size_t)sm.gslot[g] * a.fp4_stride;
 }
+
+// A group's h in LDS: lane l's 64 bytes (elements 32l .. 32l+31) as four
+// 16-byte pieces, piece i in slot 4l + ((i + r) & 3) with a per-lane rotation
+// r, so that the lanes' i-th 16-byte reads fall in different banks (with
+// pieces in order, lanes 64 bytes apart would share banks four ways).  The
+// rotation is conflict-free for 32 and for 64 banks of 4 bytes.
+__device__ __forceinline__ int h_slot(int l, int i) { return 4 * l + ((i + ((l >> 1) ^ (l >> 3))) & 3); }
 
 // one gate/up row of one group: both halves of H, w1 and w3
 struct GURow {
@@ -212,7 +217,9 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
     const uint32_t tag = handoff_tag(a.sync, unit);
     // 1. the activation, the routing inputs (wavefront 0), the shared
     // expert's row: none of it needs the routing
-    const uint4 xv = ((const uint4*)a.x)[tid];  // x elements 8 tid .. 8 tid + 7
+    B1Chunk x0, x1;
+    x0.load_global(a.x, (size_t)lane * 32);
+    x1.load_global(a.x, (size_t)(64 + lane) * 32);
     float lv[EPL > 0 ? EPL : 1];
     int my_slot = -1;
     float my_w = 0.0f;
@@ -227,22 +234,6 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
     GURow ring[WIN];
     if constexpr (SH) issue_gu(ring[0], a.shared);
     __builtin_amdgcn_sched_barrier(0);
-
-    // x split into its two E4M3 parts (tile_fp4_x), placed as the MFMA's A
-    // operand of each half of H (a_operand_pos); chunk C's scales go to lane C
-    {
-      const int e0 = 8 * tid, p = e0 >> 11, C = (e0 >> 5) & 63;
-      uint2 hi, lo;
-      int sh, sl, ln, j;
-      split_e4m3(xv, hi, lo, sh, sl);
-      a_operand_pos(C, e0 & 31, ln, j);
-      *(uint2*)&sm.xq[p][0][ln][j] = hi;
-      *(uint2*)&sm.xq[p][1][ln][j] = lo;
-      if ((tid & 3) == 0) {
-        sm.xs[C][2 * p] = (uint8_t)(sh + 127);
-        sm.xs[C][2 * p + 1] = (uint8_t)(sl + 127);
-      }
-    }
 
     // 2. wavefront 0 routes the token and lists the groups
     if (wave == 0) {
@@ -262,19 +253,9 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
         a.w[lane] = my_w;
       }
     }
-    lds_barrier();  // B0: groups listed, x's parts in LDS
+    lds_barrier();  // B0: groups listed
     const int ng = sm.ng;
     auto issue_rec = [&](int g) { return group_record(a, sm, g, ng, S0); };
-    v8i xa[2][2];  // [half of H][hi, lo]
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const uint4 u0 = *(const uint4*)&sm.xq[p][q][lane][0], u1 = *(const uint4*)&sm.xq[p][q][lane][16];
-        xa[p][q] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-      }
-    const uint32_t xsw = *(const uint32_t*)sm.xs[lane];
-    const uint32_t xs0h = xsw & 0xffu, xs0l = (xsw >> 8) & 0xffu, xs1h = (xsw >> 16) & 0xffu, xs1l = xsw >> 24;
 
     // 3. gate/up rows of the groups, WIN in flight; each row's SwiGLU output
     // goes to LDS.  Every batch slot is issued (past the active groups: the
@@ -287,18 +268,18 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_b1_kernel(FusedArgs a) {
 #pragma unroll
     for (int g = 0; g < NB; ++g) {
       GURow& r = ring[g % WIN];
-      v4f tg = {0.0f, 0.0f, 0.0f, 0.0f}, tu = {0.0f, 0.0f, 0.0f, 0.0f};
-      tg = tile_fp4_x(xa[0][0], xa[0][1], xs0h, xs0l, r.c1[0], r.s1[0], tg);
-      tu = tile_fp4_x(xa[0][0], xa[0][1], xs0h, xs0l, r.c3[0], r.s3[0], tu);
-      tg = tile_fp4_x(xa[1][0], xa[1][1], xs1h, xs1l, r.c1[1], r.s1[1], tg);
-      tu = tile_fp4_x(xa[1][0], xa[1][1], xs1h, xs1l, r.c3[1], r.s3[1], tu);
+      float g0 = 0.0f, g1 = 0.0f, u0 = 0.0f, u1 = 0.0f;
+      x0.fp4_acc(r.c1[0], e8m0_to_f32(r.s1[0]), g0, g1);
+      x1.fp4_acc(r.c1[1], e8m0_to_f32(r.s1[1]), g0, g1);
+      x0.fp4_acc(r.c3[0], e8m0_to_f32(r.s3[0]), u0, u1);
+      x1.fp4_acc(r.c3[1], e8m0_to_f32(r.s3[1]), u0, u1);
       if (g + WIN < NB) {
         issue_gu(r, issue_rec(g + WIN));
         if (g + WIN == NB - 1 && lane == 0) atomicAdd(&sm.issued, 1u);
       }
       __builtin_amdgcn_sched_barrier(0);
-      const float gs = wave_sum_to_lane63(tile_diag(tg, lane));
-      const float us = wave_sum_to_lane63(tile_diag(tu, lane));
+      const float gs = wave_sum_to_lane63(g0 + g1);
+      const float us = wave_sum_to_lane63(u0 + u1);
       if (lane == 63 && g < ng) sm.hrow[g][wave] = silu_mul_b1(gs, us);
     }
     lds_barrier();  // B1: the unit's SwiGLU outputs are in LDS

@@ -154,11 +154,10 @@ def test_single_launch_given_ids_with_drops(gpu_lib, with_shared):
 
 
 def _x_wide_range():
-    """bf16 activations whose 32-element blocks stress the single launch's
-    two-part E4M3 form of x: an all-zero block (+0 and -0), a block whose
-    elements sit 2^-30 below its largest (past the exactly split range), a
-    block of bf16 subnormals, blocks alternating 2^6 and 2^-8 magnitudes, and
-    ordinary N(0,1) blocks elsewhere."""
+    """bf16 activations with unusual 32-element blocks: an all-zero block (+0
+    and -0), a block whose elements sit 2^-30 below its largest, a block of
+    bf16 subnormals, blocks alternating 2^6 and 2^-8 magnitudes, a block near
+    the bottom of the normal range, and ordinary N(0,1) blocks elsewhere."""
     x = W.bf16_normal(7, (43,), (1, 4096)).copy()
     rng = np.random.default_rng(43)
     sign = lambda n: np.where(rng.random(n) < 0.5, 0x8000, 0).astype(np.uint16)
@@ -175,8 +174,7 @@ def _x_wide_range():
 
 def test_single_launch_x_edge_blocks(gpu_lib):
     """The single launch on activations with zero, subnormal and wide-range
-    blocks (x enters its gate/up matrix-core products as two E4M3 parts):
-    within tolerance of the oracle, with no non-finite output."""
+    blocks: within tolerance of the oracle, with no non-finite output."""
     torch = _torch()
     st = _bank(gpu_lib)
     H, I, k = 4096, 2048, 8
