@@ -237,3 +237,48 @@ def test_single_launch_graph_replays(gpu_lib):
         torch.cuda.synchronize()
         assert torch.equal(scratch, ref[rep:rep + 1]), rep
     assert _err_word(gpu_lib, ws, k) == 0
+
+
+@pytest.mark.parametrize("single", [True, False])
+def test_decode_wide_routing(gpu_lib, single):
+    """E = 1000 logits: both batch-1 forms route with 16 logits per lane (the
+    other instantiation of their in-kernel top-k).  The bank's 256 records
+    are repeated over 1000 slots on the device (13.4 GB), so expert e runs
+    record e mod 256; ids and weights are bit-exact against the oracle's
+    routing over all 1000 logits, outputs within tolerance."""
+    torch = _torch()
+    st = _bank(gpu_lib)
+    cfg = W.WORKLOADS["decode-b1"]
+    H, I, k, E = 4096, 2048, 8, 1000
+    base = st["bank_dev"]
+    log(f"wide routing ({'single launch' if single else 'two launches'}): {E} slots of {base.shape[0]} records")
+    big = base.repeat(-(-E // base.shape[0]), 1)[:E].contiguous()
+    desc = gpu_lib.make_layer(H, I, fp4_base=big, fp4_stride=big.shape[1], num_slots=E, shared=st["shared_dev"],
+                              flags=gpu_lib.MOE_LAYER_SINGLE_LAUNCH if single else 0)
+    ws = gpu_lib.expert_workspace(H, I, 1, k, True)
+    n = 3
+    lg = W.router_logits(cfg["seed"], (47,), n, E)
+    xs = W.bf16_normal(cfg["seed"], (48,), (n, H))
+    ids = torch.empty((n, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((n, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+    lgd = dev(lg)
+    for i in range(n):
+        gpu_lib.moe_layer_decode(desc, lgd[i], bf16_dev(xs[i:i + 1]), k, ids[i], w[i], out[i:i + 1], ws)
+    torch.cuda.synchronize()
+    if single:
+        assert _err_word(gpu_lib, ws, k) == 0
+    got_ids, got_w, got = ids.cpu().numpy(), w.cpu().numpy(), to_f64(out)
+    del big, desc
+    torch.cuda.empty_cache()
+    for i in range(n):
+        oids, ow = O.route(lg[i:i + 1], k)
+        assert np.array_equal(got_ids[i], oids[0]), i
+        assert np.max(np.abs(got_w[i] - ow[0])) <= 1e-6, i
+        assert np.any(oids[0] >= 256), "the routing reaches past the first 256 experts"
+        x64 = O.bf16_bits_to_f64(xs[i:i + 1])[0]
+        ys = np.stack([O.expert_mlp(x64, *_expert(st, int(e) % 256)) for e in oids[0]])
+        ref = O.combine(ys, ow[0], O.expert_mlp(x64, *_expert(st, -1)))
+        err = max_rel(got[i], ref)
+        log(f"  token {i}: ids {oids[0].tolist()}, max-rel {err:.3e}")
+        assert err <= TOL_BF16_MAX_REL, (i, err)
