@@ -538,8 +538,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(PrefillArgs a) {
   const RecordLayout L = record_layout(H, I, 4);
   const uint32_t wrowb = (uint32_t)K / 2, wrows = (uint32_t)K / 32;
 
-  for (int item = virtual_block(); item < nitems; item += gridDim.x) {
-    const int mi = item / ncol, nt = item - mi * ncol;
+  // a workgroup takes `pair` N tiles of one M tile in a row: the second
+  // reuses the first's activation offsets (the tile entry and its rows'
+  // token ids, two dependent trips); consecutive pairs still go to
+  // neighbouring workgroups of one XCD
+  const int pair = (ncol % 2 == 0) ? 2 : 1;
+  const int nchunks = nitems / pair;
+  for (int chunk = virtual_block(); chunk < nchunks; chunk += gridDim.x) {
+    const int mi = chunk / (ncol / pair), nt0 = (chunk - mi * (ncol / pair)) * pair;
     const int key = a.items[1 + 3 * mi], start = a.items[2 + 3 * mi], rows = a.items[3 + 3 * mi];  // first grouped position of the tile
     const uint8_t* rec = key_record(a, key);
     // activation rows: x (gathered by token) for gate/up, h (grouped) for down
@@ -549,8 +555,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(PrefillArgs a) {
       r = min(r, rows - 1);
       return NMAT == 2 ? (uint32_t)(a.perm[start + r] / a.K1) : (uint32_t)(start + r);
     };
-    // weight rows of the item: offsets of codes or scales inside the record
-    auto weight_row = [&](int wr, bool scales) -> uint32_t {
+    // weight rows of N tile nt: offsets of codes or scales inside the record
+    auto weight_row = [&](int nt, int wr, bool scales) -> uint32_t {
       uint32_t n, off;
       if (NMAT == 2) {
         const int mat = wr / (kNR / 2);
@@ -569,22 +575,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(PrefillArgs a) {
       x.O.a[j] = act_row(p / kCA) * (uint32_t)K + 16u * (p % kCA);
     }
     x.O.as = act_row(tid) * (uint32_t)(K / 32);
-#pragma unroll
-    for (int j = 0; j < kPiecesB; ++j) {
-      const int p = tid + j * kThreads;
-      x.O.b[j] = weight_row(p / kCB, false) + 16u * (p % kCB);
-    }
-    x.O.bs = weight_row(tid % kNR, true);
     x.abase = abase, x.asbase = asbase, x.rec = rec;
     x.tid = tid, x.c = c, x.h = h, x.mp = mp, x.nh = nh, x.nstage = nstage;
-    x.rows = rows, x.start = start, x.nt = nt;
+    x.rows = rows, x.start = start;
     // the wavefront's live M blocks: mp, mp + 2, mp + 4 while below the tile's rows
     const int nl = max(0, min(kMB / 2, (rows - 32 * mp + 63) / 64));
-    switch (nl) {
-      case 0: gemm_item<NMAT, 0>(sm, a, x); break;
-      case 1: gemm_item<NMAT, 1>(sm, a, x); break;
-      case 2: gemm_item<NMAT, 2>(sm, a, x); break;
-      default: gemm_item<NMAT, 3>(sm, a, x); break;
+    for (int u = 0; u < pair; ++u) {
+      const int nt = nt0 + u;
+#pragma unroll
+      for (int j = 0; j < kPiecesB; ++j) {
+        const int p = tid + j * kThreads;
+        x.O.b[j] = weight_row(nt, p / kCB, false) + 16u * (p % kCB);
+      }
+      x.O.bs = weight_row(nt, tid % kNR, true);
+      x.nt = nt;
+      switch (nl) {
+        case 0: gemm_item<NMAT, 0>(sm, a, x); break;
+        case 1: gemm_item<NMAT, 1>(sm, a, x); break;
+        case 2: gemm_item<NMAT, 2>(sm, a, x); break;
+        default: gemm_item<NMAT, 3>(sm, a, x); break;
+      }
     }
   }
 }
